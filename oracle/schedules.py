@@ -1,0 +1,269 @@
+"""DASH tile schedules, dQ accumulation ordinals, validator and DAG simulator.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).  Plain Python, written
+from the pages' description of the method; it shares nothing with the C++
+schedule generator, and the tests compare the two element by element.
+
+Vocabulary.  N tiles per sequence (query and key/value alike).  A *step* is
+one (query head, query tile qi, key/value tile kj) pair.  A *chain* is every
+step of one key/value tile of one key/value group (batch b, kv head hk): the
+g query heads of the group in ascending order, each walking its query tiles.
+A chain runs contiguously on one workgroup so that its dK/dV stay in
+registers ([summary] §2.1, restrictions).  The *ordinal* of a step is its
+position in the accumulation sequence of its dQ tile (head, qi); a fixed
+ordinal per step is what makes dQ bitwise reproducible ([summary] §1).
+
+Schedules ([summary] §2.2; [news] §2.3):
+* SERIAL    -- the serialized fixed-order baseline: each chain walks qi
+               ascending; dQ_qi accumulates key/value tiles in ascending kj.
+* DESC_Q    -- same ordinals, but each chain walks qi descending
+               ([summary] §2.2.A).
+* SHIFT     -- full mask: a gang of N workgroups handles one kv group; the
+               workgroup holding key/value tile p visits query tiles
+               p, p+1, ..., N-1, 0, ..., p-1 ([summary] §2.2.B; [news] §2.3
+               and its four-tile figure).  dQ_qi's t-th contributor is the
+               tile visited at step t, so no two workgroups touch one dQ tile
+               at the same step.
+* SYM_SHIFT -- causal mask: a gang of N/2 workgroups; workgroup p owns tiles
+               p and N-1-p and covers a dense rectangle then a folded
+               triangle ([summary] §2.2.B, symmetric shift).  The index
+               formulas are this implementation's reading of that sentence.
+Gang schedules rank each dQ tile's contributors by their lock-step time key
+(position in the workgroup's list for that group), ties broken by kj.
+
+Parity status: pinned by the four-tile example of [news] §2.3, the closed-form
+times of [news] §2.3, coverage/Latin/monotonicity properties ([summary]
+§2.2.B lemma) and exhaustive small-N checks (tests/test_schedule_oracle.py).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+FULL, CAUSAL = 0, 1
+SERIAL, DESC_Q, SHIFT, SYM_SHIFT = 0, 1, 2, 3
+NAMES = {SERIAL: "serial", DESC_Q: "desc_q", SHIFT: "shift", SYM_SHIFT: "sym_shift"}
+
+
+@dataclass(frozen=True)
+class Step:
+    head: int    # global query head index (b * Hq + hq)
+    qi: int
+    kj: int
+    ord: int
+    first: bool  # first step of its chain
+    last: bool   # last step of its chain
+
+
+class ScheduleError(ValueError):
+    pass
+
+
+def kv_walk(mask: int, sched: int, N: int, kj: int) -> list[int]:
+    """Query tiles visited by key/value tile kj for the serial/descending walks."""
+    lo = kj if mask == CAUSAL else 0
+    tiles = list(range(lo, N))
+    return tiles[::-1] if sched == DESC_Q else tiles
+
+
+def _chain(group: int, g: int, kj: int, per_head_walk: list[int]) -> list[tuple[int, int, int]]:
+    return [(group * g + u, qi, kj) for u in range(g) for qi in per_head_walk]
+
+
+def _flagged(chain: list[tuple[int, int, int, int]]) -> list[Step]:
+    n = len(chain)
+    return [Step(h, qi, kj, o, i == 0, i == n - 1) for i, (h, qi, kj, o) in enumerate(chain)]
+
+
+def gang_slot(gang: int, p: int, n_gangs: int, gang_size: int, xcd_local: bool) -> int:
+    """Workgroup index of member p of a gang.
+
+    With ``xcd_local`` members of one gang get indices congruent modulo the
+    number of gangs, which the round-robin dispatch of workgroups over the
+    chiplets keeps together when the gang count is a multiple of 8.
+    """
+    return p * n_gangs + gang if xcd_local else gang * gang_size + p
+
+
+def build(mask: int, sched: int, N: int, g: int, groups: int, P: int, xcd_local: bool = True) -> list[list[Step]]:
+    """Per-workgroup step lists for ``groups`` kv groups of g query heads, N tiles, P workgroups."""
+    if N < 1 or g < 1 or groups < 1 or P < 1:
+        raise ScheduleError("sizes must be positive")
+    out: list[list[Step]] = [[] for _ in range(P)]
+    if sched in (SERIAL, DESC_Q):
+        # Chains in (group, kj) order go to the least-loaded workgroup (unit
+        # cost per step, ties to the lowest index): a static stand-in for the
+        # in-order dispatch of the baseline's one-block-per-KV-tile launch.
+        load = [0] * P
+        for grp in range(groups):
+            for kj in range(N):
+                walk = kv_walk(mask, sched, N, kj)
+                w = min(range(P), key=lambda x: (load[x], x))
+                # ordinal = kj: every dQ tile accumulates key/value tiles in ascending order
+                out[w].extend(_flagged([(h, qi, k, k) for (h, qi, k) in _chain(grp, g, kj, walk)]))
+                load[w] += g * len(walk)
+        return out
+    if sched == SHIFT:
+        if mask != FULL:
+            raise ScheduleError("shift scheduling needs a full mask")
+        gang_size = N
+    elif sched == SYM_SHIFT:
+        if mask != CAUSAL:
+            raise ScheduleError("symmetric shift needs a causal mask")
+        if N % 2:
+            raise ScheduleError("symmetric shift needs an even tile count")
+        gang_size = N // 2
+    else:
+        raise ScheduleError(f"unknown schedule {sched}")
+    n_gangs = P // gang_size
+    if n_gangs < 1:
+        raise ScheduleError("gang larger than the workgroup count")
+    for grp in range(groups):
+        gang = grp % n_gangs
+        members = []  # per member: list of chains, each a list of (head, qi, kj)
+        for p in range(gang_size):
+            if sched == SHIFT:
+                members.append([_chain(grp, g, p, [(p + t) % N for t in range(N)])])
+            else:
+                M = gang_size
+                a_walk = [M + (p + t) % M for t in range(M)] + [p + s for s in range(M - p)]
+                b_walk = [N - 1 - s + M - p for s in range(M - p, M + 1)]
+                members.append([_chain(grp, g, p, a_walk), _chain(grp, g, N - 1 - p, b_walk)])
+        # ordinal = rank of (time key, kj) among each dQ tile's contributors,
+        # where the time key is the step's position in its member's list
+        keys: dict[tuple[int, int], list[tuple[int, int]]] = {}
+        for chains in members:
+            pos = 0
+            for ch in chains:
+                for (h, qi, kj) in ch:
+                    keys.setdefault((h, qi), []).append((pos, kj))
+                    pos += 1
+        rank = {}
+        for (h, qi), lst in keys.items():
+            for o, (_, kj) in enumerate(sorted(lst)):
+                rank[(h, qi, kj)] = o
+        for p, chains in enumerate(members):
+            w = gang_slot(gang, p, n_gangs, gang_size, xcd_local)
+            for ch in chains:
+                out[w].extend(_flagged([(h, qi, kj, rank[(h, qi, kj)]) for (h, qi, kj) in ch]))
+    return out
+
+
+def contributors(mask: int, N: int, qi: int) -> int:
+    """Number of key/value tiles that add into dQ tile qi."""
+    return qi + 1 if mask == CAUSAL else N
+
+
+def validate(lists: list[list[Step]], mask: int, N: int, g: int, groups: int) -> None:
+    """Raise ScheduleError unless the lists are a complete, contiguous, well-ordered, deadlock-free schedule."""
+    heads = g * groups
+    seen = set()
+    for lst in lists:
+        for s in lst:
+            if not (0 <= s.head < heads and 0 <= s.qi < N and 0 <= s.kj < N):
+                raise ScheduleError(f"index out of range: {s}")
+            if mask == CAUSAL and s.kj > s.qi:
+                raise ScheduleError(f"masked tile scheduled: {s}")
+            key = (s.head, s.qi, s.kj)
+            if key in seen:
+                raise ScheduleError(f"tile pair scheduled twice: {key}")
+            seen.add(key)
+    expect = sum(contributors(mask, N, qi) for qi in range(N)) * heads
+    if len(seen) != expect:
+        raise ScheduleError(f"coverage {len(seen)} != {expect}")
+    # chain contiguity: each (group, kj) appears as exactly one run, flagged first..last
+    chain_owner = {}
+    for w, lst in enumerate(lists):
+        run = None
+        for i, s in enumerate(lst):
+            ck = (s.head // g, s.kj)
+            if s.first:
+                if run is not None:
+                    raise ScheduleError(f"chain {run} not closed before {s}")
+                if ck in chain_owner:
+                    raise ScheduleError(f"chain {ck} split")
+                chain_owner[ck] = w
+                run = ck
+            if i == 0 and not s.first:
+                raise ScheduleError("list does not start a chain")
+            if (s.head // g, s.kj) != run:
+                raise ScheduleError(f"chain {run} interrupted by {s}")
+            if s.last:
+                run = None
+        if lst and not lst[-1].last:
+            raise ScheduleError("list ends inside a chain")
+    if len(chain_owner) != groups * N:
+        raise ScheduleError("chain count mismatch")
+    # ordinals: a permutation of 0..count-1 per dQ tile
+    ords: dict[tuple[int, int], list[int]] = {}
+    for lst in lists:
+        for s in lst:
+            ords.setdefault((s.head, s.qi), []).append(s.ord)
+    for (h, qi), o in ords.items():
+        if sorted(o) != list(range(contributors(mask, N, qi))):
+            raise ScheduleError(f"ordinals of dQ tile {(h, qi)} are {sorted(o)}")
+    simulate(lists, 1.0, 1.0)  # raises on deadlock
+
+
+def simulate(lists: list[list[Step]], c: float, r: float):
+    """Unit-cost DAG model of [news] §2.2 / [summary] §2.1.
+
+    Every step costs c of compute and then r of reduction into its dQ tile;
+    the reduction may start only after the tile's previous ordinal finished
+    its own.  A workgroup runs its list in order and idles while waiting.
+    Returns (makespan, total wait).  Raises ScheduleError on deadlock.
+    """
+    P = len(lists)
+    idx = [0] * P
+    t = [0.0] * P
+    count: dict[tuple[int, int], int] = {}
+    done_at: dict[tuple[int, int], float] = {}
+    wait = 0.0
+    remaining = sum(len(l) for l in lists)
+    while remaining:
+        progressed = False
+        for w in range(P):
+            while idx[w] < len(lists[w]):
+                s = lists[w][idx[w]]
+                key = (s.head, s.qi)
+                if count.get(key, 0) != s.ord:
+                    break
+                ready = t[w] + c
+                start = max(ready, done_at.get(key, 0.0))
+                wait += start - ready
+                t[w] = start + r
+                done_at[key] = t[w]
+                count[key] = s.ord + 1
+                idx[w] += 1
+                remaining -= 1
+                progressed = True
+        if not progressed:
+            raise ScheduleError("deadlock: no workgroup can make progress")
+    return max(t), wait
+
+
+def monotone_in_lockstep(lists: list[list[Step]], g: int) -> bool:
+    """The checkable form of the [summary] §2.2.B lemma for gang schedules:
+    along every dQ tile's accumulation sequence the lock-step time key never
+    decreases (no zero-weight edge points to a shallower node), and with one
+    query head per group it strictly increases (no two workgroups reduce into
+    one dQ tile at the same step)."""
+    times = {}
+    for lst in lists:
+        pos, cur = 0, None
+        for s in lst:
+            grp = s.head // g
+            if grp != cur:
+                pos, cur = 0, grp
+            times[(s.head, s.qi, s.kj)] = pos
+            pos += 1
+    seq: dict[tuple[int, int], list[tuple[int, int]]] = {}
+    for lst in lists:
+        for s in lst:
+            seq.setdefault((s.head, s.qi), []).append((s.ord, times[(s.head, s.qi, s.kj)]))
+    strict = g == 1
+    for lst in seq.values():
+        lst.sort()
+        for (o1, t1), (o2, t2) in zip(lst, lst[1:]):
+            if t2 < t1 or (strict and t2 == t1):
+                return False
+    return True

@@ -1,0 +1,68 @@
+"""Seeded synthetic inputs for the attention backward workloads.
+
+This module only draws random numbers and rounds them to bfloat16. It holds
+none of the attention arithmetic, so both the CPU oracle (through the tests)
+and the GPU path use it without sharing any computation.
+
+Recipe: numpy ``default_rng(seed)``; fp32 standard normals drawn in the order
+Q, K, V, dO, multiplied by ``std``; then rounded to bfloat16 with
+round-to-nearest-even.  Q and dO have shape [B, Hq, S, D]; K and V have shape
+[B, Hkv, S, D]; all contiguous row-major (BHSD).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bfloat16 (nearest, ties to even); return the uint16 bit patterns."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounding = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return ((u + rounding) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to fp32."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclass
+class AttnInputs:
+    """bfloat16 bit patterns (uint16) of Q, K, V, dO plus the problem sizes."""
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    do: np.ndarray
+    B: int
+    Hq: int
+    Hkv: int
+    S: int
+    D: int
+
+    def as_f64(self, name: str) -> np.ndarray:
+        return bf16_bits_to_f32(getattr(self, name)).astype(np.float64)
+
+
+def make_inputs(B: int, Hq: int, Hkv: int, S: int, D: int, seed: int = 0, std: float = 1.0) -> AttnInputs:
+    rng = np.random.default_rng(seed)
+    shapes = {"q": (B, Hq, S, D), "k": (B, Hkv, S, D), "v": (B, Hkv, S, D), "do": (B, Hq, S, D)}
+    out = {}
+    for name in ("q", "k", "v", "do"):
+        x = rng.standard_normal(size=shapes[name], dtype=np.float32)
+        if std != 1.0:
+            x *= np.float32(std)
+        out[name] = f32_to_bf16_bits(x)
+    return AttnInputs(B=B, Hq=Hq, Hkv=Hkv, S=S, D=D, **out)
+
+
+# The five workloads: (name, B, Hq, Hkv, S, D, causal, tile, std).
+WORKLOADS = {
+    "c1_full_s256_d64": dict(B=1, Hq=1, Hkv=1, S=256, D=64, causal=False, tile=64, std=1.0),
+    "c2_causal_s2048_d128": dict(B=4, Hq=16, Hkv=16, S=2048, D=128, causal=True, tile=128, std=1.0),
+    "c3_full_s4096_d64": dict(B=2, Hq=24, Hkv=24, S=4096, D=64, causal=False, tile=128, std=1.0),
+    "c4_full_s16384_d128": dict(B=1, Hq=16, Hkv=16, S=16384, D=128, causal=False, tile=128, std=1.0),
+    "c4_causal_s16384_d128": dict(B=1, Hq=16, Hkv=16, S=16384, D=128, causal=True, tile=128, std=1.0),
+    "c5_gqa_causal_s8192_d128": dict(B=1, Hq=32, Hkv=8, S=8192, D=128, causal=True, tile=128, std=0.5),
+}

@@ -1,0 +1,165 @@
+"""Pins for the schedule oracle (CPU only).
+
+Against the pages: the four-tile shift example and the two closed-form times
+of [news] §2.3 ("DASH如何革新LLM确定性训练"); the lemma of [summary] §2.2.B
+("Resumo Técnico: DASH ...") in its checkable lock-step form.  Against
+exhaustive enumeration: coverage, chain contiguity and ordinal permutations
+for every small tile count.
+"""
+import os
+
+import pytest
+
+from oracle import schedules as Sch
+from oracle.schedules import CAUSAL, DESC_Q, FULL, SERIAL, SHIFT, SYM_SHIFT, Step
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_shift_example():
+    rows = []
+    for line in open(os.path.join(GOLDEN, "shift_n4_example.txt")):
+        line = line.split("#")[0].strip()
+        if line:
+            vals = [int(x) for x in line.split()]
+            rows.append((vals[0], vals[1:]))
+    return rows
+
+
+def test_shift_four_tiles_matches_the_figure():
+    lists = Sch.build(FULL, SHIFT, 4, 1, 1, 4, xcd_local=False)
+    for cu, order in _read_shift_example():
+        assert [s.kj for s in lists[cu]] == [cu] * 4
+        assert [s.qi for s in lists[cu]] == order
+        # dQ tile qi receives its t-th contribution at step t: ordinal = position
+        assert [s.ord for s in lists[cu]] == [0, 1, 2, 3]
+
+
+def _closed_form_serial_lists(n, m, mask, walk_desc=False):
+    """Chain kj of every head on workgroup kj (the model behind [news] §2.3's formulas)."""
+    lists = [[] for _ in range(n)]
+    for h in range(m):
+        for kj in range(n):
+            qs = list(range(kj if mask == CAUSAL else 0, n))
+            if walk_desc:
+                qs = qs[::-1]
+            for i, qi in enumerate(qs):
+                lists[kj].append(Step(h, qi, kj, kj, i == 0, i == len(qs) - 1))
+    return lists
+
+
+@pytest.mark.parametrize("n,m", [(2, 1), (4, 3), (8, 5), (16, 2)])
+@pytest.mark.parametrize("c,r", [(1.0, 1.0), (3.0, 0.5), (1.0, 2.0)])
+def test_serial_causal_matches_T_causal(n, m, c, r):
+    # [news] §2.3: T_causal = m*n*(c+r) + (n-1)*r
+    mk, _ = Sch.simulate(_closed_form_serial_lists(n, m, CAUSAL), c, r)
+    assert abs(mk - (m * n * (c + r) + (n - 1) * r)) < 1e-9
+
+
+@pytest.mark.parametrize("n,m", [(4, 8), (8, 16), (16, 12)])
+def test_desc_q_causal_close_to_T_reversed(n, m):
+    # [news] §2.3: T_reversed ~= m*(n+1)*(c+r)/2 + (n-1)*r, with freed workgroups taking the next heads
+    c, r = 1.0, 1.0
+    lists = Sch.build(CAUSAL, DESC_Q, n, 1, m, n)
+    mk, _ = Sch.simulate(lists, c, r)
+    t_rev = m * (n + 1) * (c + r) / 2 + (n - 1) * r
+    assert abs(mk - t_rev) <= n * (c + r)
+    # and the descending walk beats the serialized baseline's closed form
+    assert mk < m * n * (c + r) + (n - 1) * r
+
+
+@pytest.mark.parametrize("n,m", [(4, 1), (4, 3), (8, 4), (32, 2)])
+@pytest.mark.parametrize("c,r", [(1.0, 1.0), (2.0, 0.25)])
+def test_shift_full_reaches_the_lower_bound(n, m, c, r):
+    # [summary] §2.2.B: shift scheduling is optimal; on one gang every workgroup
+    # works m*n steps back to back, so the makespan is exactly m*n*(c+r).
+    lists = Sch.build(FULL, SHIFT, n, 1, m, n)
+    mk, wait = Sch.simulate(lists, c, r)
+    assert abs(mk - m * n * (c + r)) < 1e-9 and wait == 0
+
+
+@pytest.mark.parametrize("n,m", [(4, 2), (8, 4), (16, 2)])
+def test_sym_shift_causal_has_no_waits(n, m):
+    # Two heads at a time on n workgroups: each member does n+1 steps per head
+    lists = Sch.build(CAUSAL, SYM_SHIFT, n, 1, m, n)
+    mk, wait = Sch.simulate(lists, 1.0, 1.0)
+    assert wait == 0
+    assert abs(mk - m * (n + 1) * 2.0 / 2) < 1e-9
+
+
+def test_sym_shift_four_tiles_worked_example():
+    lists = Sch.build(CAUSAL, SYM_SHIFT, 4, 1, 1, 2, xcd_local=False)
+    assert [(s.kj, s.qi) for s in lists[0]] == [(0, 2), (0, 3), (0, 0), (0, 1), (3, 3)]
+    assert [(s.kj, s.qi) for s in lists[1]] == [(1, 3), (1, 2), (1, 1), (2, 3), (2, 2)]
+    order = {}
+    for lst in lists:
+        for s in lst:
+            order.setdefault(s.qi, {})[s.ord] = s.kj
+    assert [order[q][o] for q in range(4) for o in sorted(order[q])] == [0, 1, 0, 0, 1, 2, 1, 0, 2, 3]
+
+
+@pytest.mark.parametrize("mask,sched", [(FULL, SERIAL), (FULL, DESC_Q), (FULL, SHIFT),
+                                        (CAUSAL, SERIAL), (CAUSAL, DESC_Q), (CAUSAL, SYM_SHIFT)])
+def test_exhaustive_small_schedules_are_valid(mask, sched):
+    for N in range(1, 11):
+        if sched == SYM_SHIFT and N % 2:
+            continue
+        gang = N if sched == SHIFT else max(1, N // 2)
+        for g in (1, 2, 4):
+            for groups in (1, 3):
+                for P in sorted({gang, gang + 1, 2 * gang + 1, 5}):
+                    if sched in (SHIFT, SYM_SHIFT) and P < gang:
+                        continue
+                    lists = Sch.build(mask, sched, N, g, groups, P)
+                    Sch.validate(lists, mask, N, g, groups)
+                    if sched in (SERIAL, DESC_Q):
+                        assert all(s.ord == s.kj for l in lists for s in l)
+                    else:
+                        assert Sch.monotone_in_lockstep(lists, g)
+
+
+def test_serial_and_desc_q_share_ordinals_but_not_walks():
+    a = Sch.build(CAUSAL, SERIAL, 6, 1, 2, 4)
+    b = Sch.build(CAUSAL, DESC_Q, 6, 1, 2, 4)
+    key = lambda lists: sorted((s.head, s.qi, s.kj, s.ord) for l in lists for s in l)
+    assert key(a) == key(b)
+    assert [s.qi for s in a[0]] != [s.qi for s in b[0]]
+
+
+def test_validator_rejects_duplicate_ordinal():
+    lists = Sch.build(FULL, SHIFT, 4, 1, 1, 4)
+    s = lists[1][0]
+    lists[1][0] = Step(s.head, s.qi, s.kj, (s.ord + 1) % 4, s.first, s.last)
+    with pytest.raises(Sch.ScheduleError):
+        Sch.validate(lists, FULL, 4, 1, 1)
+
+
+def test_validator_rejects_cyclic_wait():
+    # Two workgroups, each waiting for the other's later step: a deadlock.
+    lists = [
+        [Step(0, 0, 0, 1, True, False), Step(0, 1, 0, 0, False, True)],
+        [Step(0, 1, 1, 1, True, False), Step(0, 0, 1, 0, False, True)],
+    ]
+    with pytest.raises(Sch.ScheduleError):
+        Sch.simulate(lists, 1.0, 1.0)
+
+
+def test_validator_rejects_missing_and_split_chains():
+    lists = Sch.build(CAUSAL, DESC_Q, 4, 1, 1, 2)
+    with pytest.raises(Sch.ScheduleError):
+        Sch.validate([l[:-1] for l in lists], CAUSAL, 4, 1, 1)
+    moved = [list(l) for l in lists]
+    moved[1].append(moved[0].pop(3))  # last step of the four-step chain of tile 0
+    with pytest.raises(Sch.ScheduleError):
+        Sch.validate(moved, CAUSAL, 4, 1, 1)
+
+
+def test_rejects_bad_combinations():
+    with pytest.raises(Sch.ScheduleError):
+        Sch.build(CAUSAL, SHIFT, 4, 1, 1, 4)
+    with pytest.raises(Sch.ScheduleError):
+        Sch.build(FULL, SYM_SHIFT, 4, 1, 1, 4)
+    with pytest.raises(Sch.ScheduleError):
+        Sch.build(CAUSAL, SYM_SHIFT, 5, 1, 1, 4)
+    with pytest.raises(Sch.ScheduleError):
+        Sch.build(FULL, SHIFT, 8, 1, 1, 4)
