@@ -1,0 +1,182 @@
+#!/usr/bin/env python3
+"""Deterministic attention backward on one MI355X: TFLOP/s, % of the dense
+bf16 matrix-core peak, and the ratio to the non-deterministic atomic variant.
+
+A step is one full backward pass through the C ABI (Delta preprocess,
+persistent backward kernel, dQ finalize) over one batch of seeded synthetic
+bf16 inputs already resident in device memory.  FLOPs per step are
+10 * B * Hq * S^2 * D, halved for the causal mask.  Every deterministic
+schedule and every atomic walk of the workload is timed; the reported value is
+the best deterministic schedule.  The persistent kernel is also timed on its
+own with HIP events recorded on the launch stream, for the roofline.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 matrix-core peak (256 CU x 4096 flop/clk x 2.4 GHz)
+METRIC = "deterministic attn-bwd TFLOP/s (1 GPU) + % of bf16 MFMA peak + ratio vs atomic"
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "bwd_kernel_counters.json")
+
+
+def flops(B, Hq, S, D, causal):
+    f = 10.0 * B * Hq * S * S * D
+    return f / 2 if causal else f
+
+
+def cpu_baseline(wl, seconds_hint=20.0):
+    """The float64 oracle on a bounded sample of the workload: one (batch, head)."""
+    import numpy as np
+    from oracle import attention as A
+    from scheduling_persistent_fa_amd.inputs import bf16_bits_to_f32, make_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        cores = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    S, D, causal = wl["S"], wl["D"], wl["causal"]
+    inp = make_inputs(1, 1, 1, S, D, seed=0, std=wl["std"])
+    f64 = lambda x: bf16_bits_to_f32(x).astype(np.float64)
+    t0 = time.perf_counter()
+    A.backward(f64(inp.q), f64(inp.k), f64(inp.v), f64(inp.do), 1.0 / math.sqrt(D), causal)
+    dt = time.perf_counter() - t0
+    return {"value": flops(1, 1, S, D, causal) / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"one (batch, head) of the workload: B=1 H=1 S={S} D={D} {'causal' if causal else 'full'}, "
+                      f"float64 forward+backward, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c4_full_s16384_d128")
+    ap.add_argument("--schedules", default="", help="comma list (serial,desc_q,shift,sym_shift); default: all for the mask")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-atomic", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(the path shards by (batch, kv head) with no exchange; see DESIGN.md)"}))
+        sys.exit(2)
+
+    import torch
+    from scheduling_persistent_fa_amd import _lib
+    from scheduling_persistent_fa_amd.attention import attn_bwd, attn_fwd, bf16_from_bits, device_info, make_opts
+    from scheduling_persistent_fa_amd.inputs import WORKLOADS, make_inputs
+
+    wl = dict(WORKLOADS[args.workload])
+    B, Hq, Hkv, S, D, causal, tile = wl["B"], wl["Hq"], wl["Hkv"], wl["S"], wl["D"], wl["causal"], wl["tile"]
+    torch.cuda.set_device(0)
+    info = device_info(0)
+    inp = make_inputs(B, Hq, Hkv, S, D, seed=0, std=wl["std"])
+    q, k, v, do = (bf16_from_bits(getattr(inp, n)) for n in ("q", "k", "v", "do"))
+    o, lse = attn_fwd(q, k, v, causal)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    torch.cuda.synchronize()
+    fl = flops(B, Hq, S, D, causal)
+
+    det_names = ["serial", "desc_q"] + (["sym_shift"] if causal else ["shift"])
+    if args.schedules:
+        det_names = [s for s in args.schedules.split(",") if s]
+    ids = {"serial": _lib.SERIAL, "desc_q": _lib.DESC_Q, "shift": _lib.SHIFT, "sym_shift": _lib.SYM_SHIFT}
+    runs = [(n, ids[n], -1) for n in det_names]
+    if not args.no_atomic:
+        walks = ["serial", "desc_q"] + (["sym_shift"] if causal else ["shift"])
+        runs += [(f"atomic[{w}]", _lib.ATOMIC, ids[w]) for w in walks]
+
+    stream = torch.cuda.current_stream()
+    results = {}
+    for name, sched, walk in runs:
+        print(f"[bench] {args.workload} {name}", file=sys.stderr, flush=True)
+        base_opts = dict(tile=tile, atomic_walk=walk)
+        for _ in range(args.warmup):
+            attn_bwd(q, k, v, o, do, lse, causal, sched, dq=dq, dk=dk, dv=dv, opts=make_opts(**base_opts))
+        ref_bits = dq.view(torch.int16).clone(), dk.view(torch.int16).clone(), dv.view(torch.int16).clone()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for a_, b_ in evs:  # materialise the underlying HIP events
+            a_.record(stream)
+            b_.record(stream)
+        opts = [make_opts(events=e, **base_opts) for e in evs]
+        t_beg, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_beg.record(stream)
+        for i in range(args.steps):
+            attn_bwd(q, k, v, o, do, lse, causal, sched, dq=dq, dk=dk, dv=dv, opts=opts[i])
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        ms = t_beg.elapsed_time(t_end) / args.steps
+        kms = sum(a_.elapsed_time(b_) for a_, b_ in evs) / args.steps
+        same = all(torch.equal(x.view(torch.int16), r) for x, r in zip((dq, dk, dv), ref_bits))
+        rec = {"ms_per_step": ms, "tflops": fl / (ms * 1e-3) / 1e12, "kernel_ms": kms,
+               "kernel_tflops": fl / (kms * 1e-3) / 1e12, "repeat_bitwise": bool(same)}
+        if sched != _lib.ATOMIC:
+            stall = torch.zeros(2 * info["num_cu"], dtype=torch.int64, device="cuda")
+            attn_bwd(q, k, v, o, do, lse, causal, sched, dq=dq, dk=dk, dv=dv,
+                     opts=make_opts(stall=stall, sync_check=True, **base_opts))
+            st = stall.view(-1, 2).double().sum(0).tolist()
+            rec["sem_stall_frac"] = st[0] / max(st[1], 1.0)
+        results[name] = rec
+        print(f"[bench]   {ms:.3f} ms/step  {rec['tflops']:.1f} TFLOP/s  kernel {kms:.3f} ms", file=sys.stderr, flush=True)
+
+    det = {n: r for n, r in results.items() if not n.startswith("atomic")}
+    atom = {n: r for n, r in results.items() if n.startswith("atomic")}
+    best = max(det, key=lambda n: det[n]["tflops"])
+    best_atomic = max(atom, key=lambda n: atom[n]["tflops"]) if atom else None
+    value = det[best]["tflops"]
+    ratio = value / atom[best_atomic]["tflops"] if best_atomic else None
+    for r in results.values():
+        r["pct_of_bf16_peak"] = 100.0 * r["tflops"] / PEAK_BF16_TFLOPS
+        if best_atomic:
+            r["ratio_vs_atomic"] = r["tflops"] / atom[best_atomic]["tflops"]
+
+    traffic = None
+    if os.path.exists(PROFILE_COUNTERS):
+        try:
+            c = json.load(open(PROFILE_COUNTERS))
+            if c.get("workload") == args.workload and c.get("schedule") == best:
+                traffic = c.get("hbm_bytes_per_launch")
+        except Exception:
+            traffic = None
+    kt = det[best]["kernel_tflops"]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(det[best]["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "Hq": Hq, "Hkv": Hkv, "S": S, "D": D,
+                   "mask": "causal" if causal else "full", "tile": tile, "schedule": best,
+                   "workgroups": info["num_cu"]},
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "ratio_vs_atomic": None if ratio is None else round(ratio, 4),
+        "fastest_atomic": best_atomic,
+        "roofline": {"bound": "mfma", "achieved": round(kt, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(kt / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "bwd_kernel (persistent)", "kernel_ms": round(det[best]["kernel_ms"], 4)},
+        "schedules": {n: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in r.items()}
+                      for n, r in results.items()},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,174 @@
+/*
+ * dash_attn.h -- C ABI of the deterministic attention backward library
+ * (libdash_attn.so) for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes softmax attention forward (O, LSE) and backward
+ * (dQ, dK, dV) with the tile schedules of DASH, "Deterministic Attention
+ * Scheduling for High-Throughput".  Sources, cited by page title and section:
+ *   [summary] "Resumo Técnico: DASH – Agendamento de Atenção Determinístico
+ *             para Treinamento de LLM de Alto Rendimento" (gist.science)
+ *   [news]    "DASH如何革新LLM确定性训练" (pwwt.cn)
+ *
+ * Conventions shared by every entry point:
+ *  - Tensors are contiguous row-major BHSD: Q, O, dO, dQ are [B, Hq, S, D];
+ *    K, V, dK, dV are [B, Hkv, S, D]; all bfloat16 (2-byte) device buffers.
+ *    LSE is [B, Hq, S] float32 (natural logarithm).  Every device pointer
+ *    must be 16-byte aligned.  The caller owns all buffers.
+ *  - Query head hq reads key/value head hq / (Hq / Hkv) (grouped-query
+ *    attention with contiguous groups).
+ *  - The causal mask is top-left aligned: key j is visible to query i iff
+ *    j <= i.
+ *  - softmax_scale <= 0 selects 1/sqrt(D).
+ *  - `stream` is a hipStream_t passed as void* (NULL = default stream).
+ *    Device work is enqueued on it and the call returns without waiting;
+ *    the caller keeps buffers alive until the stream has passed the work.
+ *  - Return value: DASH_OK (0) or a negative status.  Arguments are checked
+ *    before anything is enqueued; on error nothing is launched and
+ *    dash_last_error() describes the problem.  No exception crosses the ABI.
+ *  - Supported: D in {64, 128}; S a positive multiple of the tile (64 or
+ *    128); Hq a multiple of Hkv.
+ */
+#ifndef DASH_ATTN_H
+#define DASH_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum dash_status {
+  DASH_OK = 0,
+  DASH_ERR_INVALID_ARG = -1,      /* null pointer, non-positive size, Hq % Hkv != 0 */
+  DASH_ERR_UNSUPPORTED = -2,      /* valid but not implemented: D, tile, S % tile, mask/schedule pair, gang > workgroups */
+  DASH_ERR_HIP = -3,              /* a HIP runtime call failed */
+  DASH_ERR_INVALID_SCHEDULE = -4, /* a step list failed validation */
+  DASH_ERR_TIMEOUT = -5,          /* a workgroup gave up waiting on a dQ semaphore (reported with sync_check) */
+  DASH_ERR_WORKSPACE = -6         /* caller workspace too small or misaligned */
+};
+
+enum dash_mask { DASH_MASK_FULL = 0, DASH_MASK_CAUSAL = 1 };
+
+/*
+ * Backward schedules.  The first four are deterministic: each dQ tile
+ * accumulates its key/value contributions in an order fixed by the schedule
+ * ([summary] §1: a fixed accumulation order for dQ gives bitwise
+ * reproducibility), enforced by per-dQ-tile semaphores in global memory.
+ *   SERIAL    serialized fixed-order baseline: ascending query walk,
+ *             ascending key/value order per dQ tile ([summary] §1, §4).
+ *   DESC_Q    descending query-tile walk, same order ([summary] §2.2.A).
+ *   SHIFT     full mask only: cyclic shift, the workgroup holding key/value
+ *             tile i visits query tiles i, i+1, ..., N-1, 0, ..., i-1
+ *             ([summary] §2.2.B; [news] §2.3).  A gang of N workgroups per
+ *             key/value group.
+ *   SYM_SHIFT causal mask only: tiles i and N-1-i paired on one workgroup,
+ *             dense rectangle then folded triangle ([summary] §2.2.B).  N
+ *             even; a gang of N/2 workgroups per key/value group.
+ *   ATOMIC    non-deterministic ceiling: fp32 atomic adds into dQ in any
+ *             order ([summary] §1, the non-deterministic counterpart).
+ */
+enum dash_schedule_kind {
+  DASH_SCHED_SERIAL = 0,
+  DASH_SCHED_DESC_Q = 1,
+  DASH_SCHED_SHIFT = 2,
+  DASH_SCHED_SYM_SHIFT = 3,
+  DASH_SCHED_ATOMIC = 4
+};
+
+/* Optional knobs of dash_attn_bwd.  Zero-initialise, then set struct_size. */
+typedef struct dash_bwd_opts {
+  uint32_t struct_size;      /* sizeof(dash_bwd_opts) */
+  int num_workgroups;        /* persistent workgroups; 0 = one per compute unit */
+  int tile;                  /* tile edge 64 or 128; 0 = 64 when S < 512 else 128 */
+  int atomic_walk;           /* ATOMIC only: walk of SERIAL/DESC_Q/SHIFT/SYM_SHIFT; <0 = SERIAL (full) / DESC_Q (causal) */
+  int xcd_local;             /* gang members on one chiplet where possible: 1 (default when 0) / -1 off */
+  void* workspace;           /* optional device workspace, 256-byte aligned; NULL = library-managed */
+  size_t workspace_bytes;    /* size of `workspace` (>= dash_attn_bwd_workspace_bytes) */
+  unsigned long long* stall_cycles_out; /* optional device buffer [num_workgroups][2]: cycles spent waiting
+                                           on dQ semaphores, cycles in the persistent kernel (per workgroup) */
+  unsigned long long spin_timeout_cycles; /* semaphore wait budget per wait; 0 = 2^33 cycles (~3.6 s) */
+  int sync_check;            /* 1: synchronise the stream and report DASH_ERR_TIMEOUT / HIP faults */
+  void* event_start;         /* optional hipEvent_t recorded on `stream` just before the persistent kernel */
+  void* event_stop;          /* optional hipEvent_t recorded on `stream` just after it */
+} dash_bwd_opts;
+
+/*
+ * Forward pass: O = softmax(scale * Q K^T [+ causal mask]) V and its
+ * log-sum-exp per query row.  O is bfloat16 [B,Hq,S,D], lse float32 [B,Hq,S].
+ * The backward pass takes O and lse from here.
+ */
+int dash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int Hq, int Hkv, int S, int D, float softmax_scale, int mask,
+                  void* stream);
+
+/*
+ * Backward pass: dQ, dK, dV (bfloat16) from Q, K, V, O, dO (bfloat16) and
+ * lse (float32).  Runs the Delta = rowsum(dO * O) preprocess, the persistent
+ * backward kernel (one workgroup per compute unit; each key/value tile's
+ * chain stays on one workgroup with dK/dV in registers, [summary] §2.1), and
+ * the dQ fp32 -> bf16 finalize.  For the deterministic schedules the result
+ * is bitwise identical from run to run and independent of num_workgroups.
+ * `opts` may be NULL.
+ */
+int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                  const float* lse, void* dq, void* dk, void* dv,
+                  int B, int Hq, int Hkv, int S, int D, float softmax_scale, int mask,
+                  int schedule, const dash_bwd_opts* opts, void* stream);
+
+/* Bytes of device workspace dash_attn_bwd needs for these sizes (fp32 dQ
+ * accumulator, Delta, semaphores, error word).  Returns DASH_OK or an error. */
+int dash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D, size_t* bytes);
+
+/* Delta[b,h,i] = sum_d dO[b,h,i,d] * O[b,h,i,d] in fp32 ([B*H*S] float32
+ * output), the preprocess step of the backward pass, exposed for testing. */
+int dash_attn_bwd_delta(const void* o, const void* dO, float* delta, int B, int H, int S, int D,
+                        void* stream);
+
+/* ---- host-only schedule interface (no GPU needed) ---------------------- */
+
+/* Opaque per-workgroup step lists for one problem shape. */
+typedef struct dash_schedule dash_schedule;
+
+/* Build step lists for `groups` key/value groups of g query heads each,
+ * N tiles per sequence and P workgroups.  schedule may be any of the five
+ * kinds (ATOMIC builds the walk of `atomic_walk` as in dash_bwd_opts).
+ * xcd_local != 0 places the members of a gang on indices congruent modulo
+ * the gang count.  *out receives a schedule to free with dash_schedule_free. */
+int dash_schedule_build(int mask, int schedule, int N, int g, int groups, int P, int xcd_local,
+                        int atomic_walk, dash_schedule** out);
+
+int dash_schedule_num_workgroups(const dash_schedule* s);
+long long dash_schedule_num_steps(const dash_schedule* s);
+
+/* Copy the lists out: offsets[P+1] (step index where each workgroup's list
+ * starts) and steps[4*num_steps] as (head, qi, kj, ord | flags) with
+ * flags bit 28 = first step of a chain, bit 29 = last step of a chain. */
+int dash_schedule_export(const dash_schedule* s, int32_t* offsets, int32_t* steps);
+
+/* DASH_OK, or DASH_ERR_INVALID_SCHEDULE if any step is out of range or
+ * masked, a tile pair is missing or repeated, a chain is split, a dQ tile's
+ * ordinals are not 0..count-1, or the lists can deadlock. */
+int dash_schedule_validate(const dash_schedule* s);
+
+/* Unit-cost DAG model ([news] §2.2; [summary] §2.1): each step costs c of
+ * compute then r of reduction, a reduction waits for its dQ tile's previous
+ * ordinal.  Returns makespan and total waiting time. */
+int dash_schedule_simulate(const dash_schedule* s, double c, double r, double* makespan,
+                           double* total_wait);
+
+void dash_schedule_free(dash_schedule* s);
+
+/* ---- misc -------------------------------------------------------------- */
+
+const char* dash_status_string(int status);
+/* Message of the last error raised on the calling thread ("" if none). */
+const char* dash_last_error(void);
+/* Compute units, LDS bytes per workgroup and shader clock (kHz) of a device. */
+int dash_device_info(int device, int* num_cu, int* lds_bytes, int* clock_khz);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DASH_ATTN_H */

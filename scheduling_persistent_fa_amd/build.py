@@ -1,0 +1,51 @@
+"""Build libdash_attn.so in-tree with hipcc for gfx950.
+
+``python -m scheduling_persistent_fa_amd.build`` compiles the HIP kernels, the
+C ABI and the host scheduler into ``scheduling_persistent_fa_amd/libdash_attn.so``.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libdash_attn.so")
+ARCH = "gfx950"
+
+# Packed fp32 VALU forms are disabled for device code (a host-pass warning
+# about the unknown feature is expected and harmless).
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-munsafe-fp-atomics"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def build(verbose: bool = False, resource_usage: bool = False) -> str:
+    sources = [os.path.join(CSRC, f) for f in ("kernels.hip", "api.cpp", "schedule.cpp")]
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+           "-Wall", "-Wno-unused-function", *DEVICE_FLAGS, "-o", tmp, *sources]
+    if resource_usage:
+        cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{msgs}")
+    if verbose or resource_usage:
+        print(msgs)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True, resource_usage="--resource-usage" in sys.argv)

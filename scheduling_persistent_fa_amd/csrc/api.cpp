@@ -1,0 +1,366 @@
+// C ABI of libdash_attn.so (declared in include/dash_attn.h).
+//
+// Everything is validated before anything is enqueued.  The library owns a
+// per-device cache of uploaded step lists and, when the caller passes no
+// workspace, a grow-only per-device workspace; both live until process exit.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "../../include/dash_attn.h"
+#include "kernels.hpp"
+#include "schedule.hpp"
+
+struct dash_schedule {
+  dash::Schedule s;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const std::string& msg) {
+  g_last_error = msg;
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(DASH_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+struct DeviceInfo {
+  int num_cu = 0, lds = 0, clock_khz = 0;
+};
+
+std::mutex g_mu;
+std::map<int, DeviceInfo> g_devinfo;
+
+int device_info(int dev, DeviceInfo* out) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_devinfo.find(dev);
+  if (it == g_devinfo.end()) {
+    hipDeviceProp_t p;
+    hipError_t e = hipGetDeviceProperties(&p, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    DeviceInfo d;
+    d.num_cu = p.multiProcessorCount;
+    d.lds = (int)p.sharedMemPerBlock;
+    d.clock_khz = p.clockRate;
+    it = g_devinfo.emplace(dev, d).first;
+  }
+  *out = it->second;
+  return DASH_OK;
+}
+
+// Uploaded step lists, keyed by everything that shapes them.
+struct DevSchedule {
+  int32_t* steps = nullptr;
+  int32_t* offsets = nullptr;
+  long long num_steps = 0;
+};
+using SchedKey = std::tuple<int, int, int, int, int, int, int, int, int>;  // dev, mask, kind, N, g, groups, P, xcd, walk
+std::map<SchedKey, DevSchedule> g_sched;
+
+struct Workspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::map<int, Workspace> g_ws;
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct WsLayout {
+  size_t ws_dq, delta, sem, err, total;
+};
+
+WsLayout ws_layout(int B, int Hq, int S, int D) {
+  WsLayout L;
+  const size_t rows = (size_t)B * Hq * S;
+  size_t off = 0;
+  L.ws_dq = off;
+  off = align256(off + rows * D * sizeof(float));
+  L.delta = off;
+  off = align256(off + rows * sizeof(float));
+  L.sem = off;
+  off = align256(off + (size_t)B * Hq * (S / 64) * sizeof(int));
+  L.err = off;
+  off = align256(off + 16);
+  L.total = off;
+  return L;
+}
+
+int check_common(const void* const* ptrs, int nptr, int B, int Hq, int Hkv, int S, int D, int mask) {
+  for (int i = 0; i < nptr; ++i) {
+    if (!ptrs[i]) return fail(DASH_ERR_INVALID_ARG, "null tensor pointer (argument " + std::to_string(i) + ")");
+    if (reinterpret_cast<uintptr_t>(ptrs[i]) % 16) return fail(DASH_ERR_INVALID_ARG, "tensor pointer not 16-byte aligned");
+  }
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || D <= 0) return fail(DASH_ERR_INVALID_ARG, "sizes must be positive");
+  if (Hq % Hkv) return fail(DASH_ERR_INVALID_ARG, "Hq must be a multiple of Hkv");
+  if (mask != DASH_MASK_FULL && mask != DASH_MASK_CAUSAL) return fail(DASH_ERR_INVALID_ARG, "unknown mask");
+  if (D != 64 && D != 128) return fail(DASH_ERR_UNSUPPORTED, "head dimension must be 64 or 128");
+  if (S % 64) return fail(DASH_ERR_UNSUPPORTED, "sequence length must be a multiple of 64");
+  if ((long long)B * Hq * S * D >= (1LL << 40)) return fail(DASH_ERR_UNSUPPORTED, "problem too large");
+  return DASH_OK;
+}
+
+float default_scale(float s, int D) { return s > 0.f ? s : 1.0f / std::sqrt((float)D); }
+
+}  // namespace
+
+extern "C" {
+
+const char* dash_status_string(int status) {
+  switch (status) {
+    case DASH_OK: return "ok";
+    case DASH_ERR_INVALID_ARG: return "invalid argument";
+    case DASH_ERR_UNSUPPORTED: return "unsupported";
+    case DASH_ERR_HIP: return "HIP runtime error";
+    case DASH_ERR_INVALID_SCHEDULE: return "invalid schedule";
+    case DASH_ERR_TIMEOUT: return "semaphore wait timed out";
+    case DASH_ERR_WORKSPACE: return "workspace too small or misaligned";
+    default: return "unknown status";
+  }
+}
+
+const char* dash_last_error(void) { return g_last_error.c_str(); }
+
+int dash_device_info(int device, int* num_cu, int* lds_bytes, int* clock_khz) {
+  DeviceInfo d;
+  int st = device_info(device, &d);
+  if (st) return st;
+  if (num_cu) *num_cu = d.num_cu;
+  if (lds_bytes) *lds_bytes = d.lds;
+  if (clock_khz) *clock_khz = d.clock_khz;
+  return DASH_OK;
+}
+
+int dash_schedule_build(int mask, int schedule, int N, int g, int groups, int P, int xcd_local, int atomic_walk,
+                        dash_schedule** out) {
+  if (!out) return fail(DASH_ERR_INVALID_ARG, "null output");
+  *out = nullptr;
+  auto s = std::make_unique<dash_schedule>();
+  std::string err = dash::build_schedule(mask, schedule, N, g, groups, P, xcd_local != 0, atomic_walk, &s->s);
+  if (!err.empty()) {
+    const bool bad = (N < 1 || g < 1 || groups < 1 || P < 1 || (mask != 0 && mask != 1) || schedule < 0 || schedule > 4);
+    return fail(bad ? DASH_ERR_INVALID_ARG : DASH_ERR_UNSUPPORTED, err);
+  }
+  *out = s.release();
+  return DASH_OK;
+}
+
+int dash_schedule_num_workgroups(const dash_schedule* s) { return s ? s->s.P : 0; }
+long long dash_schedule_num_steps(const dash_schedule* s) { return s ? (long long)s->s.steps.size() : 0; }
+
+int dash_schedule_export(const dash_schedule* s, int32_t* offsets, int32_t* steps) {
+  if (!s || !offsets || !steps) return fail(DASH_ERR_INVALID_ARG, "null argument");
+  std::memcpy(offsets, s->s.offsets.data(), s->s.offsets.size() * sizeof(int32_t));
+  std::memcpy(steps, s->s.steps.data(), s->s.steps.size() * sizeof(dash::StepRec));
+  return DASH_OK;
+}
+
+int dash_schedule_validate(const dash_schedule* s) {
+  if (!s) return fail(DASH_ERR_INVALID_ARG, "null schedule");
+  std::string err = dash::validate_schedule(s->s);
+  return err.empty() ? DASH_OK : fail(DASH_ERR_INVALID_SCHEDULE, err);
+}
+
+int dash_schedule_simulate(const dash_schedule* s, double c, double r, double* makespan, double* total_wait) {
+  if (!s) return fail(DASH_ERR_INVALID_ARG, "null schedule");
+  if (!dash::simulate_schedule(s->s, c, r, makespan, total_wait)) return fail(DASH_ERR_INVALID_SCHEDULE, "deadlock");
+  return DASH_OK;
+}
+
+void dash_schedule_free(dash_schedule* s) { delete s; }
+
+int dash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int S,
+                  int D, float softmax_scale, int mask, void* stream) {
+  const void* ptrs[] = {q, k, v, o, lse};
+  int st = check_common(ptrs, 5, B, Hq, Hkv, S, D, mask);
+  if (st) return st;
+  if ((long long)B * Hq > 65535) return fail(DASH_ERR_UNSUPPORTED, "B*Hq exceeds the grid limit");
+  hipError_t e = dash::launch_fwd(q, k, v, o, lse, B, Hq, Hkv, S, D, default_scale(softmax_scale, D), mask,
+                                  (hipStream_t)stream);
+  return e == hipSuccess ? DASH_OK : hip_fail(e, "forward launch");
+}
+
+int dash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D, size_t* bytes) {
+  if (!bytes) return fail(DASH_ERR_INVALID_ARG, "null output");
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || D <= 0) return fail(DASH_ERR_INVALID_ARG, "sizes must be positive");
+  *bytes = ws_layout(B, Hq, S, D).total;
+  return DASH_OK;
+}
+
+int dash_attn_bwd_delta(const void* o, const void* dO, float* delta, int B, int H, int S, int D, void* stream) {
+  const void* ptrs[] = {o, dO, delta};
+  int st = check_common(ptrs, 3, B, H, H, S, D, DASH_MASK_FULL);
+  if (st) return st;
+  hipError_t e = dash::launch_delta(o, dO, delta, (long long)B * H * S, D, nullptr, 0, nullptr, 0, (hipStream_t)stream);
+  return e == hipSuccess ? DASH_OK : hip_fail(e, "delta launch");
+}
+
+int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                  void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int S, int D, float softmax_scale, int mask,
+                  int schedule, const dash_bwd_opts* opts, void* stream) {
+  const void* ptrs[] = {q, k, v, o, dO, lse, dq, dk, dv};
+  int st = check_common(ptrs, 9, B, Hq, Hkv, S, D, mask);
+  if (st) return st;
+  if (schedule < DASH_SCHED_SERIAL || schedule > DASH_SCHED_ATOMIC) return fail(DASH_ERR_INVALID_ARG, "unknown schedule");
+  dash_bwd_opts op;
+  std::memset(&op, 0, sizeof(op));
+  if (opts) {
+    if (opts->struct_size == 0 || opts->struct_size > sizeof(dash_bwd_opts))
+      return fail(DASH_ERR_INVALID_ARG, "dash_bwd_opts.struct_size must be sizeof(dash_bwd_opts)");
+    std::memcpy(&op, opts, opts->struct_size);
+  }
+  hipStream_t strm = (hipStream_t)stream;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  DeviceInfo di;
+  st = device_info(dev, &di);
+  if (st) return st;
+
+  const int T = op.tile ? op.tile : (S < 512 ? 64 : 128);
+  if (T != 64 && T != 128) return fail(DASH_ERR_UNSUPPORTED, "tile must be 64 or 128");
+  if (S % T) return fail(DASH_ERR_UNSUPPORTED, "sequence length must be a multiple of the tile");
+  const int N = S / T;
+  const int P = op.num_workgroups > 0 ? op.num_workgroups : di.num_cu;
+  if (op.num_workgroups < 0) return fail(DASH_ERR_INVALID_ARG, "negative workgroup count");
+  const int g = Hq / Hkv;
+  const int groups = B * Hkv;
+  const bool atomic = schedule == DASH_SCHED_ATOMIC;
+  const int xcd = op.xcd_local >= 0 ? 1 : 0;
+  const int walk = atomic ? op.atomic_walk : -1;
+  const float scale = default_scale(softmax_scale, D);
+
+  // Co-residency: the semaphore waits need every workgroup resident at once.
+  if (!atomic) {
+    bool fits = false;
+    e = dash::bwd_kernel_fits(D, T, false, di.num_cu, P, &fits);
+    if (e != hipSuccess) return hip_fail(e, "occupancy query");
+    if (!fits) return fail(DASH_ERR_UNSUPPORTED, "persistent grid larger than the co-resident capacity");
+  }
+
+  // Step lists (validated once, then cached on the device).
+  DevSchedule ds;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    SchedKey key{dev, mask, schedule, N, g, groups, P, xcd, atomic ? (walk < 0 ? -1 : walk) : -1};
+    auto it = g_sched.find(key);
+    if (it == g_sched.end()) {
+      dash::Schedule s;
+      std::string err = dash::build_schedule(mask, schedule, N, g, groups, P, xcd != 0, walk, &s);
+      if (!err.empty()) return fail(DASH_ERR_UNSUPPORTED, err);
+      err = dash::validate_schedule(s);
+      if (!err.empty()) return fail(DASH_ERR_INVALID_SCHEDULE, err);
+      DevSchedule d;
+      d.num_steps = (long long)s.steps.size();
+      e = hipMalloc((void**)&d.steps, std::max<size_t>(16, s.steps.size() * sizeof(dash::StepRec)));
+      if (e != hipSuccess) return hip_fail(e, "hipMalloc(steps)");
+      e = hipMalloc((void**)&d.offsets, s.offsets.size() * sizeof(int32_t));
+      if (e != hipSuccess) { (void)hipFree(d.steps); return hip_fail(e, "hipMalloc(offsets)"); }
+      e = hipMemcpy(d.steps, s.steps.data(), s.steps.size() * sizeof(dash::StepRec), hipMemcpyHostToDevice);
+      if (e == hipSuccess)
+        e = hipMemcpy(d.offsets, s.offsets.data(), s.offsets.size() * sizeof(int32_t), hipMemcpyHostToDevice);
+      if (e != hipSuccess) { (void)hipFree(d.steps); (void)hipFree(d.offsets); return hip_fail(e, "hipMemcpy(schedule)"); }
+      it = g_sched.emplace(key, d).first;
+    }
+    ds = it->second;
+  }
+
+  // Workspace.
+  const WsLayout L = ws_layout(B, Hq, S, D);
+  char* ws = nullptr;
+  if (op.workspace) {
+    if (reinterpret_cast<uintptr_t>(op.workspace) % 256) return fail(DASH_ERR_WORKSPACE, "workspace not 256-byte aligned");
+    if (op.workspace_bytes < L.total) return fail(DASH_ERR_WORKSPACE, "workspace too small");
+    ws = (char*)op.workspace;
+  } else {
+    std::lock_guard<std::mutex> lk(g_mu);
+    Workspace& w = g_ws[dev];
+    if (w.bytes < L.total) {
+      // The previous buffer may still be in use by queued work on any stream.
+      if (w.ptr) {
+        e = hipDeviceSynchronize();
+        if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+        (void)hipFree(w.ptr);
+        w.ptr = nullptr;
+        w.bytes = 0;
+      }
+      e = hipMalloc(&w.ptr, L.total);
+      if (e != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
+      w.bytes = L.total;
+    }
+    ws = (char*)w.ptr;
+  }
+  float* ws_dq = (float*)(ws + L.ws_dq);
+  float* delta = (float*)(ws + L.delta);
+  int* sem = (int*)(ws + L.sem);
+  int* err = (int*)(ws + L.err);
+  const long long rows = (long long)B * Hq * S;
+  const long long n_sem = (long long)((L.err - L.sem) / 4) + 4;  // semaphores, padding and the error word
+
+  e = dash::launch_delta(o, dO, delta, rows, D, sem, n_sem, atomic ? ws_dq : nullptr, atomic ? rows * D : 0, strm);
+  if (e != hipSuccess) return hip_fail(e, "preprocess launch");
+
+  dash::BwdLaunch bl;
+  bl.q = q;
+  bl.k = k;
+  bl.v = v;
+  bl.dO = dO;
+  bl.lse = lse;
+  bl.delta = delta;
+  bl.ws = ws_dq;
+  bl.sem = sem;
+  bl.err = err;
+  bl.dk = dk;
+  bl.dv = dv;
+  bl.steps = ds.steps;
+  bl.offsets = ds.offsets;
+  bl.stall = op.stall_cycles_out;
+  const unsigned long long budget_cycles = op.spin_timeout_cycles ? op.spin_timeout_cycles : (1ULL << 33);
+  // wait budget in 100 MHz real-time ticks, from shader cycles at the device clock
+  bl.spin_ticks = (long long)((double)budget_cycles * 1e5 / std::max(1, di.clock_khz));
+  if (bl.spin_ticks < 1) bl.spin_ticks = 1;
+  bl.scale = scale;
+  bl.S = S;
+  bl.D = D;
+  bl.T = T;
+  bl.g = g;
+  bl.causal = mask;
+  bl.P = P;
+  bl.atomic = atomic;
+  if (op.event_start) {
+    e = hipEventRecord((hipEvent_t)op.event_start, strm);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(start)");
+  }
+  e = dash::launch_bwd(bl, strm);
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
+  if (op.event_stop) {
+    e = hipEventRecord((hipEvent_t)op.event_stop, strm);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(stop)");
+  }
+  e = dash::launch_dq_finalize(ws_dq, dq, rows * D, D, scale, strm);
+  if (e != hipSuccess) return hip_fail(e, "finalize launch");
+
+  if (op.sync_check) {
+    e = hipStreamSynchronize(strm);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    int h_err = 0;
+    e = hipMemcpy(&h_err, err, sizeof(int), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpy(error word)");
+    if (h_err) return fail(DASH_ERR_TIMEOUT, "a workgroup timed out waiting on a dQ semaphore");
+  }
+  return DASH_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,675 @@
+// HIP kernels for softmax attention forward and the DASH deterministic
+// backward pass on gfx950 (MI355X, CDNA4).
+//
+// Sources (cited by page title and section):
+//   [summary] "Resumo Técnico: DASH – Agendamento de Atenção Determinístico
+//             para Treinamento de LLM de Alto Rendimento" (gist.science)
+//   [news]    "DASH如何革新LLM确定性训练" (pwwt.cn)
+//
+// Matrix-core conventions (v_mfma_f32_32x32x16_bf16, wave64):
+//   A (32 x 16): lane l holds row l%32, k = 8*(l/32) .. +7
+//   B (16 x 32): lane l holds col l%32, k = 8*(l/32) .. +7
+//   C (32 x 32): lane l, register r holds col l%32, row 8*(r/4) + 4*(l/32) + r%4
+// Contractions may use any permutation of k as long as A and B agree.  A C
+// tile whose rows are the contraction index therefore feeds the next MFMA
+// directly: registers 8e..8e+7 form the operand for rows
+// 16e + {4h..4h+3, 8+4h..8+4h+3} (h = l/32), and the partner operand is read
+// from LDS with the gfx950 transposing read ds_read_b64_tr_b16, which gives
+// each lane four consecutive rows of one column of a 4 x 16 row-major block.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kernels.hpp"
+
+namespace dash {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Four bf16 values, one column of a 4 x 16 block, per lane (see header).
+__device__ __forceinline__ bf16x4 lds_tr4(const LDS char* p) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)p);
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ bf16x8 lds_row8(const LDS char* p) { return *(const LDS bf16x8*)p; }
+
+// Operand from two transposing reads: rows row0 + (l%16)/4 and row0 + 4 + (l%16)/4
+// (pitch in bytes), columns col0 + 16*((l/16)%2) + 4*(l%4) (bf16 elements).
+// Lane l receives rows row0..row0+3 then row0+4..row0+7 of column col0 + l%32.
+__device__ __forceinline__ bf16x8 lds_tr8_consecutive(const LDS char* base, int pitch_bytes, int row0, int col0,
+                                                      int lane) {
+  const int r = row0 + ((lane & 15) >> 2);
+  const int c = col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const LDS char* p = base + r * pitch_bytes + c * 2;
+  return cat8(lds_tr4(p), lds_tr4(p + 4 * pitch_bytes));
+}
+
+// Same, but the second group of four rows starts 8 rows after the first:
+// the k-permutation of a C tile reused as an operand.
+__device__ __forceinline__ bf16x8 lds_tr8_split(const LDS char* base, int pitch_bytes, int row0, int col0,
+                                                int lane) {
+  const int r = row0 + ((lane & 15) >> 2);
+  const int c = col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const LDS char* p = base + r * pitch_bytes + c * 2;
+  return cat8(lds_tr4(p), lds_tr4(p + 8 * pitch_bytes));
+}
+
+__device__ __forceinline__ bf16x8 pack8(const f32x16& x, int first) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (__bf16)x[first + e];
+  return r;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// ---------------------------------------------------------------------------
+// Forward: O = softmax(scale Q K^T) V, LSE (natural log).  One workgroup per
+// (32*NW query rows, query head); each wave keeps 32 query rows of Q in
+// registers and computes S^T = K Q^T so that a lane owns one query row; the
+// online softmax ([summary] §2: the backward consumes the forward's LSE) is
+// then per lane plus one exchange between the two half-waves.
+// ---------------------------------------------------------------------------
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                                                         const __bf16* __restrict__ v, __bf16* __restrict__ o,
+                                                         float* __restrict__ lse, int Hq, int g, int S,
+                                                         float scale_log2, int causal) {
+  constexpr int KVT = 64;               // key/value rows per LDS tile
+  constexpr int PITCH = (D + 8) * 2;    // bytes per LDS row (16-byte pad)
+  constexpr int TILE_BYTES = KVT * PITCH;
+  constexpr int DC = D / 16;            // 16-wide d chunks
+  constexpr int DB = D / 32;            // 32-wide d blocks
+  constexpr int NT = 64 * NW;
+  constexpr int CHUNKS = KVT * D / 8;   // 16-byte chunks per K or V tile
+  constexpr int CPT = CHUNKS / NT;      // chunks per thread
+  __shared__ __attribute__((aligned(16))) char smem[4 * TILE_BYTES];
+  LDS char* base = (LDS char*)smem;
+
+  const int lane = lane_id(), w = wave_id(), h2 = lane >> 5, c32 = lane & 31;
+  const int head = blockIdx.y;  // b * Hq + hq
+  const int kvh = head / g;
+  const int q_base = blockIdx.x * 32 * NW;
+  const int q_row = q_base + 32 * w + c32;  // this lane's query row
+  const __bf16* qh = q + (size_t)head * S * D;
+  const __bf16* kh = k + (size_t)kvh * S * D;
+  const __bf16* vh = v + (size_t)kvh * S * D;
+
+  bf16x8 qb[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) qb[c] = *(const bf16x8*)(qh + (size_t)q_row * D + 16 * c + 8 * h2);
+
+  const int n_tiles = causal ? (q_base + 32 * NW - 1) / KVT + 1 : S / KVT;
+
+  bf16x8 pk[CPT], pv[CPT];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ch = threadIdx.x + i * NT, row = ch / (D / 8), col = (ch % (D / 8)) * 8;
+      pk[i] = *(const bf16x8*)(kh + (size_t)(t * KVT + row) * D + col);
+      pv[i] = *(const bf16x8*)(vh + (size_t)(t * KVT + row) * D + col);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ch = threadIdx.x + i * NT, row = ch / (D / 8), col = (ch % (D / 8)) * 8;
+      *(LDS bf16x8*)(base + (2 * buf) * TILE_BYTES + row * PITCH + col * 2) = pk[i];
+      *(LDS bf16x8*)(base + (2 * buf + 1) * TILE_BYTES + row * PITCH + col * 2) = pv[i];
+    }
+  };
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  float m_run = -INFINITY, l_part = 0.f;
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    const LDS char* sk = base + (2 * buf) * TILE_BYTES;
+    const LDS char* sv = base + (2 * buf + 1) * TILE_BYTES;
+    if (t + 1 < n_tiles) load_tile(t + 1);
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < DC; ++c) s[kb] = mfma32(lds_row8(sk + (kb * 32 + c32) * PITCH + (16 * c + 8 * h2) * 2), qb[c], s[kb]);
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = s[kb][r] * scale_log2;
+        if (causal) {
+          const int kv = t * KVT + kb * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+          if (kv > q_row) x = -INFINITY;
+        }
+        s[kb][r] = x;
+        mt = fmaxf(mt, x);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(s[kb][r] - m_new);
+        s[kb][r] = p;
+        rs += p;
+      }
+    l_part = l_part * alpha + rs;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+    // O^T[d][q] += V^T[d][kv] P^T[kv][q]
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const bf16x8 bp = pack8(s[kb], 8 * e);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          acc[db] = mfma32(lds_tr8_split(sv, PITCH, kb * 32 + 16 * e + 4 * h2, db * 32, lane), bp, acc[db]);
+      }
+    if (t + 1 < n_tiles) {
+      __syncthreads();  // everyone done with the other buffer's previous tile
+      store_tile(buf ^ 1);
+      __syncthreads();
+    }
+  }
+  const float l_tot = l_part + __shfl_xor(l_part, 32);
+  const float inv = 1.f / l_tot;
+  __bf16* oh = o + (size_t)head * S * D + (size_t)q_row * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf16x4 out;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[i] = (__bf16)(acc[db][4 * j + i] * inv);
+      *(bf16x4*)(oh + db * 32 + 8 * j + 4 * h2) = out;
+    }
+  if (h2 == 0) lse[(size_t)head * S + q_row] = (m_run + __log2f(l_tot)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------
+// Backward preprocess: Delta_i = sum_d dO_id O_id (fp32), and zeroing of the
+// semaphores, the error word and (for the atomic variant) the dQ workspace.
+// Cleared with stores from this kernel rather than memset so that the whole
+// backward can be captured into a graph.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void delta_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ dO,
+                                                     float* __restrict__ delta, long long rows,
+                                                     int* __restrict__ zero_i32, long long n_zero_i32,
+                                                     float* __restrict__ zero_f32, long long n_zero_f32) {
+  constexpr int TPR = D / 8;  // threads per row
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long row = gid / TPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const int col = (int)(gid % TPR) * 8;
+    const bf16x8 a = *(const bf16x8*)(o + row * D + col);
+    const bf16x8 b = *(const bf16x8*)(dO + row * D + col);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += (float)a[e] * (float)b[e];
+  }
+#pragma unroll
+  for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  if (row < rows && (gid % TPR) == 0) delta[row] = acc;
+  const long long stride = (long long)gridDim.x * 256;
+  for (long long i = gid; i < n_zero_i32; i += stride) zero_i32[i] = 0;
+  for (long long i = gid * 4; i < n_zero_f32; i += stride * 4) *(f32x4*)(zero_f32 + i) = f32x4{};
+}
+
+// ---------------------------------------------------------------------------
+// Persistent backward.  One workgroup per compute unit walks its step list
+// (built on the host); each chain (key/value tile x its query heads) runs
+// contiguously with dK/dV in registers ([summary] §2.1).  Per 64-row query
+// block the workgroup adds its dQ partial into the fp32 workspace either in
+// the order fixed by the step's ordinal -- waiting on a per-block semaphore
+// in global memory with acquire/release at device scope -- or, for the
+// non-deterministic ceiling, with fp32 atomic adds.
+//
+// Workspace dQ layout: per (query head, 64-row block) a 64 x D fp32 block
+// stored as 32 x 32 MFMA C tiles (tile = qb * D/32 + db), each tile as
+// [r/4][lane][r%4] so that every lane moves float4s and a wave moves 1 KiB
+// contiguous per access.
+// ---------------------------------------------------------------------------
+struct BwdArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const __bf16* dO;
+  const float* lse;
+  const float* delta;
+  float* ws;
+  int* sem;
+  int* err;
+  __bf16* dk;
+  __bf16* dv;
+  const int4* steps;
+  const int* offsets;
+  unsigned long long* stall;
+  long long spin_ticks;
+  float scale;       // softmax scale
+  float scale_log2;  // softmax scale * log2(e)
+  int S, g, causal;
+};
+
+template <int D, int T, bool ATOMIC>
+__global__ __launch_bounds__(2 * T, 1) void bwd_kernel(BwdArgs a) {
+  constexpr int NW = T / 32;          // waves; each owns 32 key/value rows
+  constexpr int NT = 64 * NW;
+  constexpr int M = 64;               // query rows per sub-step
+  constexpr int SUBS = T / M;
+  constexpr int DC = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int TPW = 2 * DB / NW;    // dQ C tiles per wave
+  constexpr int PQ = (D + 8) * 2;     // LDS pitch (bytes) of Q / dO / K rows
+  constexpr int PS = (M + 8) * 2;     // LDS pitch (bytes) of dS^T rows
+  constexpr int QBUF = M * PQ;
+  constexpr int OFF_Q = 0;                     // [2][M][PQ]
+  constexpr int OFF_DO = OFF_Q + 2 * QBUF;     // [2][M][PQ]
+  constexpr int OFF_K = OFF_DO + 2 * QBUF;     // [T][PQ]
+  constexpr int OFF_DS = OFF_K + T * PQ;       // [T][PS]  dS^T
+  constexpr int OFF_LSE = OFF_DS + T * PS;     // [2][M] f32, log2 domain
+  constexpr int OFF_DEL = OFF_LSE + 2 * M * 4; // [2][M] f32
+  constexpr int OFF_FLAG = OFF_DEL + 2 * M * 4;
+  constexpr int SMEM = OFF_FLAG + 16;
+  constexpr int QCH = M * D / 8 / NT;          // 16-byte chunks per thread of one Q (or dO) block
+  static_assert(QCH >= 1 && (M * D / 8) % NT == 0, "tile split");
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
+  LDS char* base = (LDS char*)smem;
+  volatile LDS int* s_flag = (volatile LDS int*)(base + OFF_FLAG);
+
+  const int lane = lane_id(), w = wave_id(), h2 = lane >> 5, c32 = lane & 31;
+  const int kv0 = 32 * w;  // first key/value row of this wave within the tile
+  const int wg = blockIdx.x;
+  const int beg = a.offsets[wg], end = a.offsets[wg + 1];
+  const int S = a.S, g = a.g;
+  const int nblk = S / M;  // 64-row blocks per head
+  unsigned long long stall = 0;
+  const unsigned long long t_start = __builtin_amdgcn_s_memtime();
+
+  // Prefetch registers for the next Q/dO block and its LSE/Delta.
+  bf16x8 pq[QCH], pdo[QCH];
+  float plse = 0.f, pdel = 0.f;
+  auto load_block = [&](int head, int row0) {
+    const __bf16* qh = a.q + ((size_t)head * S + row0) * D;
+    const __bf16* doh = a.dO + ((size_t)head * S + row0) * D;
+#pragma unroll
+    for (int i = 0; i < QCH; ++i) {
+      const int ch = threadIdx.x + i * NT;
+      pq[i] = *(const bf16x8*)(qh + (size_t)ch * 8);
+      pdo[i] = *(const bf16x8*)(doh + (size_t)ch * 8);
+    }
+    if (threadIdx.x < M) plse = a.lse[(size_t)head * S + row0 + threadIdx.x] * kLog2e;
+    else if (threadIdx.x < 2 * M) pdel = a.delta[(size_t)head * S + row0 + threadIdx.x - M];
+  };
+  auto store_block = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < QCH; ++i) {
+      const int ch = threadIdx.x + i * NT, row = ch / (D / 8), col = (ch % (D / 8)) * 8;
+      *(LDS bf16x8*)(base + OFF_Q + buf * QBUF + row * PQ + col * 2) = pq[i];
+      *(LDS bf16x8*)(base + OFF_DO + buf * QBUF + row * PQ + col * 2) = pdo[i];
+    }
+    if (threadIdx.x < M) *(LDS float*)(base + OFF_LSE + (buf * M + threadIdx.x) * 4) = plse;
+    else if (threadIdx.x < 2 * M) *(LDS float*)(base + OFF_DEL + (buf * M + threadIdx.x - M) * 4) = pdel;
+  };
+
+  bf16x8 kb[DC], vb[DC];
+  f32x16 dk_acc[DB], dv_acc[DB];
+  int buf = 0;
+  if (beg < end) {
+    const int4 r0 = a.steps[beg];
+    load_block(r0.x, r0.y * T);
+    store_block(0);
+  }
+  bool aborted = false;
+
+  for (int i = beg; i < end && !aborted; ++i) {
+    const int4 rec = a.steps[i];
+    const int head = rec.x, qi = rec.y, kj = rec.z, ordf = rec.w;
+    const int ord = ordf & ((1 << 28) - 1);
+    const bool first = ordf & (1 << 28), last = ordf & (1 << 29);
+    const int kvh = head / g;
+    const __bf16* kh = a.k + ((size_t)kvh * S + (size_t)kj * T) * D;
+    const __bf16* vh = a.v + ((size_t)kvh * S + (size_t)kj * T) * D;
+    if (first) {
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        kb[c] = *(const bf16x8*)(kh + (size_t)(kv0 + c32) * D + 16 * c + 8 * h2);
+        vb[c] = *(const bf16x8*)(vh + (size_t)(kv0 + c32) * D + 16 * c + 8 * h2);
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        dk_acc[db] = f32x16{};
+        dv_acc[db] = f32x16{};
+      }
+      __syncthreads();  // previous chain's dQ contraction is done with sK
+      for (int ch = threadIdx.x; ch < T * D / 8; ch += NT) {
+        const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
+        *(LDS bf16x8*)(base + OFF_K + row * PQ + col * 2) = *(const bf16x8*)(kh + (size_t)row * D + col);
+      }
+    }
+    const bool diag = a.causal && (qi == kj);
+
+    for (int sub = 0; sub < SUBS; ++sub) {
+      __syncthreads();  // B1: Q/dO/LSE/Delta of this block (and sK) visible
+      // Prefetch the next block while this one is computed.
+      int nhead = -1, nrow = 0;
+      if (sub + 1 < SUBS) {
+        nhead = head;
+        nrow = qi * T + (sub + 1) * M;
+      } else if (i + 1 < end) {
+        const int4 nr = a.steps[i + 1];
+        nhead = nr.x;
+        nrow = nr.y * T;
+      }
+      if (nhead >= 0) load_block(nhead, nrow);
+
+      const LDS char* sq = base + OFF_Q + buf * QBUF;
+      const LDS char* sdo = base + OFF_DO + buf * QBUF;
+      const LDS float* slse = (const LDS float*)(base + OFF_LSE + buf * M * 4);
+      const LDS float* sdel = (const LDS float*)(base + OFF_DEL + buf * M * 4);
+
+      // S = Q K^T and dP = dO V^T for this wave's 32 key/value columns.
+      f32x16 s[2], dp[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        s[qb] = f32x16{};
+        dp[qb] = f32x16{};
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+          const int off = (qb * 32 + c32) * PQ + (16 * c + 8 * h2) * 2;
+          s[qb] = mfma32(lds_row8(sq + off), kb[c], s[qb]);
+          dp[qb] = mfma32(lds_row8(sdo + off), vb[c], dp[qb]);
+        }
+      }
+      // P = exp2(S*scale*log2e - LSE*log2e); dS = P * (dP - Delta).
+      const int kv_local = kv0 + c32;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 l4 = *(const LDS f32x4*)(slse + qb * 32 + 8 * j + 4 * h2);
+          const f32x4 d4 = *(const LDS f32x4*)(sdel + qb * 32 + 8 * j + 4 * h2);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * j + e;
+            float p = __builtin_amdgcn_exp2f(s[qb][r] * a.scale_log2 - l4[e]);
+            if (diag && kv_local > sub * M + qb * 32 + 8 * j + 4 * h2 + e) p = 0.f;
+            s[qb][r] = p;
+            dp[qb][r] = p * (dp[qb][r] - d4[e]);
+          }
+        }
+      // dS^T to LDS for the dQ contraction (4 consecutive query rows per store).
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          bf16x4 t4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) t4[e] = (__bf16)dp[qb][4 * j + e];
+          *(LDS bf16x4*)(base + OFF_DS + kv_local * PS + (qb * 32 + 8 * j + 4 * h2) * 2) = t4;
+        }
+      // dV += P^T dO, dK += dS^T Q (contraction over the 64 query rows).
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const bf16x8 ap = pack8(s[qb], 8 * e);
+          const bf16x8 ads = pack8(dp[qb], 8 * e);
+          const int row0 = qb * 32 + 16 * e + 4 * h2;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            dv_acc[db] = mfma32(ap, lds_tr8_split(sdo, PQ, row0, db * 32, lane), dv_acc[db]);
+            dk_acc[db] = mfma32(ads, lds_tr8_split(sq, PQ, row0, db * 32, lane), dk_acc[db]);
+          }
+        }
+      // The other buffer is free (read before B1): stage the prefetched block.
+      if (nhead >= 0) store_block(buf ^ 1);
+      __syncthreads();  // B2: dS^T complete
+
+      // dQ partial = dS K over all T key/value rows of the tile.
+      f32x16 dq[TPW];
+#pragma unroll
+      for (int ti = 0; ti < TPW; ++ti) {
+        const int t_idx = w + NW * ti, qb = t_idx / DB, db = t_idx % DB;
+        dq[ti] = f32x16{};
+#pragma unroll
+        for (int c = 0; c < T / 16; ++c) {
+          const bf16x8 ads = lds_tr8_consecutive(base + OFF_DS, PS, 16 * c + 8 * h2, qb * 32, lane);
+          const bf16x8 bk = lds_tr8_consecutive(base + OFF_K, PQ, 16 * c + 8 * h2, db * 32, lane);
+          dq[ti] = mfma32(ads, bk, dq[ti]);
+        }
+      }
+
+      const int blk = qi * SUBS + sub;
+      float* wsb = a.ws + ((size_t)head * nblk + blk) * (size_t)(M * D);
+      if constexpr (ATOMIC) {
+#pragma unroll
+        for (int ti = 0; ti < TPW; ++ti) {
+          const int t_idx = w + NW * ti;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float* p = wsb + t_idx * 1024 + j * 256 + lane * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              __hip_atomic_fetch_add(p + e, dq[ti][4 * j + e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+      } else {
+        int* semp = a.sem + (size_t)head * nblk + blk;
+        if (threadIdx.x == 0) {
+          int ab = 0;
+          if (ord > 0) {
+            const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+            const long long deadline = (long long)__builtin_amdgcn_s_memrealtime() + a.spin_ticks;
+            while (__hip_atomic_load(semp, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != ord) {
+              if (__hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) { ab = 1; break; }
+              if ((long long)__builtin_amdgcn_s_memrealtime() > deadline) {
+                __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                ab = 1;
+                break;
+              }
+              __builtin_amdgcn_s_sleep(1);
+            }
+            stall += __builtin_amdgcn_s_memtime() - t0;
+          }
+          *s_flag = ab;
+        }
+        __syncthreads();  // B3: predecessor's dQ visible to the whole workgroup
+        if (*s_flag) {
+          aborted = true;
+          break;
+        }
+#pragma unroll
+        for (int ti = 0; ti < TPW; ++ti) {
+          const int t_idx = w + NW * ti;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            f32x4* p = (f32x4*)(wsb + t_idx * 1024 + j * 256 + lane * 4);
+            f32x4 x = {dq[ti][4 * j], dq[ti][4 * j + 1], dq[ti][4 * j + 2], dq[ti][4 * j + 3]};
+            if (ord > 0) x += *p;
+            *p = x;
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __syncthreads();  // B4: every wave's dQ stores issued and fenced
+        if (threadIdx.x == 0) __hip_atomic_store(semp, ord + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      buf ^= 1;
+    }
+
+    if (last && !aborted) {
+      // Chain epilogue: single writer of dK (scaled) and dV for this tile.
+      __bf16* dkh = a.dk + ((size_t)kvh * S + (size_t)kj * T) * D;
+      __bf16* dvh = a.dv + ((size_t)kvh * S + (size_t)kj * T) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = kv0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+          dkh[(size_t)row * D + db * 32 + c32] = (__bf16)(dk_acc[db][r] * a.scale);
+          dvh[(size_t)row * D + db * 32 + c32] = (__bf16)dv_acc[db][r];
+        }
+    }
+  }
+  if (a.stall && threadIdx.x == 0) {
+    a.stall[2 * wg] = stall;
+    a.stall[2 * wg + 1] = __builtin_amdgcn_s_memtime() - t_start;
+  }
+}
+
+// dQ = bf16(scale * workspace), undoing the fragment order.
+template <int D>
+__global__ __launch_bounds__(256) void dq_finalize_kernel(const float* __restrict__ ws, __bf16* __restrict__ dq,
+                                                          long long n_f4, float scale) {
+  const long long f = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (f >= n_f4) return;
+  constexpr int F4_PER_BLOCK = 64 * D / 4;
+  const long long blk = f / F4_PER_BLOCK;  // (head, 64-row block)
+  const int rem = (int)(f % F4_PER_BLOCK);
+  const int tile = rem / 256, j = (rem % 256) / 64, l = rem % 64;
+  const int qb = tile / (D / 32), db = tile % (D / 32);
+  const f32x4 x = *(const f32x4*)(ws + f * 4);
+  const int col = db * 32 + (l & 31);
+  const int row0 = qb * 32 + 8 * j + 4 * (l >> 5);
+  __bf16* out = dq + (size_t)blk * 64 * D;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) out[(size_t)(row0 + e) * D + col] = (__bf16)(x[e] * scale);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Host launchers.
+// ---------------------------------------------------------------------------
+hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                      int S, int D, float scale, int causal, hipStream_t st) {
+  const int g = Hq / Hkv;
+  const float sl2 = scale * kLog2e;
+  const bool big = (S % 128) == 0;
+  dim3 grid(S / (big ? 128 : 64), B * Hq);
+  auto qp = (const __bf16*)q;
+  auto kp = (const __bf16*)k;
+  auto vp = (const __bf16*)v;
+  auto op = (__bf16*)o;
+  if (D == 128) {
+    if (big) hipLaunchKernelGGL((fwd_kernel<128, 4>), grid, dim3(256), 0, st, qp, kp, vp, op, lse, Hq, g, S, sl2, causal);
+    else hipLaunchKernelGGL((fwd_kernel<128, 2>), grid, dim3(128), 0, st, qp, kp, vp, op, lse, Hq, g, S, sl2, causal);
+  } else {
+    if (big) hipLaunchKernelGGL((fwd_kernel<64, 4>), grid, dim3(256), 0, st, qp, kp, vp, op, lse, Hq, g, S, sl2, causal);
+    else hipLaunchKernelGGL((fwd_kernel<64, 2>), grid, dim3(128), 0, st, qp, kp, vp, op, lse, Hq, g, S, sl2, causal);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_delta(const void* o, const void* dO, float* delta, long long rows, int D, int* zero_i32,
+                        long long n_zero_i32, float* zero_f32, long long n_zero_f32, hipStream_t st) {
+  const long long threads = rows * (D / 8);
+  long long blocks = (threads + 255) / 256;
+  const long long zb = (std::max(n_zero_i32, n_zero_f32 / 4) + 255) / 256;
+  if (blocks < zb) blocks = std::min<long long>(zb, 65536);
+  if (blocks < 1) blocks = 1;
+  if (D == 128)
+    hipLaunchKernelGGL((delta_kernel<128>), dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)o, (const __bf16*)dO,
+                       delta, rows, zero_i32, n_zero_i32, zero_f32, n_zero_f32);
+  else
+    hipLaunchKernelGGL((delta_kernel<64>), dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)o, (const __bf16*)dO,
+                       delta, rows, zero_i32, n_zero_i32, zero_f32, n_zero_f32);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdLaunch& L, hipStream_t st) {
+  BwdArgs a;
+  a.q = (const __bf16*)L.q;
+  a.k = (const __bf16*)L.k;
+  a.v = (const __bf16*)L.v;
+  a.dO = (const __bf16*)L.dO;
+  a.lse = L.lse;
+  a.delta = L.delta;
+  a.ws = L.ws;
+  a.sem = L.sem;
+  a.err = L.err;
+  a.dk = (__bf16*)L.dk;
+  a.dv = (__bf16*)L.dv;
+  a.steps = (const int4*)L.steps;
+  a.offsets = L.offsets;
+  a.stall = L.stall;
+  a.spin_ticks = L.spin_ticks;
+  a.scale = L.scale;
+  a.scale_log2 = L.scale * kLog2e;
+  a.S = L.S;
+  a.g = L.g;
+  a.causal = L.causal;
+  dim3 grid(L.P);
+#define DASH_BWD_CASE(D_, T_)                                                                     \
+  if (L.D == D_ && L.T == T_) {                                                                   \
+    if (L.atomic) hipLaunchKernelGGL((bwd_kernel<D_, T_, true>), grid, dim3(2 * T_), 0, st, a);   \
+    else hipLaunchKernelGGL((bwd_kernel<D_, T_, false>), grid, dim3(2 * T_), 0, st, a);           \
+    return hipGetLastError();                                                                     \
+  }
+  DASH_BWD_CASE(128, 128)
+  DASH_BWD_CASE(64, 128)
+  DASH_BWD_CASE(128, 64)
+  DASH_BWD_CASE(64, 64)
+#undef DASH_BWD_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t bwd_kernel_fits(int D, int T, bool atomic, int num_cu, int P, bool* fits) {
+  int per_cu = 0;
+  hipError_t e = hipErrorInvalidValue;
+#define DASH_OCC_CASE(D_, T_)                                                                                  \
+  if (D == D_ && T == T_)                                                                                      \
+    e = atomic ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_kernel<D_, T_, true>, 2 * T_, 0)    \
+               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_kernel<D_, T_, false>, 2 * T_, 0);
+  DASH_OCC_CASE(128, 128)
+  DASH_OCC_CASE(64, 128)
+  DASH_OCC_CASE(128, 64)
+  DASH_OCC_CASE(64, 64)
+#undef DASH_OCC_CASE
+  if (e != hipSuccess) return e;
+  *fits = (long long)per_cu * num_cu >= P;
+  return hipSuccess;
+}
+
+hipError_t launch_dq_finalize(const float* ws, void* dq, long long elems, int D, float scale, hipStream_t st) {
+  const long long n_f4 = elems / 4;
+  const unsigned blocks = (unsigned)((n_f4 + 255) / 256);
+  if (D == 128) hipLaunchKernelGGL((dq_finalize_kernel<128>), dim3(blocks), dim3(256), 0, st, ws, (__bf16*)dq, n_f4, scale);
+  else hipLaunchKernelGGL((dq_finalize_kernel<64>), dim3(blocks), dim3(256), 0, st, ws, (__bf16*)dq, n_f4, scale);
+  return hipGetLastError();
+}
+
+}  // namespace dash

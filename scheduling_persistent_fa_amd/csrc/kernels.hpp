@@ -1,0 +1,39 @@
+// Host-side launchers of the gfx950 attention kernels (kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace dash {
+
+struct BwdLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dO;
+  const float* lse;
+  const float* delta;
+  float* ws;           // fp32 dQ accumulator, fragment order
+  int* sem;            // one per (query head, 64-row block)
+  int* err;            // error word (non-zero: a wait timed out)
+  void* dk;
+  void* dv;
+  const int32_t* steps;    // 4 ints per step
+  const int32_t* offsets;  // P + 1
+  unsigned long long* stall;
+  long long spin_ticks;    // wait budget in 100 MHz real-time ticks
+  float scale;
+  int S, D, T, g, causal, P;
+  bool atomic;
+};
+
+hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                      int S, int D, float scale, int causal, hipStream_t st);
+hipError_t launch_delta(const void* o, const void* dO, float* delta, long long rows, int D, int* zero_i32,
+                        long long n_zero_i32, float* zero_f32, long long n_zero_f32, hipStream_t st);
+hipError_t launch_bwd(const BwdLaunch& L, hipStream_t st);
+hipError_t bwd_kernel_fits(int D, int T, bool atomic, int num_cu, int P, bool* fits);
+hipError_t launch_dq_finalize(const float* ws, void* dq, long long elems, int D, float scale, hipStream_t st);
+
+}  // namespace dash

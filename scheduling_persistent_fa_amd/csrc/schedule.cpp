@@ -1,0 +1,262 @@
+// Host-side DASH schedule generator, validator and DAG simulator.
+//
+// Schedules ("Resumo Técnico: DASH ...", §2.2; "DASH如何革新LLM确定性训练", §2.3):
+//  SERIAL    each chain walks query tiles ascending; a dQ tile accumulates
+//            key/value tiles in ascending order (the serialized baseline).
+//  DESC_Q    same accumulation order, query tiles walked descending (§2.2.A).
+//  SHIFT     full mask: a gang of N workgroups per key/value group; the
+//            workgroup keeping key/value tile p visits query tiles
+//            p, p+1, ..., N-1, 0, ..., p-1, so the t-th contribution to every
+//            dQ tile arrives at step t and no two workgroups meet (§2.2.B).
+//  SYM_SHIFT causal mask: a gang of N/2 workgroups; member p keeps tile p
+//            through a dense rectangle phase (query tiles N/2..N-1, shifted)
+//            and its own triangle part, then tile N-1-p through the folded
+//            triangle, N+1 steps per member (§2.2.B, symmetric shift).
+// Gang schedules order each dQ tile's contributions by lock-step time (the
+// step's position in its workgroup's list for that group), ties by kj.
+#include "schedule.hpp"
+
+#include <algorithm>
+#include <queue>
+#include <utility>
+
+namespace dash {
+namespace {
+
+struct Triple {
+  int32_t head, qi, kj;
+};
+
+// Append one chain with first/last flags.
+void push_chain(std::vector<StepRec>& dst, const std::vector<Triple>& chain,
+                const std::vector<int32_t>& ords) {
+  const size_t n = chain.size();
+  for (size_t i = 0; i < n; ++i) {
+    int32_t f = ords[i];
+    if (i == 0) f |= kFirstFlag;
+    if (i + 1 == n) f |= kLastFlag;
+    dst.push_back({chain[i].head, chain[i].qi, chain[i].kj, f});
+  }
+}
+
+std::string build_list_scheduled(const Schedule& s, std::vector<std::vector<StepRec>>& per_wg) {
+  // Chains in (group, kj) order go to the workgroup with the least work so
+  // far (unit cost per step; ties to the lowest index).
+  using Slot = std::pair<long long, int>;
+  std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> heap;
+  for (int w = 0; w < s.P; ++w) heap.push({0, w});
+  std::vector<Triple> chain;
+  std::vector<int32_t> ords;
+  for (int grp = 0; grp < s.groups; ++grp) {
+    for (int kj = 0; kj < s.N; ++kj) {
+      const int lo = (s.mask == kMaskCausal) ? kj : 0;
+      chain.clear();
+      ords.clear();
+      for (int u = 0; u < s.g; ++u) {
+        for (int t = 0; t < s.N - lo; ++t) {
+          const int qi = (s.walk == kDescQ) ? (s.N - 1 - t) : (lo + t);
+          chain.push_back({grp * s.g + u, qi, kj});
+          ords.push_back(kj);  // ascending key/value order for every dQ tile
+        }
+      }
+      Slot top = heap.top();
+      heap.pop();
+      push_chain(per_wg[top.second], chain, ords);
+      heap.push({top.first + static_cast<long long>(chain.size()), top.second});
+    }
+  }
+  return {};
+}
+
+std::string build_gang(const Schedule& s, std::vector<std::vector<StepRec>>& per_wg) {
+  const int N = s.N;
+  const int gang = (s.walk == kShift) ? N : N / 2;
+  const int n_gangs = s.P / gang;
+  if (n_gangs < 1) return "gang of " + std::to_string(gang) + " workgroups exceeds " + std::to_string(s.P);
+  // Per member: its chains as (kj, walk of one head).
+  std::vector<std::vector<std::pair<int, std::vector<int>>>> member(gang);
+  for (int p = 0; p < gang; ++p) {
+    if (s.walk == kShift) {
+      std::vector<int> w(N);
+      for (int t = 0; t < N; ++t) w[t] = (p + t) % N;
+      member[p].push_back({p, std::move(w)});
+    } else {
+      const int M = gang;
+      std::vector<int> a, b;
+      for (int t = 0; t < M; ++t) a.push_back(M + (p + t) % M);   // dense rectangle
+      for (int q = p; q < M; ++q) a.push_back(q);                  // own triangle part
+      for (int q = N - 1; q >= N - 1 - p; --q) b.push_back(q);     // folded triangle
+      member[p].push_back({p, std::move(a)});
+      member[p].push_back({N - 1 - p, std::move(b)});
+    }
+  }
+  // Ordinals: rank of (position, kj) among the contributors of each
+  // (head-in-group u, qi).  Identical for every group, so computed once.
+  std::vector<std::vector<std::pair<int, int>>> bucket(static_cast<size_t>(s.g) * N);
+  for (int p = 0; p < gang; ++p) {
+    int pos = 0;
+    for (auto& ch : member[p])
+      for (int u = 0; u < s.g; ++u)
+        for (int qi : ch.second) bucket[static_cast<size_t>(u) * N + qi].push_back({pos++, ch.first});
+  }
+  std::vector<int32_t> rank(static_cast<size_t>(s.g) * N * N, -1);  // [u][qi][kj]
+  for (int u = 0; u < s.g; ++u)
+    for (int qi = 0; qi < N; ++qi) {
+      auto& v = bucket[static_cast<size_t>(u) * N + qi];
+      std::sort(v.begin(), v.end());
+      for (size_t r = 0; r < v.size(); ++r)
+        rank[(static_cast<size_t>(u) * N + qi) * N + v[r].second] = static_cast<int32_t>(r);
+    }
+  std::vector<Triple> chain;
+  std::vector<int32_t> ords;
+  for (int grp = 0; grp < s.groups; ++grp) {
+    const int gi = grp % n_gangs;
+    for (int p = 0; p < gang; ++p) {
+      const int w = s.xcd_local ? p * n_gangs + gi : gi * gang + p;
+      for (auto& ch : member[p]) {
+        chain.clear();
+        ords.clear();
+        for (int u = 0; u < s.g; ++u)
+          for (int qi : ch.second) {
+            chain.push_back({grp * s.g + u, qi, ch.first});
+            ords.push_back(rank[(static_cast<size_t>(u) * N + qi) * N + ch.first]);
+          }
+        push_chain(per_wg[w], chain, ords);
+      }
+    }
+  }
+  return {};
+}
+
+}  // namespace
+
+std::string build_schedule(int mask, int kind, int N, int g, int groups, int P, bool xcd_local,
+                           int atomic_walk, Schedule* out) {
+  if (N < 1 || g < 1 || groups < 1 || P < 1) return "sizes must be positive";
+  if (mask != kMaskFull && mask != kMaskCausal) return "unknown mask";
+  if (kind < kSerial || kind > kAtomic) return "unknown schedule";
+  if (N > 32767) return "too many tiles";
+  int walk = kind;
+  if (kind == kAtomic) {
+    walk = (atomic_walk < 0) ? (mask == kMaskCausal ? kDescQ : kSerial) : atomic_walk;
+    if (walk < kSerial || walk > kSymShift) return "unknown atomic walk";
+  }
+  if (walk == kShift && mask != kMaskFull) return "shift scheduling needs a full mask";
+  if (walk == kSymShift && mask != kMaskCausal) return "symmetric shift needs a causal mask";
+  if (walk == kSymShift && (N % 2)) return "symmetric shift needs an even tile count";
+  Schedule s;
+  s.mask = mask;
+  s.kind = kind;
+  s.walk = walk;
+  s.N = N;
+  s.g = g;
+  s.groups = groups;
+  s.P = P;
+  s.xcd_local = xcd_local;
+  std::vector<std::vector<StepRec>> per_wg(P);
+  std::string err = (walk == kSerial || walk == kDescQ) ? build_list_scheduled(s, per_wg) : build_gang(s, per_wg);
+  if (!err.empty()) return err;
+  s.offsets.resize(P + 1);
+  size_t total = 0;
+  for (int w = 0; w < P; ++w) {
+    s.offsets[w] = static_cast<int32_t>(total);
+    total += per_wg[w].size();
+  }
+  s.offsets[P] = static_cast<int32_t>(total);
+  s.steps.reserve(total);
+  for (auto& v : per_wg) s.steps.insert(s.steps.end(), v.begin(), v.end());
+  *out = std::move(s);
+  return {};
+}
+
+bool simulate_schedule(const Schedule& s, double c, double r, double* makespan, double* total_wait) {
+  const size_t tiles = static_cast<size_t>(s.g) * s.groups * s.N;
+  std::vector<int32_t> count(tiles, 0);
+  std::vector<double> done_at(tiles, 0.0);
+  std::vector<int32_t> idx(s.P, 0);
+  std::vector<double> t(s.P, 0.0);
+  long long remaining = static_cast<long long>(s.steps.size());
+  double wait = 0.0;
+  while (remaining > 0) {
+    bool progressed = false;
+    for (int w = 0; w < s.P; ++w) {
+      const int32_t end = s.offsets[w + 1];
+      while (s.offsets[w] + idx[w] < end) {
+        const StepRec& st = s.steps[s.offsets[w] + idx[w]];
+        const size_t key = static_cast<size_t>(st.head) * s.N + st.qi;
+        const int32_t ord = st.ordflags & kOrdMask;
+        if (count[key] != ord) break;
+        const double ready = t[w] + c;
+        const double start = std::max(ready, done_at[key]);
+        wait += start - ready;
+        t[w] = start + r;
+        done_at[key] = t[w];
+        count[key] = ord + 1;
+        ++idx[w];
+        --remaining;
+        progressed = true;
+      }
+    }
+    if (!progressed) return false;
+  }
+  double mk = 0.0;
+  for (double x : t) mk = std::max(mk, x);
+  if (makespan) *makespan = mk;
+  if (total_wait) *total_wait = wait;
+  return true;
+}
+
+std::string validate_schedule(const Schedule& s) {
+  const int N = s.N;
+  const long long heads = static_cast<long long>(s.g) * s.groups;
+  if (static_cast<int>(s.offsets.size()) != s.P + 1) return "offset table size";
+  if (s.offsets[0] != 0 || s.offsets[s.P] != static_cast<int32_t>(s.steps.size())) return "offset table bounds";
+  std::vector<uint8_t> seen(static_cast<size_t>(heads) * N * N, 0);
+  std::vector<int32_t> owner(static_cast<size_t>(s.groups) * N, -1);
+  long long covered = 0;
+  for (int w = 0; w < s.P; ++w) {
+    if (s.offsets[w + 1] < s.offsets[w]) return "offsets decrease";
+    long long run = -1;  // chain key (group * N + kj) of the open chain
+    for (int32_t i = s.offsets[w]; i < s.offsets[w + 1]; ++i) {
+      const StepRec& st = s.steps[i];
+      if (st.head < 0 || st.head >= heads || st.qi < 0 || st.qi >= N || st.kj < 0 || st.kj >= N)
+        return "step index out of range";
+      if (s.mask == kMaskCausal && st.kj > st.qi) return "masked tile pair scheduled";
+      const size_t pair = (static_cast<size_t>(st.head) * N + st.qi) * N + st.kj;
+      if (seen[pair]) return "tile pair scheduled twice";
+      seen[pair] = 1;
+      ++covered;
+      const long long ck = static_cast<long long>(st.head / s.g) * N + st.kj;
+      if (st.ordflags & kFirstFlag) {
+        if (run >= 0) return "chain not closed before the next starts";
+        if (owner[ck] >= 0) return "chain split";
+        owner[ck] = w;
+        run = ck;
+      }
+      if (run != ck) return "chain interrupted";
+      if (st.ordflags & kLastFlag) run = -1;
+    }
+    if (run >= 0) return "list ends inside a chain";
+  }
+  long long expect = 0;
+  for (int qi = 0; qi < N; ++qi) expect += (s.mask == kMaskCausal) ? qi + 1 : N;
+  if (covered != expect * heads) return "coverage mismatch";
+  for (int32_t o : owner)
+    if (o < 0) return "missing chain";
+  // ordinals of each dQ tile: exactly 0..count-1
+  std::vector<int32_t> cnt(static_cast<size_t>(heads) * N, 0);
+  std::vector<uint8_t> ordseen(static_cast<size_t>(heads) * N * N, 0);
+  for (const StepRec& st : s.steps) {
+    const int32_t ord = st.ordflags & kOrdMask;
+    const int32_t lim = (s.mask == kMaskCausal) ? st.qi + 1 : N;
+    if (ord < 0 || ord >= lim) return "ordinal out of range";
+    const size_t k = (static_cast<size_t>(st.head) * N + st.qi) * N + ord;
+    if (ordseen[k]) return "ordinal repeated";
+    ordseen[k] = 1;
+  }
+  double mk, wt;
+  if (!simulate_schedule(s, 1.0, 1.0, &mk, &wt)) return "deadlock";
+  return {};
+}
+
+}  // namespace dash

@@ -1,0 +1,48 @@
+// Host-side DASH schedule generator, validator and DAG simulator.
+// Plain C++17, no HIP dependency.
+//
+// A step is one (query head, query tile qi, key/value tile kj) pair.  A chain
+// is every step of one key/value tile of one key/value group (the group's g
+// query heads in ascending order); it runs contiguously on one workgroup so
+// dK/dV stay in registers ("Resumo Técnico: DASH ...", §2.1, restrictions).
+// Each step carries its ordinal: the position of its contribution in the
+// accumulation sequence of its dQ tile, which fixes the summation order.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+namespace dash {
+
+enum : int { kMaskFull = 0, kMaskCausal = 1 };
+enum : int { kSerial = 0, kDescQ = 1, kShift = 2, kSymShift = 3, kAtomic = 4 };
+
+constexpr int32_t kFirstFlag = 1 << 28;
+constexpr int32_t kLastFlag = 1 << 29;
+constexpr int32_t kOrdMask = (1 << 28) - 1;
+
+struct StepRec {
+  int32_t head;      // b * Hq + hq
+  int32_t qi;        // query tile
+  int32_t kj;        // key/value tile
+  int32_t ordflags;  // ordinal | kFirstFlag | kLastFlag
+};
+
+struct Schedule {
+  int mask = 0, kind = 0, walk = 0;  // walk: the ordering schedule (== kind unless kind is ATOMIC)
+  int N = 0, g = 1, groups = 1, P = 1;
+  bool xcd_local = true;
+  std::vector<int32_t> offsets;  // P + 1
+  std::vector<StepRec> steps;
+};
+
+// Returns an empty string on success, else the reason (unsupported combination).
+std::string build_schedule(int mask, int kind, int N, int g, int groups, int P, bool xcd_local,
+                           int atomic_walk, Schedule* out);
+// Empty string if valid, else the first violation found.
+std::string validate_schedule(const Schedule& s);
+// Unit-cost DAG simulation; returns false on deadlock.
+bool simulate_schedule(const Schedule& s, double c, double r, double* makespan, double* total_wait);
+
+}  // namespace dash

@@ -1,0 +1,54 @@
+"""Python view of the library's host-side schedule generator (no GPU needed)."""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+
+from . import _lib
+
+
+class Schedule:
+    """Per-workgroup step lists built by ``dash_schedule_build``.
+
+    ``offsets`` has P+1 entries; ``steps`` is [num_steps, 4] int32 with columns
+    (head, qi, kj, ord | flags).
+    """
+
+    def __init__(self, mask: int, schedule: int, N: int, g: int, groups: int, P: int,
+                 xcd_local: bool = True, atomic_walk: int = -1):
+        L = _lib.lib()
+        h = ctypes.c_void_p()
+        _lib.check(L.dash_schedule_build(mask, schedule, N, g, groups, P, int(bool(xcd_local)), atomic_walk,
+                                         ctypes.byref(h)))
+        self._h = h
+        self.P = L.dash_schedule_num_workgroups(h)
+        self.num_steps = L.dash_schedule_num_steps(h)
+        self.offsets = np.zeros(self.P + 1, dtype=np.int32)
+        self.steps = np.zeros((max(1, self.num_steps), 4), dtype=np.int32)
+        _lib.check(L.dash_schedule_export(h, self.offsets.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                          self.steps.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
+        self.steps = self.steps[: self.num_steps]
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            _lib.lib().dash_schedule_free(h)
+            self._h = None
+
+    def validate(self) -> None:
+        _lib.check(_lib.lib().dash_schedule_validate(self._h))
+
+    def simulate(self, c: float, r: float):
+        mk, wt = ctypes.c_double(), ctypes.c_double()
+        _lib.check(_lib.lib().dash_schedule_simulate(self._h, c, r, ctypes.byref(mk), ctypes.byref(wt)))
+        return mk.value, wt.value
+
+    def lists(self):
+        """Per workgroup: list of (head, qi, kj, ord, first, last) tuples."""
+        out = []
+        for w in range(self.P):
+            rows = self.steps[self.offsets[w]: self.offsets[w + 1]]
+            out.append([(int(h), int(q), int(k), int(o & _lib.ORD_MASK), bool(o & _lib.FIRST_FLAG),
+                         bool(o & _lib.LAST_FLAG)) for h, q, k, o in rows])
+        return out

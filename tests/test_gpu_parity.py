@@ -1,0 +1,140 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Small shapes span several tiles and are compared element by element; the
+workload shapes at full size are compared on sampled rows, in the launch
+configuration the benchmark times (one workgroup per compute unit).
+Tolerance: max|err| / max|ref| <= 2e-2 for dQ, dK, dV and O; LSE and Delta
+within 2e-2 * max(1, max|ref|).
+"""
+import numpy as np
+import pytest
+
+from oracle import attention as A
+from tests._gpu_helpers import TOL, DeviceProblem, rel_err, say, to_f64
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from scheduling_persistent_fa_amd import _lib  # noqa: E402
+from scheduling_persistent_fa_amd.attention import (ATOMIC, DESC_Q, SERIAL, SHIFT, SYM_SHIFT, attn_bwd,  # noqa: E402
+                                                    attn_fwd, bwd_delta, make_opts)
+
+
+def _schedules(causal, N):
+    det = [SERIAL, DESC_Q] + ([SYM_SHIFT] if causal and N % 2 == 0 else []) + ([] if causal else [SHIFT])
+    return det + [ATOMIC]
+
+
+SMALL = [
+    # (name, B, Hq, Hkv, S, D, causal, tile, std, workgroups)
+    ("c1_full_s256_d64_shift_4wg", 1, 1, 1, 256, 64, False, 64, 1.0, 4),
+    ("full_d128_n4", 1, 2, 2, 512, 128, False, 128, 1.0, 0),
+    ("causal_d128_n4", 1, 2, 2, 512, 128, True, 128, 1.0, 0),
+    ("gqa4_causal_d128_n4", 2, 8, 2, 512, 128, True, 128, 0.5, 0),
+    ("full_d64_n8", 1, 3, 3, 1024, 64, False, 128, 1.0, 0),
+    ("causal_d64_t64_n6", 2, 2, 1, 384, 64, True, 64, 1.0, 0),
+    ("causal_d128_t64_n5_odd", 1, 2, 2, 320, 128, True, 64, 1.0, 0),
+    ("full_d64_t64_n5_few_wg", 1, 2, 1, 320, 64, False, 64, 1.0, 7),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_shapes_match_oracle(case):
+    name, B, Hq, Hkv, S, D, causal, tile, std, wgs = case
+    say(f"[parity] {name}: B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} causal={causal} tile={tile} wgs={wgs}")
+    pb = DeviceProblem(B, Hq, Hkv, S, D, causal, std=std)
+    ref = A.backward(pb.f64("q"), pb.f64("k"), pb.f64("v"), pb.f64("do"), pb.scale, causal)
+    o, lse = attn_fwd(pb.q, pb.k, pb.v, causal)
+    torch.cuda.synchronize()
+    assert rel_err(to_f64(o), ref["o"]) <= TOL
+    assert np.abs(to_f64(lse) - ref["lse"]).max() <= TOL * max(1.0, np.abs(ref["lse"]).max())
+    delta = bwd_delta(o, pb.do)
+    torch.cuda.synchronize()
+    assert np.abs(to_f64(delta) - ref["delta"]).max() <= TOL * max(1.0, np.abs(ref["delta"]).max())
+    N = S // tile
+    for sched in _schedules(causal, N):
+        if sched == SHIFT and wgs and wgs < N:
+            continue
+        say(f"  schedule {_lib.SCHEDULE_NAMES[sched]}")
+        opts = make_opts(num_workgroups=wgs, tile=tile, sync_check=True)
+        dq, dk, dv = attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, causal, sched, opts=opts)
+        torch.cuda.synchronize()
+        for nm, got in (("dq", dq), ("dk", dk), ("dv", dv)):
+            e = rel_err(to_f64(got), ref[nm])
+            assert e <= TOL, (name, _lib.SCHEDULE_NAMES[sched], nm, e)
+
+
+FULL_SIZE = [
+    ("c2_causal_s2048_d128", 4, 16, 16, 2048, 128, True, 1.0, [SERIAL, DESC_Q, SYM_SHIFT, ATOMIC]),
+    ("c3_full_s4096_d64", 2, 24, 24, 4096, 64, False, 1.0, [SERIAL, DESC_Q, SHIFT, ATOMIC]),
+    ("c4_full_s16384_d128", 1, 16, 16, 16384, 128, False, 1.0, [SERIAL, DESC_Q, SHIFT, ATOMIC]),
+    ("c4_causal_s16384_d128", 1, 16, 16, 16384, 128, True, 1.0, [SERIAL, DESC_Q, SYM_SHIFT, ATOMIC]),
+    ("c5_gqa_causal_s8192_d128", 1, 32, 8, 8192, 128, True, 0.5, [SERIAL, DESC_Q, SYM_SHIFT, ATOMIC]),
+]
+
+
+@pytest.mark.parametrize("case", FULL_SIZE, ids=[c[0] for c in FULL_SIZE])
+def test_workload_shapes_on_sampled_rows(case):
+    name, B, Hq, Hkv, S, D, causal, std, scheds = case
+    say(f"[parity-full] {name}")
+    pb = DeviceProblem(B, Hq, Hkv, S, D, causal, std=std)
+    o, lse = attn_fwd(pb.q, pb.k, pb.v, causal)
+    torch.cuda.synchronize()
+    q64, k64, v64, do64 = pb.f64("q"), pb.f64("k"), pb.f64("v"), pb.f64("do")
+    g = Hq // Hkv
+    b, hk = B - 1, Hkv - 1                      # last batch, last kv head
+    heads = list(range(hk * g, hk * g + g))
+    rows = sorted({0, 1, 127, 128, S // 2 + 5, S - 129, S - 1})
+    stats = {hq: A.head_stats(q64, k64, v64, do64, b, hq, pb.scale, causal) for hq in heads}
+    say("  oracle stats done")
+    ref_dq = A.dq_rows(q64, k64, v64, do64, b, heads[-1], rows, pb.scale, causal)
+    ref_dk, ref_dv = A.dkdv_rows(q64, k64, v64, do64, b, hk, rows, pb.scale, causal, stats=stats)
+    lse_ref = stats[heads[-1]][0]
+    got_lse = to_f64(lse[b, heads[-1]])
+    assert np.abs(got_lse - lse_ref).max() <= TOL * max(1.0, np.abs(lse_ref).max())
+    for sched in scheds:
+        say(f"  schedule {_lib.SCHEDULE_NAMES[sched]}")
+        dq, dk, dv = attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, causal, sched, opts=make_opts(sync_check=True))
+        torch.cuda.synchronize()
+        e_dq = rel_err(to_f64(dq[b, heads[-1], rows]), ref_dq)
+        e_dk = rel_err(to_f64(dk[b, hk, rows]), ref_dk)
+        e_dv = rel_err(to_f64(dv[b, hk, rows]), ref_dv)
+        say(f"    rel err dq {e_dq:.2e} dk {e_dk:.2e} dv {e_dv:.2e}")
+        assert max(e_dq, e_dk, e_dv) <= TOL
+        # every output finite
+        for t in (dq, dk, dv):
+            assert torch.isfinite(t.float()).all()
+
+
+def test_unsupported_shapes_are_rejected_before_launch():
+    pb = DeviceProblem(1, 1, 1, 320, 64, True)
+    o, lse = attn_fwd(pb.q, pb.k, pb.v, True)
+    with pytest.raises(_lib.DashError) as ei:  # 320 is not a multiple of the 128 tile
+        attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, True, SERIAL, opts=make_opts(tile=128))
+    assert ei.value.status == _lib.ERR_UNSUPPORTED
+    with pytest.raises(_lib.DashError) as ei:  # shift needs a full mask
+        attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, True, SHIFT, opts=make_opts(tile=64))
+    assert ei.value.status == _lib.ERR_UNSUPPORTED
+    with pytest.raises(_lib.DashError) as ei:  # symmetric shift needs an even tile count (N = 5)
+        attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, True, SYM_SHIFT, opts=make_opts(tile=64))
+    assert ei.value.status == _lib.ERR_UNSUPPORTED
+    pf = DeviceProblem(1, 1, 1, 256, 64, False)
+    of, lf = attn_fwd(pf.q, pf.k, pf.v, False)
+    with pytest.raises(_lib.DashError) as ei:  # gang of 4 does not fit 2 workgroups
+        attn_bwd(pf.q, pf.k, pf.v, of, pf.do, lf, False, SHIFT, opts=make_opts(tile=64, num_workgroups=2))
+    assert ei.value.status == _lib.ERR_UNSUPPORTED
+
+
+def test_wait_budget_exhaustion_is_reported_and_recovers():
+    # A one-cycle wait budget makes the first waiting workgroup give up; every
+    # workgroup then leaves its loop and the call reports a timeout.
+    pb = DeviceProblem(1, 2, 2, 2048, 128, False)
+    o, lse = attn_fwd(pb.q, pb.k, pb.v, False)
+    with pytest.raises(_lib.DashError) as ei:
+        attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, False, SERIAL,
+                 opts=make_opts(spin_timeout_cycles=1, sync_check=True))
+    assert ei.value.status == _lib.ERR_TIMEOUT
+    ref = A.backward(pb.f64("q"), pb.f64("k"), pb.f64("v"), pb.f64("do"), pb.scale, False)
+    dq, dk, dv = attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, False, SERIAL, opts=make_opts(sync_check=True))
+    torch.cuda.synchronize()
+    assert rel_err(to_f64(dq), ref["dq"]) <= TOL and rel_err(to_f64(dk), ref["dk"]) <= TOL

@@ -1,0 +1,112 @@
+"""CPU tests of libdash_attn.so: it loads, exports every declared symbol, and
+its host-side schedule generator matches the schedule oracle exactly."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import schedules as Sch
+from scheduling_persistent_fa_amd import _lib
+from scheduling_persistent_fa_amd.schedule import Schedule
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_symbol():
+    header = open(os.path.join(ROOT, "include", "dash_attn.h")).read()
+    declared = set(re.findall(r"\b(dash_[a-z_]+)\s*\(", header))
+    assert declared == set(_lib.EXPORTS)
+    L = _lib.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    L = _lib.lib()
+    assert L.dash_status_string(0) == b"ok"
+    assert L.dash_status_string(_lib.ERR_TIMEOUT) == b"semaphore wait timed out"
+
+
+def _oracle_tuples(lists):
+    return [[(s.head, s.qi, s.kj, s.ord, s.first, s.last) for s in l] for l in lists]
+
+
+CASES = [
+    (Sch.FULL, Sch.SERIAL, 4, 1, 1, 4), (Sch.FULL, Sch.SHIFT, 4, 1, 1, 4), (Sch.CAUSAL, Sch.SYM_SHIFT, 4, 1, 1, 2),
+    (Sch.FULL, Sch.SERIAL, 16, 1, 8, 256), (Sch.FULL, Sch.DESC_Q, 16, 2, 3, 20),
+    (Sch.CAUSAL, Sch.SERIAL, 16, 1, 64, 256), (Sch.CAUSAL, Sch.DESC_Q, 16, 1, 64, 256),
+    (Sch.CAUSAL, Sch.SYM_SHIFT, 16, 1, 64, 256), (Sch.FULL, Sch.SHIFT, 32, 1, 48, 256),
+    (Sch.CAUSAL, Sch.SYM_SHIFT, 64, 4, 8, 256), (Sch.CAUSAL, Sch.DESC_Q, 64, 4, 8, 256),
+    (Sch.FULL, Sch.SHIFT, 6, 3, 5, 13), (Sch.CAUSAL, Sch.SYM_SHIFT, 10, 2, 3, 11),
+]
+
+
+@pytest.mark.parametrize("mask,sched,N,g,groups,P", CASES)
+@pytest.mark.parametrize("xcd", [True, False])
+def test_host_schedule_matches_oracle_exactly(mask, sched, N, g, groups, P, xcd):
+    lib_s = Schedule(mask, sched, N, g, groups, P, xcd_local=xcd)
+    lib_s.validate()
+    ora = Sch.build(mask, sched, N, g, groups, P, xcd_local=xcd)
+    assert lib_s.lists() == _oracle_tuples(ora)
+
+
+@pytest.mark.parametrize("mask,sched,N,g,groups,P", CASES[:8])
+def test_host_simulator_matches_oracle(mask, sched, N, g, groups, P):
+    lib_s = Schedule(mask, sched, N, g, groups, P)
+    ora = Sch.build(mask, sched, N, g, groups, P)
+    for c, r in ((1.0, 1.0), (2.5, 0.75)):
+        assert lib_s.simulate(c, r) == pytest.approx(Sch.simulate(ora, c, r), rel=1e-12, abs=1e-9)
+
+
+def test_full_size_schedules_validate():
+    # the workloads' shapes: (mask, schedule, N, g, groups) with 256 workgroups
+    for mask, sched, N, g, groups in [(1, 0, 16, 1, 64), (1, 1, 16, 1, 64), (1, 3, 16, 1, 64),
+                                      (0, 0, 32, 1, 48), (0, 2, 32, 1, 48), (0, 2, 128, 1, 16),
+                                      (0, 1, 128, 1, 16), (1, 3, 128, 1, 16), (1, 1, 128, 1, 16),
+                                      (1, 3, 64, 4, 8), (1, 0, 64, 4, 8)]:
+        s = Schedule(mask, sched, N, g, groups, 256)
+        s.validate()
+        expect = g * groups * (N * N if mask == 0 else N * (N + 1) // 2)
+        assert s.num_steps == expect
+
+
+def test_atomic_walks_follow_their_base_schedule():
+    for walk in (_lib.SERIAL, _lib.DESC_Q, _lib.SYM_SHIFT):
+        a = Schedule(_lib.MASK_CAUSAL, _lib.ATOMIC, 8, 1, 4, 16, atomic_walk=walk)
+        b = Schedule(_lib.MASK_CAUSAL, walk, 8, 1, 4, 16)
+        assert np.array_equal(a.steps, b.steps)
+    d = Schedule(_lib.MASK_FULL, _lib.ATOMIC, 8, 1, 4, 16)  # default full-mask walk: serial
+    assert np.array_equal(d.steps, Schedule(_lib.MASK_FULL, _lib.SERIAL, 8, 1, 4, 16).steps)
+
+
+def test_schedule_build_rejects_bad_input():
+    for args, status in [((1, 2, 4, 1, 1, 4), _lib.ERR_UNSUPPORTED), ((0, 3, 4, 1, 1, 4), _lib.ERR_UNSUPPORTED),
+                         ((1, 3, 5, 1, 1, 4), _lib.ERR_UNSUPPORTED), ((0, 2, 8, 1, 1, 4), _lib.ERR_UNSUPPORTED),
+                         ((0, 0, 0, 1, 1, 4), _lib.ERR_INVALID_ARG), ((0, 9, 4, 1, 1, 4), _lib.ERR_INVALID_ARG)]:
+        with pytest.raises(_lib.DashError) as ei:
+            Schedule(*args)
+        assert ei.value.status == status
+
+
+def test_bwd_argument_errors_need_no_gpu():
+    L = _lib.lib()
+    vp = ctypes.c_void_p
+    good = [vp(4096 * (i + 1)) for i in range(9)]
+    # null pointer
+    st = L.dash_attn_bwd(*([vp(0)] + good[1:]), 1, 1, 1, 128, 64, 0.0, 0, 0, None, None)
+    assert st == _lib.ERR_INVALID_ARG
+    # Hq not a multiple of Hkv
+    assert L.dash_attn_bwd(*good, 1, 3, 2, 128, 64, 0.0, 0, 0, None, None) == _lib.ERR_INVALID_ARG
+    # unsupported head dimension / sequence length
+    assert L.dash_attn_bwd(*good, 1, 1, 1, 128, 96, 0.0, 0, 0, None, None) == _lib.ERR_UNSUPPORTED
+    assert L.dash_attn_bwd(*good, 1, 1, 1, 100, 64, 0.0, 0, 0, None, None) == _lib.ERR_UNSUPPORTED
+    # misaligned pointer
+    bad = list(good)
+    bad[3] = vp(4096 + 8)
+    assert L.dash_attn_bwd(*bad, 1, 1, 1, 128, 64, 0.0, 0, 0, None, None) == _lib.ERR_INVALID_ARG
+    assert b"aligned" in L.dash_last_error()
+    n = ctypes.c_size_t()
+    assert L.dash_attn_bwd_workspace_bytes(2, 24, 24, 4096, 64, ctypes.byref(n)) == 0
+    assert n.value >= 2 * 24 * 4096 * 64 * 4
