@@ -80,6 +80,8 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& x, int first) {
   return r;
 }
 
+constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
@@ -260,8 +262,19 @@ __global__ __launch_bounds__(256) void delta_kernel(const __bf16* __restrict__ o
 //
 // Workspace dQ layout: per (query head, 64-row block) a 64 x D fp32 block
 // stored as 32 x 32 MFMA C tiles (tile = qb * D/32 + db), each tile as
-// [r/4][lane][r%4] so that every lane moves float4s and a wave moves 1 KiB
-// contiguous per access.
+// [register][lane], so one wave access covers 256 contiguous bytes.
+//
+// Ordering protocol of the deterministic schedules.  The workspace and the
+// semaphores are only touched with device-scope relaxed atomic loads and
+// stores, which bypass the chiplet-local caches that are not coherent across
+// the device; no cache write-back or invalidate is issued.  A workgroup
+//   1. spins (one lane) until sem == ordinal, then a workgroup barrier;
+//   2. reads the block (ordinal > 0), adds its partial, writes it back;
+//   3. at the next sub-step's second barrier -- after every wave has waited
+//      for all of its outstanding vector memory operations, so the writes
+//      are complete at device scope -- one lane stores sem = ordinal + 1.
+// Deferring step 3 overlaps the write latency with the next sub-step's
+// compute; it never waits on another workgroup, so no cycle can form.
 // ---------------------------------------------------------------------------
 struct BwdArgs {
   const __bf16* q;
@@ -293,19 +306,20 @@ __global__ __launch_bounds__(2 * T, 1) void bwd_kernel(BwdArgs a) {
   constexpr int DC = D / 16;
   constexpr int DB = D / 32;
   constexpr int TPW = 2 * DB / NW;    // dQ C tiles per wave
+  constexpr int KC = T / 16;          // 16-row key/value chunks of the dQ contraction
   constexpr int PQ = (D + 8) * 2;     // LDS pitch (bytes) of Q / dO / K rows
   constexpr int PS = (M + 8) * 2;     // LDS pitch (bytes) of dS^T rows
   constexpr int QBUF = M * PQ;
-  constexpr int OFF_Q = 0;                     // [2][M][PQ]
-  constexpr int OFF_DO = OFF_Q + 2 * QBUF;     // [2][M][PQ]
-  constexpr int OFF_K = OFF_DO + 2 * QBUF;     // [T][PQ]
-  constexpr int OFF_DS = OFF_K + T * PQ;       // [T][PS]  dS^T
-  constexpr int OFF_LSE = OFF_DS + T * PS;     // [2][M] f32, log2 domain
-  constexpr int OFF_DEL = OFF_LSE + 2 * M * 4; // [2][M] f32
-  constexpr int OFF_FLAG = OFF_DEL + 2 * M * 4;
+  constexpr int OFF_Q = 0;                       // [2][M][PQ]
+  constexpr int OFF_DO = OFF_Q + 2 * QBUF;       // [2][M][PQ]
+  constexpr int OFF_K = OFF_DO + 2 * QBUF;       // [T][PQ]
+  constexpr int OFF_DS = OFF_K + T * PQ;         // [T][PS]  dS^T
+  constexpr int OFF_STAT = OFF_DS + T * PS;      // [2][2][M] f32: LSE (log2 domain), Delta
+  constexpr int OFF_FLAG = OFF_STAT + 4 * M * 4;
   constexpr int SMEM = OFF_FLAG + 16;
-  constexpr int QCH = M * D / 8 / NT;          // 16-byte chunks per thread of one Q (or dO) block
+  constexpr int QCH = M * D / 8 / NT;            // 16-byte chunks per thread of one Q (or dO) block
   static_assert(QCH >= 1 && (M * D / 8) % NT == 0, "tile split");
+  static_assert(NT >= 2 * M, "one statistic per thread");
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
   LDS char* base = (LDS char*)smem;
   volatile LDS int* s_flag = (volatile LDS int*)(base + OFF_FLAG);
@@ -319,9 +333,11 @@ __global__ __launch_bounds__(2 * T, 1) void bwd_kernel(BwdArgs a) {
   unsigned long long stall = 0;
   const unsigned long long t_start = __builtin_amdgcn_s_memtime();
 
-  // Prefetch registers for the next Q/dO block and its LSE/Delta.
+  // Prefetch registers for the next Q/dO block and one LSE-or-Delta value.
   bf16x8 pq[QCH], pdo[QCH];
-  float plse = 0.f, pdel = 0.f;
+  float pstat = 0.f;
+  const int st_tid = threadIdx.x < 2 * M ? threadIdx.x : 0;
+  const float st_mul = st_tid < M ? kLog2e : 1.f;
   auto load_block = [&](int head, int row0) {
     const __bf16* qh = a.q + ((size_t)head * S + row0) * D;
     const __bf16* doh = a.dO + ((size_t)head * S + row0) * D;
@@ -331,8 +347,8 @@ __global__ __launch_bounds__(2 * T, 1) void bwd_kernel(BwdArgs a) {
       pq[i] = *(const bf16x8*)(qh + (size_t)ch * 8);
       pdo[i] = *(const bf16x8*)(doh + (size_t)ch * 8);
     }
-    if (threadIdx.x < M) plse = a.lse[(size_t)head * S + row0 + threadIdx.x] * kLog2e;
-    else if (threadIdx.x < 2 * M) pdel = a.delta[(size_t)head * S + row0 + threadIdx.x - M];
+    const float* src = st_tid < M ? a.lse : a.delta;
+    pstat = src[(size_t)head * S + row0 + (st_tid & (M - 1))];
   };
   auto store_block = [&](int buf) {
 #pragma unroll
@@ -341,13 +357,14 @@ __global__ __launch_bounds__(2 * T, 1) void bwd_kernel(BwdArgs a) {
       *(LDS bf16x8*)(base + OFF_Q + buf * QBUF + row * PQ + col * 2) = pq[i];
       *(LDS bf16x8*)(base + OFF_DO + buf * QBUF + row * PQ + col * 2) = pdo[i];
     }
-    if (threadIdx.x < M) *(LDS float*)(base + OFF_LSE + (buf * M + threadIdx.x) * 4) = plse;
-    else if (threadIdx.x < 2 * M) *(LDS float*)(base + OFF_DEL + (buf * M + threadIdx.x - M) * 4) = pdel;
+    if (threadIdx.x < 2 * M) *(LDS float*)(base + OFF_STAT + (buf * 2 * M + threadIdx.x) * 4) = pstat * st_mul;
   };
 
   bf16x8 kb[DC], vb[DC];
   f32x16 dk_acc[DB], dv_acc[DB];
   int buf = 0;
+  int* pend_sem = nullptr;  // semaphore to release at the next second barrier
+  int pend_val = 0;
   if (beg < end) {
     const int4 r0 = a.steps[beg];
     load_block(r0.x, r0.y * T);
@@ -398,78 +415,103 @@ __global__ __launch_bounds__(2 * T, 1) void bwd_kernel(BwdArgs a) {
 
       const LDS char* sq = base + OFF_Q + buf * QBUF;
       const LDS char* sdo = base + OFF_DO + buf * QBUF;
-      const LDS float* slse = (const LDS float*)(base + OFF_LSE + buf * M * 4);
-      const LDS float* sdel = (const LDS float*)(base + OFF_DEL + buf * M * 4);
+      const LDS float* slse = (const LDS float*)(base + OFF_STAT + buf * 2 * M * 4);
+      const LDS float* sdel = slse + M;
+      const int kv_local = kv0 + c32;
 
-      // S = Q K^T and dP = dO V^T for this wave's 32 key/value columns.
-      f32x16 s[2], dp[2];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        s[qb] = f32x16{};
-        dp[qb] = f32x16{};
+        // S = Q K^T and dP = dO V^T for 32 query rows x this wave's 32 key/value columns.
+        bf16x8 aq[DC], ado[DC];
 #pragma unroll
         for (int c = 0; c < DC; ++c) {
           const int off = (qb * 32 + c32) * PQ + (16 * c + 8 * h2) * 2;
-          s[qb] = mfma32(lds_row8(sq + off), kb[c], s[qb]);
-          dp[qb] = mfma32(lds_row8(sdo + off), vb[c], dp[qb]);
+          aq[c] = lds_row8(sq + off);
+          ado[c] = lds_row8(sdo + off);
         }
-      }
-      // P = exp2(S*scale*log2e - LSE*log2e); dS = P * (dP - Delta).
-      const int kv_local = kv0 + c32;
+        f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+        for (int c = 0; c < DC; ++c) {
+          s = mfma32(aq[c], kb[c], s);
+          dp = mfma32(ado[c], vb[c], dp);
+        }
+        // P = exp2(S*scale*log2e - LSE*log2e); dS = P * (dP - Delta).
+        f32x4 l4[4], d4[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const f32x4 l4 = *(const LDS f32x4*)(slse + qb * 32 + 8 * j + 4 * h2);
-          const f32x4 d4 = *(const LDS f32x4*)(sdel + qb * 32 + 8 * j + 4 * h2);
+          l4[j] = *(const LDS f32x4*)(slse + qb * 32 + 8 * j + 4 * h2);
+          d4[j] = *(const LDS f32x4*)(sdel + qb * 32 + 8 * j + 4 * h2);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * j + e;
-            float p = __builtin_amdgcn_exp2f(s[qb][r] * a.scale_log2 - l4[e]);
+            float p = __builtin_amdgcn_exp2f(s[r] * a.scale_log2 - l4[j][e]);
             if (diag && kv_local > sub * M + qb * 32 + 8 * j + 4 * h2 + e) p = 0.f;
-            s[qb][r] = p;
-            dp[qb][r] = p * (dp[qb][r] - d4[e]);
+            s[r] = p;
+            dp[r] = p * (dp[r] - d4[j][e]);
           }
-        }
-      // dS^T to LDS for the dQ contraction (4 consecutive query rows per store).
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+        // dS^T to LDS for the dQ contraction (4 consecutive query rows per store).
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           bf16x4 t4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) t4[e] = (__bf16)dp[qb][4 * j + e];
+          for (int e = 0; e < 4; ++e) t4[e] = (__bf16)dp[4 * j + e];
           *(LDS bf16x4*)(base + OFF_DS + kv_local * PS + (qb * 32 + 8 * j + 4 * h2) * 2) = t4;
         }
-      // dV += P^T dO, dK += dS^T Q (contraction over the 64 query rows).
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+        // dV += P^T dO, dK += dS^T Q over these 32 query rows.
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const bf16x8 ap = pack8(s[qb], 8 * e);
-          const bf16x8 ads = pack8(dp[qb], 8 * e);
+          const bf16x8 ap = pack8(s, 8 * e);
+          const bf16x8 ads = pack8(dp, 8 * e);
           const int row0 = qb * 32 + 16 * e + 4 * h2;
+          bf16x8 bdo[DB], bq[DB];
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            dv_acc[db] = mfma32(ap, lds_tr8_split(sdo, PQ, row0, db * 32, lane), dv_acc[db]);
-            dk_acc[db] = mfma32(ads, lds_tr8_split(sq, PQ, row0, db * 32, lane), dk_acc[db]);
+            bdo[db] = lds_tr8_split(sdo, PQ, row0, db * 32, lane);
+            bq[db] = lds_tr8_split(sq, PQ, row0, db * 32, lane);
+          }
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            dv_acc[db] = mfma32(ap, bdo[db], dv_acc[db]);
+            dk_acc[db] = mfma32(ads, bq[db], dk_acc[db]);
           }
         }
+      }
       // The other buffer is free (read before B1): stage the prefetched block.
       if (nhead >= 0) store_block(buf ^ 1);
-      __syncthreads();  // B2: dS^T complete
+      if constexpr (!ATOMIC) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();  // B2: dS^T complete; previous dQ writes complete
+      if constexpr (!ATOMIC) {
+        if (pend_sem != nullptr && threadIdx.x == 0)
+          __hip_atomic_store(pend_sem, pend_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        pend_sem = nullptr;
+      }
 
       // dQ partial = dS K over all T key/value rows of the tile.
       f32x16 dq[TPW];
+      {
+        // tile t = w + NW*ti has d block t % DB; the blocks repeat every NDB tiles
+        constexpr int NDB = (DB / gcd_c(DB, NW)) < TPW ? (DB / gcd_c(DB, NW)) : TPW;
+        static_assert(TPW % NDB == 0 && (NW * NDB) % DB == 0 || NDB == TPW, "tile split");
 #pragma unroll
-      for (int ti = 0; ti < TPW; ++ti) {
-        const int t_idx = w + NW * ti, qb = t_idx / DB, db = t_idx % DB;
-        dq[ti] = f32x16{};
+        for (int nd = 0; nd < NDB; ++nd) {
+          const int db = (w + NW * nd) % DB;
+          bf16x8 bk[KC];
 #pragma unroll
-        for (int c = 0; c < T / 16; ++c) {
-          const bf16x8 ads = lds_tr8_consecutive(base + OFF_DS, PS, 16 * c + 8 * h2, qb * 32, lane);
-          const bf16x8 bk = lds_tr8_consecutive(base + OFF_K, PQ, 16 * c + 8 * h2, db * 32, lane);
-          dq[ti] = mfma32(ads, bk, dq[ti]);
+          for (int c = 0; c < KC; ++c) bk[c] = lds_tr8_consecutive(base + OFF_K, PQ, 16 * c + 8 * h2, db * 32, lane);
+#pragma unroll
+          for (int ti = nd; ti < TPW; ti += NDB) {
+            const int t_idx = w + NW * ti, qb = t_idx / DB;
+            bf16x8 ads[KC];
+#pragma unroll
+            for (int c = 0; c < KC; ++c) ads[c] = lds_tr8_consecutive(base + OFF_DS, PS, 16 * c + 8 * h2, qb * 32, lane);
+            f32x16 acc = f32x16{};
+#pragma unroll
+            for (int c = 0; c < KC; ++c) acc = mfma32(ads[c], bk[c], acc);
+            dq[ti] = acc;
+          }
         }
       }
 
@@ -478,14 +520,10 @@ __global__ __launch_bounds__(2 * T, 1) void bwd_kernel(BwdArgs a) {
       if constexpr (ATOMIC) {
 #pragma unroll
         for (int ti = 0; ti < TPW; ++ti) {
-          const int t_idx = w + NW * ti;
+          float* p = wsb + (w + NW * ti) * 1024 + lane;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float* p = wsb + t_idx * 1024 + j * 256 + lane * 4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              __hip_atomic_fetch_add(p + e, dq[ti][4 * j + e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
+          for (int r = 0; r < 16; ++r)
+            __hip_atomic_fetch_add(p + r * 64, dq[ti][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       } else {
         int* semp = a.sem + (size_t)head * nblk + blk;
@@ -494,7 +532,7 @@ __global__ __launch_bounds__(2 * T, 1) void bwd_kernel(BwdArgs a) {
           if (ord > 0) {
             const unsigned long long t0 = __builtin_amdgcn_s_memtime();
             const long long deadline = (long long)__builtin_amdgcn_s_memrealtime() + a.spin_ticks;
-            while (__hip_atomic_load(semp, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != ord) {
+            while (__hip_atomic_load(semp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != ord) {
               if (__hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) { ab = 1; break; }
               if ((long long)__builtin_amdgcn_s_memrealtime() > deadline) {
                 __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -507,25 +545,30 @@ __global__ __launch_bounds__(2 * T, 1) void bwd_kernel(BwdArgs a) {
           }
           *s_flag = ab;
         }
-        __syncthreads();  // B3: predecessor's dQ visible to the whole workgroup
+        __syncthreads();  // B3: the predecessor's dQ writes are complete at device scope
         if (*s_flag) {
           aborted = true;
           break;
         }
+        if (ord > 0) {
+          f32x16 prev[TPW];
+#pragma unroll
+          for (int ti = 0; ti < TPW; ++ti) {
+            float* p = wsb + (w + NW * ti) * 1024 + lane;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) prev[ti][r] = __hip_atomic_load(p + r * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+#pragma unroll
+          for (int ti = 0; ti < TPW; ++ti) dq[ti] += prev[ti];
+        }
 #pragma unroll
         for (int ti = 0; ti < TPW; ++ti) {
-          const int t_idx = w + NW * ti;
+          float* p = wsb + (w + NW * ti) * 1024 + lane;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            f32x4* p = (f32x4*)(wsb + t_idx * 1024 + j * 256 + lane * 4);
-            f32x4 x = {dq[ti][4 * j], dq[ti][4 * j + 1], dq[ti][4 * j + 2], dq[ti][4 * j + 3]};
-            if (ord > 0) x += *p;
-            *p = x;
-          }
+          for (int r = 0; r < 16; ++r) __hip_atomic_store(p + r * 64, dq[ti][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        __syncthreads();  // B4: every wave's dQ stores issued and fenced
-        if (threadIdx.x == 0) __hip_atomic_store(semp, ord + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        pend_sem = semp;
+        pend_val = ord + 1;
       }
       buf ^= 1;
     }
@@ -544,29 +587,36 @@ __global__ __launch_bounds__(2 * T, 1) void bwd_kernel(BwdArgs a) {
         }
     }
   }
+  if constexpr (!ATOMIC) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (pend_sem != nullptr && !aborted && threadIdx.x == 0)
+      __hip_atomic_store(pend_sem, pend_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   if (a.stall && threadIdx.x == 0) {
     a.stall[2 * wg] = stall;
     a.stall[2 * wg + 1] = __builtin_amdgcn_s_memtime() - t_start;
   }
 }
 
-// dQ = bf16(scale * workspace), undoing the fragment order.
+// dQ = bf16(scale * workspace), undoing the fragment order.  One thread per
+// (block, tile, register group of four, lane): four rows of one column.
 template <int D>
 __global__ __launch_bounds__(256) void dq_finalize_kernel(const float* __restrict__ ws, __bf16* __restrict__ dq,
-                                                          long long n_f4, float scale) {
+                                                          long long n_groups, float scale) {
   const long long f = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (f >= n_f4) return;
-  constexpr int F4_PER_BLOCK = 64 * D / 4;
-  const long long blk = f / F4_PER_BLOCK;  // (head, 64-row block)
-  const int rem = (int)(f % F4_PER_BLOCK);
+  if (f >= n_groups) return;
+  constexpr int GROUPS_PER_BLOCK = 64 * D / 4;
+  const long long blk = f / GROUPS_PER_BLOCK;  // (head, 64-row block)
+  const int rem = (int)(f % GROUPS_PER_BLOCK);
   const int tile = rem / 256, j = (rem % 256) / 64, l = rem % 64;
   const int qb = tile / (D / 32), db = tile % (D / 32);
-  const f32x4 x = *(const f32x4*)(ws + f * 4);
+  const float* src = ws + (size_t)blk * 64 * D + tile * 1024 + (4 * j) * 64 + l;
   const int col = db * 32 + (l & 31);
   const int row0 = qb * 32 + 8 * j + 4 * (l >> 5);
   __bf16* out = dq + (size_t)blk * 64 * D;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) out[(size_t)(row0 + e) * D + col] = (__bf16)(x[e] * scale);
+  for (int e = 0; e < 4; ++e) out[(size_t)(row0 + e) * D + col] = (__bf16)(src[e * 64] * scale);
 }
 
 }  // namespace
