@@ -68,7 +68,18 @@ def main():
     ap.add_argument("--schedules", default="", help="comma list (serial,desc_q,shift,sym_shift); default: all for the mask")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-atomic", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (calibrates HBM counters)")
     args = ap.parse_args()
+    if args.copy_probe:
+        import torch
+        src = torch.empty(args.copy_probe << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": args.copy_probe << 20, "launches": 3}))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                                    "(the path shards by (batch, kv head) with no exchange; see DESIGN.md)"}))
@@ -147,8 +158,10 @@ def main():
     traffic = None
     if os.path.exists(PROFILE_COUNTERS):
         try:
+            from scheduling_persistent_fa_amd.profiling import kernel_source_digest
             c = json.load(open(PROFILE_COUNTERS))
-            if c.get("workload") == args.workload and c.get("schedule") == best:
+            if (c.get("workload") == args.workload and c.get("schedule") == best
+                    and c.get("kernel_source_sha256") == kernel_source_digest()):
                 traffic = c.get("hbm_bytes_per_launch")
         except Exception:
             traffic = None

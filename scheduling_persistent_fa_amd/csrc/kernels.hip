@@ -98,7 +98,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const __bf16* __restric
                                                          float* __restrict__ lse, int Hq, int g, int S,
                                                          float scale_log2, int causal) {
   constexpr int KVT = 64;               // key/value rows per LDS tile
-  constexpr int PITCH = (D + 8) * 2;    // bytes per LDS row (16-byte pad)
+  constexpr int PITCH = 2 * D + 32;     // bytes per LDS row: 32 mod 256
   constexpr int TILE_BYTES = KVT * PITCH;
   constexpr int DC = D / 16;            // 16-wide d chunks
   constexpr int DB = D / 32;            // 32-wide d blocks
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(2 * T, 1) void bwd_kernel(BwdArgs a) {
   constexpr int DB = D / 32;
   constexpr int TPW = 2 * DB / NW;    // dQ C tiles per wave
   constexpr int KC = T / 16;          // 16-row key/value chunks of the dQ contraction
-  constexpr int PQ = (D + 8) * 2;     // LDS pitch (bytes) of Q / dO / K rows
+  constexpr int PQ = 2 * D + 32;      // LDS pitch (bytes) of Q / dO / K rows: 32 mod 256
   constexpr int PS = (M + 8) * 2;     // LDS pitch (bytes) of dS^T rows
   constexpr int QBUF = M * PQ;
   constexpr int OFF_Q = 0;                       // [2][M][PQ]
