@@ -91,6 +91,9 @@ typedef struct dash_bwd_opts {
   int sync_check;            /* 1: synchronise the stream and report DASH_ERR_TIMEOUT / HIP faults */
   void* event_start;         /* optional hipEvent_t recorded on `stream` just before the persistent kernel */
   void* event_stop;          /* optional hipEvent_t recorded on `stream` just after it */
+  int max_gang;              /* SHIFT / SYM_SHIFT (and their ATOMIC walks): cap on the gang size; a capped
+                                gang takes its key/value tiles (or tile pairs) in rounds, so more gangs run
+                                side by side.  0 = natural size (N, or N/2); negative = DASH_ERR_INVALID_ARG */
 } dash_bwd_opts;
 
 /*
@@ -134,9 +137,10 @@ typedef struct dash_schedule dash_schedule;
  * N tiles per sequence and P workgroups.  schedule may be any of the five
  * kinds (ATOMIC builds the walk of `atomic_walk` as in dash_bwd_opts).
  * xcd_local != 0 places the members of a gang on indices congruent modulo
- * the gang count.  *out receives a schedule to free with dash_schedule_free. */
+ * the gang count; max_gang caps gang sizes as in dash_bwd_opts.  *out
+ * receives a schedule to free with dash_schedule_free. */
 int dash_schedule_build(int mask, int schedule, int N, int g, int groups, int P, int xcd_local,
-                        int atomic_walk, dash_schedule** out);
+                        int atomic_walk, int max_gang, dash_schedule** out);
 
 int dash_schedule_num_workgroups(const dash_schedule* s);
 long long dash_schedule_num_steps(const dash_schedule* s);

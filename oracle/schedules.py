@@ -84,8 +84,14 @@ def gang_slot(gang: int, p: int, n_gangs: int, gang_size: int, xcd_local: bool) 
     return p * n_gangs + gang if xcd_local else gang * gang_size + p
 
 
-def build(mask: int, sched: int, N: int, g: int, groups: int, P: int, xcd_local: bool = True) -> list[list[Step]]:
-    """Per-workgroup step lists for ``groups`` kv groups of g query heads, N tiles, P workgroups."""
+def build(mask: int, sched: int, N: int, g: int, groups: int, P: int, xcd_local: bool = True,
+          max_gang: int = 0) -> list[list[Step]]:
+    """Per-workgroup step lists for ``groups`` kv groups of g query heads, N tiles, P workgroups.
+
+    ``max_gang`` > 0 caps a gang schedule's gang below its natural size (N for
+    shift, N/2 for symmetric shift); member p then takes the units (key/value
+    tiles, or tile pairs) p, p + gang, p + 2*gang, ... one after another.
+    """
     if N < 1 or g < 1 or groups < 1 or P < 1:
         raise ScheduleError("sizes must be positive")
     out: list[list[Step]] = [[] for _ in range(P)]
@@ -105,29 +111,33 @@ def build(mask: int, sched: int, N: int, g: int, groups: int, P: int, xcd_local:
     if sched == SHIFT:
         if mask != FULL:
             raise ScheduleError("shift scheduling needs a full mask")
-        gang_size = N
+        units = N
     elif sched == SYM_SHIFT:
         if mask != CAUSAL:
             raise ScheduleError("symmetric shift needs a causal mask")
         if N % 2:
             raise ScheduleError("symmetric shift needs an even tile count")
-        gang_size = N // 2
+        units = N // 2
     else:
         raise ScheduleError(f"unknown schedule {sched}")
+    gang_size = max_gang if 0 < max_gang < units else units
     n_gangs = P // gang_size
     if n_gangs < 1:
         raise ScheduleError("gang larger than the workgroup count")
+    M = units
     for grp in range(groups):
         gang = grp % n_gangs
         members = []  # per member: list of chains, each a list of (head, qi, kj)
         for p in range(gang_size):
-            if sched == SHIFT:
-                members.append([_chain(grp, g, p, [(p + t) % N for t in range(N)])])
-            else:
-                M = gang_size
-                a_walk = [M + (p + t) % M for t in range(M)] + [p + s for s in range(M - p)]
-                b_walk = [N - 1 - s + M - p for s in range(M - p, M + 1)]
-                members.append([_chain(grp, g, p, a_walk), _chain(grp, g, N - 1 - p, b_walk)])
+            chains = []
+            for i in range(p, units, gang_size):
+                if sched == SHIFT:
+                    chains.append(_chain(grp, g, i, [(i + t) % N for t in range(N)]))
+                else:
+                    a_walk = [M + (i + t) % M for t in range(M)] + [i + s for s in range(M - i)]
+                    b_walk = [N - 1 - s + M - i for s in range(M - i, M + 1)]
+                    chains += [_chain(grp, g, i, a_walk), _chain(grp, g, N - 1 - i, b_walk)]
+            members.append(chains)
         # ordinal = rank of (time key, kj) among each dQ tile's contributors,
         # where the time key is the step's position in its member's list
         keys: dict[tuple[int, int], list[tuple[int, int]]] = {}

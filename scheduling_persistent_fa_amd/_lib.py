@@ -57,6 +57,7 @@ class BwdOpts(ctypes.Structure):
         ("sync_check", ctypes.c_int),
         ("event_start", ctypes.c_void_p),
         ("event_stop", ctypes.c_void_p),
+        ("max_gang", ctypes.c_int),
     ]
 
 
@@ -70,7 +71,7 @@ def _declare(lib):
     lib.dash_attn_bwd.argtypes = [vp] * 9 + [i, i, i, i, i, f, i, i, ctypes.POINTER(BwdOpts), vp]
     lib.dash_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, ctypes.POINTER(ctypes.c_size_t)]
     lib.dash_attn_bwd_delta.argtypes = [vp, vp, vp, i, i, i, i, vp]
-    lib.dash_schedule_build.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(vp)]
+    lib.dash_schedule_build.argtypes = [i, i, i, i, i, i, i, i, i, ctypes.POINTER(vp)]
     lib.dash_schedule_num_workgroups.argtypes = [vp]
     lib.dash_schedule_num_steps.argtypes = [vp]
     lib.dash_schedule_num_steps.restype = ctypes.c_longlong

@@ -46,7 +46,8 @@ def attn_fwd(q, k, v, causal: bool, scale: float = 0.0, out=None, lse=None, stre
 
 def make_opts(num_workgroups: int = 0, tile: int = 0, atomic_walk: int = -1, xcd_local: bool = True,
               workspace: torch.Tensor | None = None, stall: torch.Tensor | None = None,
-              spin_timeout_cycles: int = 0, sync_check: bool = False, events=None) -> _lib.BwdOpts:
+              spin_timeout_cycles: int = 0, sync_check: bool = False, events=None,
+              max_gang: int = 0) -> _lib.BwdOpts:
     o = _lib.BwdOpts()
     o.struct_size = ctypes.sizeof(_lib.BwdOpts)
     o.num_workgroups = num_workgroups
@@ -63,6 +64,7 @@ def make_opts(num_workgroups: int = 0, tile: int = 0, atomic_walk: int = -1, xcd
     if events is not None:
         o.event_start = events[0].cuda_event
         o.event_stop = events[1].cuda_event
+    o.max_gang = max_gang
     return o
 
 

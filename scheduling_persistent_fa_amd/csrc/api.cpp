@@ -67,7 +67,7 @@ struct DevSchedule {
   int32_t* offsets = nullptr;
   long long num_steps = 0;
 };
-using SchedKey = std::tuple<int, int, int, int, int, int, int, int, int>;  // dev, mask, kind, N, g, groups, P, xcd, walk
+using SchedKey = std::tuple<int, int, int, int, int, int, int, int, int, int>;  // dev, mask, kind, N, g, groups, P, xcd, walk, cap
 std::map<SchedKey, DevSchedule> g_sched;
 
 struct Workspace {
@@ -144,11 +144,12 @@ int dash_device_info(int device, int* num_cu, int* lds_bytes, int* clock_khz) {
 }
 
 int dash_schedule_build(int mask, int schedule, int N, int g, int groups, int P, int xcd_local, int atomic_walk,
-                        dash_schedule** out) {
+                        int max_gang, dash_schedule** out) {
   if (!out) return fail(DASH_ERR_INVALID_ARG, "null output");
   *out = nullptr;
   auto s = std::make_unique<dash_schedule>();
-  std::string err = dash::build_schedule(mask, schedule, N, g, groups, P, xcd_local != 0, atomic_walk, &s->s);
+  if (max_gang < 0) return fail(DASH_ERR_INVALID_ARG, "negative gang cap");
+  std::string err = dash::build_schedule(mask, schedule, N, g, groups, P, xcd_local != 0, atomic_walk, max_gang, &s->s);
   if (!err.empty()) {
     const bool bad = (N < 1 || g < 1 || groups < 1 || P < 1 || (mask != 0 && mask != 1) || schedule < 0 || schedule > 4);
     return fail(bad ? DASH_ERR_INVALID_ARG : DASH_ERR_UNSUPPORTED, err);
@@ -235,6 +236,7 @@ int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
   const int N = S / T;
   const int P = op.num_workgroups > 0 ? op.num_workgroups : di.num_cu;
   if (op.num_workgroups < 0) return fail(DASH_ERR_INVALID_ARG, "negative workgroup count");
+  if (op.max_gang < 0) return fail(DASH_ERR_INVALID_ARG, "negative gang cap");
   const int g = Hq / Hkv;
   const int groups = B * Hkv;
   const bool atomic = schedule == DASH_SCHED_ATOMIC;
@@ -254,11 +256,11 @@ int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
   DevSchedule ds;
   {
     std::lock_guard<std::mutex> lk(g_mu);
-    SchedKey key{dev, mask, schedule, N, g, groups, P, xcd, atomic ? (walk < 0 ? -1 : walk) : -1};
+    SchedKey key{dev, mask, schedule, N, g, groups, P, xcd, atomic ? (walk < 0 ? -1 : walk) : -1, op.max_gang};
     auto it = g_sched.find(key);
     if (it == g_sched.end()) {
       dash::Schedule s;
-      std::string err = dash::build_schedule(mask, schedule, N, g, groups, P, xcd != 0, walk, &s);
+      std::string err = dash::build_schedule(mask, schedule, N, g, groups, P, xcd != 0, walk, op.max_gang, &s);
       if (!err.empty()) return fail(DASH_ERR_UNSUPPORTED, err);
       err = dash::validate_schedule(s);
       if (!err.empty()) return fail(DASH_ERR_INVALID_SCHEDULE, err);

@@ -13,7 +13,9 @@
 //            and its own triangle part, then tile N-1-p through the folded
 //            triangle, N+1 steps per member (§2.2.B, symmetric shift).
 // Gang schedules order each dQ tile's contributions by lock-step time (the
-// step's position in its workgroup's list for that group), ties by kj.
+// step's position in its workgroup's list for that group), ties by kj.  A
+// gang may be capped below its natural size (N, or N/2): its members then
+// take their units in rounds, which keeps a gang on one chiplet.
 #include "schedule.hpp"
 
 #include <algorithm>
@@ -70,24 +72,29 @@ std::string build_list_scheduled(const Schedule& s, std::vector<std::vector<Step
 
 std::string build_gang(const Schedule& s, std::vector<std::vector<StepRec>>& per_wg) {
   const int N = s.N;
-  const int gang = (s.walk == kShift) ? N : N / 2;
+  // units: key/value tiles (shift) or tile pairs i, N-1-i (symmetric shift)
+  const int units = (s.walk == kShift) ? N : N / 2;
+  const int gang = (s.max_gang > 0 && s.max_gang < units) ? s.max_gang : units;
   const int n_gangs = s.P / gang;
   if (n_gangs < 1) return "gang of " + std::to_string(gang) + " workgroups exceeds " + std::to_string(s.P);
-  // Per member: its chains as (kj, walk of one head).
+  // Per member: its chains as (kj, walk of one head).  A capped gang runs
+  // its units in rounds: member p keeps units p, p + gang, p + 2*gang, ...
   std::vector<std::vector<std::pair<int, std::vector<int>>>> member(gang);
   for (int p = 0; p < gang; ++p) {
-    if (s.walk == kShift) {
-      std::vector<int> w(N);
-      for (int t = 0; t < N; ++t) w[t] = (p + t) % N;
-      member[p].push_back({p, std::move(w)});
-    } else {
-      const int M = gang;
-      std::vector<int> a, b;
-      for (int t = 0; t < M; ++t) a.push_back(M + (p + t) % M);   // dense rectangle
-      for (int q = p; q < M; ++q) a.push_back(q);                  // own triangle part
-      for (int q = N - 1; q >= N - 1 - p; --q) b.push_back(q);     // folded triangle
-      member[p].push_back({p, std::move(a)});
-      member[p].push_back({N - 1 - p, std::move(b)});
+    for (int i = p; i < units; i += gang) {
+      if (s.walk == kShift) {
+        std::vector<int> w(N);
+        for (int t = 0; t < N; ++t) w[t] = (i + t) % N;
+        member[p].push_back({i, std::move(w)});
+      } else {
+        const int M = units;
+        std::vector<int> a, b;
+        for (int t = 0; t < M; ++t) a.push_back(M + (i + t) % M);   // dense rectangle
+        for (int q = i; q < M; ++q) a.push_back(q);                  // own triangle part
+        for (int q = N - 1; q >= N - 1 - i; --q) b.push_back(q);     // folded triangle
+        member[p].push_back({i, std::move(a)});
+        member[p].push_back({N - 1 - i, std::move(b)});
+      }
     }
   }
   // Ordinals: rank of (position, kj) among the contributors of each
@@ -131,7 +138,7 @@ std::string build_gang(const Schedule& s, std::vector<std::vector<StepRec>>& per
 }  // namespace
 
 std::string build_schedule(int mask, int kind, int N, int g, int groups, int P, bool xcd_local,
-                           int atomic_walk, Schedule* out) {
+                           int atomic_walk, int max_gang, Schedule* out) {
   if (N < 1 || g < 1 || groups < 1 || P < 1) return "sizes must be positive";
   if (mask != kMaskFull && mask != kMaskCausal) return "unknown mask";
   if (kind < kSerial || kind > kAtomic) return "unknown schedule";
@@ -153,6 +160,7 @@ std::string build_schedule(int mask, int kind, int N, int g, int groups, int P, 
   s.groups = groups;
   s.P = P;
   s.xcd_local = xcd_local;
+  s.max_gang = max_gang > 0 ? max_gang : 0;
   std::vector<std::vector<StepRec>> per_wg(P);
   std::string err = (walk == kSerial || walk == kDescQ) ? build_list_scheduled(s, per_wg) : build_gang(s, per_wg);
   if (!err.empty()) return err;

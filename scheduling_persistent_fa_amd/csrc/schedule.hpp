@@ -33,13 +33,14 @@ struct Schedule {
   int mask = 0, kind = 0, walk = 0;  // walk: the ordering schedule (== kind unless kind is ATOMIC)
   int N = 0, g = 1, groups = 1, P = 1;
   bool xcd_local = true;
+  int max_gang = 0;                  // 0: natural gang size (N for shift, N/2 for symmetric shift)
   std::vector<int32_t> offsets;  // P + 1
   std::vector<StepRec> steps;
 };
 
 // Returns an empty string on success, else the reason (unsupported combination).
 std::string build_schedule(int mask, int kind, int N, int g, int groups, int P, bool xcd_local,
-                           int atomic_walk, Schedule* out);
+                           int atomic_walk, int max_gang, Schedule* out);
 // Empty string if valid, else the first violation found.
 std::string validate_schedule(const Schedule& s);
 // Unit-cost DAG simulation; returns false on deadlock.

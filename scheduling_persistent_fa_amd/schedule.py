@@ -16,11 +16,11 @@ class Schedule:
     """
 
     def __init__(self, mask: int, schedule: int, N: int, g: int, groups: int, P: int,
-                 xcd_local: bool = True, atomic_walk: int = -1):
+                 xcd_local: bool = True, atomic_walk: int = -1, max_gang: int = 0):
         L = _lib.lib()
         h = ctypes.c_void_p()
         _lib.check(L.dash_schedule_build(mask, schedule, N, g, groups, P, int(bool(xcd_local)), atomic_walk,
-                                         ctypes.byref(h)))
+                                         max_gang, ctypes.byref(h)))
         self._h = h
         self.P = L.dash_schedule_num_workgroups(h)
         self.num_steps = L.dash_schedule_num_steps(h)

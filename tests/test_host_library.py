@@ -34,28 +34,31 @@ def _oracle_tuples(lists):
 
 
 CASES = [
-    (Sch.FULL, Sch.SERIAL, 4, 1, 1, 4), (Sch.FULL, Sch.SHIFT, 4, 1, 1, 4), (Sch.CAUSAL, Sch.SYM_SHIFT, 4, 1, 1, 2),
-    (Sch.FULL, Sch.SERIAL, 16, 1, 8, 256), (Sch.FULL, Sch.DESC_Q, 16, 2, 3, 20),
-    (Sch.CAUSAL, Sch.SERIAL, 16, 1, 64, 256), (Sch.CAUSAL, Sch.DESC_Q, 16, 1, 64, 256),
-    (Sch.CAUSAL, Sch.SYM_SHIFT, 16, 1, 64, 256), (Sch.FULL, Sch.SHIFT, 32, 1, 48, 256),
-    (Sch.CAUSAL, Sch.SYM_SHIFT, 64, 4, 8, 256), (Sch.CAUSAL, Sch.DESC_Q, 64, 4, 8, 256),
-    (Sch.FULL, Sch.SHIFT, 6, 3, 5, 13), (Sch.CAUSAL, Sch.SYM_SHIFT, 10, 2, 3, 11),
+    (Sch.FULL, Sch.SERIAL, 4, 1, 1, 4, 0), (Sch.FULL, Sch.SHIFT, 4, 1, 1, 4, 0), (Sch.CAUSAL, Sch.SYM_SHIFT, 4, 1, 1, 2, 0),
+    (Sch.FULL, Sch.SERIAL, 16, 1, 8, 256, 0), (Sch.FULL, Sch.DESC_Q, 16, 2, 3, 20, 0),
+    (Sch.CAUSAL, Sch.SERIAL, 16, 1, 64, 256, 0), (Sch.CAUSAL, Sch.DESC_Q, 16, 1, 64, 256, 0),
+    (Sch.CAUSAL, Sch.SYM_SHIFT, 16, 1, 64, 256, 0), (Sch.FULL, Sch.SHIFT, 32, 1, 48, 256, 0),
+    (Sch.CAUSAL, Sch.SYM_SHIFT, 64, 4, 8, 256, 0), (Sch.CAUSAL, Sch.DESC_Q, 64, 4, 8, 256, 0),
+    (Sch.FULL, Sch.SHIFT, 6, 3, 5, 13, 0), (Sch.CAUSAL, Sch.SYM_SHIFT, 10, 2, 3, 11, 0),
+    # capped gangs (rounds)
+    (Sch.FULL, Sch.SHIFT, 128, 1, 16, 256, 32), (Sch.CAUSAL, Sch.SYM_SHIFT, 128, 1, 16, 256, 32),
+    (Sch.FULL, Sch.SHIFT, 10, 2, 3, 12, 4), (Sch.CAUSAL, Sch.SYM_SHIFT, 14, 3, 2, 9, 3),
 ]
 
 
-@pytest.mark.parametrize("mask,sched,N,g,groups,P", CASES)
+@pytest.mark.parametrize("mask,sched,N,g,groups,P,cap", CASES)
 @pytest.mark.parametrize("xcd", [True, False])
-def test_host_schedule_matches_oracle_exactly(mask, sched, N, g, groups, P, xcd):
-    lib_s = Schedule(mask, sched, N, g, groups, P, xcd_local=xcd)
+def test_host_schedule_matches_oracle_exactly(mask, sched, N, g, groups, P, cap, xcd):
+    lib_s = Schedule(mask, sched, N, g, groups, P, xcd_local=xcd, max_gang=cap)
     lib_s.validate()
-    ora = Sch.build(mask, sched, N, g, groups, P, xcd_local=xcd)
+    ora = Sch.build(mask, sched, N, g, groups, P, xcd_local=xcd, max_gang=cap)
     assert lib_s.lists() == _oracle_tuples(ora)
 
 
-@pytest.mark.parametrize("mask,sched,N,g,groups,P", CASES[:8])
-def test_host_simulator_matches_oracle(mask, sched, N, g, groups, P):
-    lib_s = Schedule(mask, sched, N, g, groups, P)
-    ora = Sch.build(mask, sched, N, g, groups, P)
+@pytest.mark.parametrize("mask,sched,N,g,groups,P,cap", CASES[:8] + CASES[-2:])
+def test_host_simulator_matches_oracle(mask, sched, N, g, groups, P, cap):
+    lib_s = Schedule(mask, sched, N, g, groups, P, max_gang=cap)
+    ora = Sch.build(mask, sched, N, g, groups, P, max_gang=cap)
     for c, r in ((1.0, 1.0), (2.5, 0.75)):
         assert lib_s.simulate(c, r) == pytest.approx(Sch.simulate(ora, c, r), rel=1e-12, abs=1e-9)
 

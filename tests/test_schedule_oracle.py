@@ -163,3 +163,30 @@ def test_rejects_bad_combinations():
         Sch.build(CAUSAL, SYM_SHIFT, 5, 1, 1, 4)
     with pytest.raises(Sch.ScheduleError):
         Sch.build(FULL, SHIFT, 8, 1, 1, 4)
+
+
+@pytest.mark.parametrize("mask,sched", [(FULL, SHIFT), (CAUSAL, SYM_SHIFT)])
+def test_capped_gangs_are_valid_and_monotone(mask, sched):
+    for N in (4, 6, 8, 12, 16):
+        units = N if sched == SHIFT else N // 2
+        for cap in range(1, units + 1):
+            for g in (1, 2):
+                lists = Sch.build(mask, sched, N, g, 3, 2 * cap + 1, max_gang=cap)
+                Sch.validate(lists, mask, N, g, 3)
+                assert Sch.monotone_in_lockstep(lists, g)
+
+
+@pytest.mark.parametrize("N,cap,m", [(8, 2, 3), (16, 4, 2), (32, 8, 4)])
+def test_capped_shift_rounds_keep_the_lower_bound(N, cap, m):
+    # one gang of `cap` workgroups takes N/cap rounds per head, each member
+    # working back to back: makespan m * N/cap * N * (c + r), no waiting
+    lists = Sch.build(FULL, SHIFT, N, 1, m, cap, max_gang=cap)
+    mk, wait = Sch.simulate(lists, 1.0, 0.5)
+    assert wait == 0 and abs(mk - m * (N // cap) * N * 1.5) < 1e-9
+
+
+@pytest.mark.parametrize("N,cap,m", [(8, 2, 2), (16, 4, 2), (32, 4, 2)])
+def test_capped_sym_shift_rounds_have_no_waits(N, cap, m):
+    lists = Sch.build(CAUSAL, SYM_SHIFT, N, 1, m, cap, max_gang=cap)
+    mk, wait = Sch.simulate(lists, 1.0, 1.0)
+    assert wait == 0 and abs(mk - m * (N // 2 // cap) * (N + 1) * 2.0) < 1e-9
