@@ -78,8 +78,11 @@ std::map<int, Workspace> g_ws;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// One semaphore word per (64-row dQ block, wave holding dQ tiles of it).
+constexpr size_t kSemWordsPerBlock = 8;
+
 struct WsLayout {
-  size_t ws_dq, delta, sem, err, total;
+  size_t ws_dq, delta, sem, err, dummy, total;
 };
 
 WsLayout ws_layout(int B, int Hq, int S, int D) {
@@ -91,9 +94,11 @@ WsLayout ws_layout(int B, int Hq, int S, int D) {
   L.delta = off;
   off = align256(off + rows * sizeof(float));
   L.sem = off;
-  off = align256(off + (size_t)B * Hq * (S / 64) * sizeof(int));
+  off = align256(off + (size_t)B * Hq * (S / 64) * kSemWordsPerBlock * sizeof(int));
   L.err = off;
   off = align256(off + 16);
+  L.dummy = off;  // 8 dQ tiles' worth of scratch for writes with no destination
+  off = align256(off + 8 * 1024 * sizeof(float));
   L.total = off;
   return L;
 }
@@ -324,6 +329,7 @@ int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
   bl.ws = ws_dq;
   bl.sem = sem;
   bl.err = err;
+  bl.dummy = (float*)(ws + L.dummy);
   bl.dk = dk;
   bl.dv = dv;
   bl.steps = ds.steps;

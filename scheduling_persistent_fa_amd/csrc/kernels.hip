@@ -32,6 +32,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS __attribute__((address_space(3)))
+#define CONST_AS __attribute__((address_space(4)))
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -73,6 +74,20 @@ __device__ __forceinline__ bf16x8 lds_tr8_split(const LDS char* base, int pitch_
   return cat8(lds_tr4(p), lds_tr4(p + 8 * pitch_bytes));
 }
 
+// Same as lds_tr8_consecutive with the lane part of the address already
+// applied: p = block + ((l%16)/4) * pitch + (16*((l/16)%2) + 4*(l%4)) * 2.
+__device__ __forceinline__ bf16x8 lds_tr8_at(const LDS char* p, int pitch_bytes) {
+  return cat8(lds_tr4(p), lds_tr4(p + 4 * pitch_bytes));
+}
+
+// Keeps a value opaque to the optimiser, so that addresses formed from it
+// fold their constant parts into instruction offsets instead of being
+// precomputed and held in registers.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 __device__ __forceinline__ bf16x8 pack8(const f32x16& x, int first) {
   bf16x8 r;
 #pragma unroll
@@ -98,7 +113,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const __bf16* __restric
                                                          float* __restrict__ lse, int Hq, int g, int S,
                                                          float scale_log2, int causal) {
   constexpr int KVT = 64;               // key/value rows per LDS tile
-  constexpr int PITCH = 2 * D + 32;     // bytes per LDS row: 32 mod 256
+  constexpr int PITCH = 2 * D + 48;     // bytes per LDS row: 16-byte row reads and transposing reads conflict-free
   constexpr int TILE_BYTES = KVT * PITCH;
   constexpr int DC = D / 16;            // 16-wide d chunks
   constexpr int DB = D / 32;            // 32-wide d blocks
@@ -252,13 +267,28 @@ __global__ __launch_bounds__(256) void delta_kernel(const __bf16* __restrict__ o
 }
 
 // ---------------------------------------------------------------------------
+// LDS row pitches.  gfx950's LDS has 64 four-byte banks.  A 16-byte row read
+// (16 lanes per cycle, 16 consecutive rows) is conflict-free when the pitch in
+// words is 4 x odd modulo 64; a transposing read (16 lanes per cycle: 4 rows x
+// 32 bytes) needs the four rows' 8-bank windows disjoint.  Pitches of 2D + 48
+// bytes (304 for D = 128, 176 for D = 64) satisfy both, as does 144 bytes for
+// the 64-column P^T / dS^T rows (also conflict-free for their 8-byte writes).
+// ---------------------------------------------------------------------------
 // Persistent backward.  One workgroup per compute unit walks its step list
 // (built on the host); each chain (key/value tile x its query heads) runs
 // contiguously with dK/dV in registers ([summary] §2.1).  Per 64-row query
 // block the workgroup adds its dQ partial into the fp32 workspace either in
 // the order fixed by the step's ordinal -- waiting on a per-block semaphore
-// in global memory with acquire/release at device scope -- or, for the
-// non-deterministic ceiling, with fp32 atomic adds.
+// in global memory -- or, for the non-deterministic ceiling, with fp32
+// atomic adds.
+//
+// Work split.  The T key/value rows of a tile are held by T/32 wave pairs
+// (two waves per SIMD).  Both waves of pair p keep K and V rows 32p..32p+31
+// as MFMA operands; wave h of the pair computes S and dP for query rows
+// 32h..32h+31 of the 64-row block, then both write P^T and dS^T (bf16) to
+// LDS, and wave h accumulates the d columns [h*D/2, (h+1)*D/2) of dK and dV
+// over all 64 query rows.  The 2*D/32 C tiles of the block's dQ partial are
+// spread over the waves.
 //
 // Workspace dQ layout: per (query head, 64-row block) a 64 x D fp32 block
 // stored as 32 x 32 MFMA C tiles (tile = qb * D/32 + db), each tile as
@@ -267,14 +297,17 @@ __global__ __launch_bounds__(256) void delta_kernel(const __bf16* __restrict__ o
 // Ordering protocol of the deterministic schedules.  The workspace and the
 // semaphores are only touched with device-scope relaxed atomic loads and
 // stores, which bypass the chiplet-local caches that are not coherent across
-// the device; no cache write-back or invalidate is issued.  A workgroup
-//   1. spins (one lane) until sem == ordinal, then a workgroup barrier;
-//   2. reads the block (ordinal > 0), adds its partial, writes it back;
-//   3. at the next sub-step's second barrier -- after every wave has waited
-//      for all of its outstanding vector memory operations, so the writes
-//      are complete at device scope -- one lane stores sem = ordinal + 1.
-// Deferring step 3 overlaps the write latency with the next sub-step's
-// compute; it never waits on another workgroup, so no cycle can form.
+// the device; no cache write-back or invalidate is issued.  Each wave that
+// holds dQ tiles
+//   1. spins until sem == ordinal;
+//   2. issues the loads of its tiles of the block (ordinal > 0), runs its
+//      dK/dV contraction while they are in flight, adds its partial and
+//      writes the tiles back;
+// and at the next sub-step's second barrier -- after every wave has waited
+// for all of its outstanding vector memory operations, so the writes are
+// complete at device scope -- one lane stores sem = ordinal + 1.  Deferring
+// the release overlaps the write latency with the next sub-step's compute;
+// it never waits on another workgroup, so no cycle can form.
 // ---------------------------------------------------------------------------
 struct BwdArgs {
   const __bf16* q;
@@ -286,6 +319,7 @@ struct BwdArgs {
   float* ws;
   int* sem;
   int* err;
+  float* dummy;      // 8 tiles of 1024 floats that absorb writes with no destination
   __bf16* dk;
   __bf16* dv;
   const int4* steps;
@@ -297,41 +331,77 @@ struct BwdArgs {
   int S, g, causal;
 };
 
+// Semaphore words per 64-row dQ block: one per wave that holds dQ tiles.
+constexpr int kSemPerBlock = 8;
+
+template <int T>
+constexpr int bwd_threads() {
+  return 64 * 2 * (T / 32);
+}
+
 template <int D, int T, bool ATOMIC>
-__global__ __launch_bounds__(2 * T, 1) void bwd_kernel(BwdArgs a) {
-  constexpr int NW = T / 32;          // waves; each owns 32 key/value rows
+__global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
+  constexpr int NP = T / 32;          // wave pairs; pair p owns key/value rows 32p .. 32p+31
+  constexpr int NW = 2 * NP;          // waves
   constexpr int NT = 64 * NW;
   constexpr int M = 64;               // query rows per sub-step
   constexpr int SUBS = T / M;
   constexpr int DC = D / 16;
   constexpr int DB = D / 32;
-  constexpr int TPW = 2 * DB / NW;    // dQ C tiles per wave
+  constexpr int DH = DB / 2;          // 32-wide d blocks of dK / dV per wave
+  constexpr int NQT = 2 * DB;         // 32 x 32 dQ tiles per 64-row block
+  constexpr int TPW = (NQT + NW - 1) / NW;
+  constexpr bool SHARE_K = (NW % DB) == 0;  // a wave's dQ tiles share one d block
   constexpr int KC = T / 16;          // 16-row key/value chunks of the dQ contraction
-  constexpr int PQ = 2 * D + 32;      // LDS pitch (bytes) of Q / dO / K rows: 32 mod 256
-  constexpr int PS = (M + 8) * 2;     // LDS pitch (bytes) of dS^T rows
+  constexpr int QC = M / 16;          // 16-row query chunks of the dK / dV contraction
+  constexpr int PQ = 2 * D + 48;      // LDS pitch (bytes) of Q / dO / K rows (see the LDS note above)
+  constexpr int PS = (M + 8) * 2;     // LDS pitch (bytes) of P^T / dS^T rows
   constexpr int QBUF = M * PQ;
   constexpr int OFF_Q = 0;                       // [2][M][PQ]
   constexpr int OFF_DO = OFF_Q + 2 * QBUF;       // [2][M][PQ]
   constexpr int OFF_K = OFF_DO + 2 * QBUF;       // [T][PQ]
-  constexpr int OFF_DS = OFF_K + T * PQ;         // [T][PS]  dS^T
+  constexpr int OFF_PT = OFF_K + T * PQ;         // [T][PS]  P^T
+  constexpr int OFF_DS = OFF_PT + T * PS;        // [T][PS]  dS^T
   constexpr int OFF_STAT = OFF_DS + T * PS;      // [2][2][M] f32: LSE (log2 domain), Delta
   constexpr int OFF_FLAG = OFF_STAT + 4 * M * 4;
   constexpr int SMEM = OFF_FLAG + 16;
   constexpr int QCH = M * D / 8 / NT;            // 16-byte chunks per thread of one Q (or dO) block
   static_assert(QCH >= 1 && (M * D / 8) % NT == 0, "tile split");
   static_assert(NT >= 2 * M, "one statistic per thread");
+  static_assert(DH >= 1 && SUBS >= 1, "shape");
+  static_assert(SMEM <= 160 * 1024, "LDS");
+  static_assert(NW <= kSemPerBlock || NQT <= kSemPerBlock, "semaphore words");
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
   LDS char* base = (LDS char*)smem;
   volatile LDS int* s_flag = (volatile LDS int*)(base + OFF_FLAG);
 
   const int lane = lane_id(), w = wave_id(), h2 = lane >> 5, c32 = lane & 31;
-  const int kv0 = 32 * w;  // first key/value row of this wave within the tile
+  const int hf = w & 1;                 // query half (S, dP) and d half (dK, dV) of this wave
+  const int kv0 = 32 * (w >> 1);        // first key/value row of this wave's pair
+  const int kv_local = kv0 + c32;
+  // Step lists are read-only for the kernel's lifetime: read them through the
+  // constant address space so that they become scalar loads.
+  const CONST_AS int* steps = (const CONST_AS int*)a.steps;
+  const CONST_AS int* offsets = (const CONST_AS int*)a.offsets;
+  auto step_at = [&](int i) { return make_int4(steps[4 * i], steps[4 * i + 1], steps[4 * i + 2], steps[4 * i + 3]); };
   const int wg = blockIdx.x;
-  const int beg = a.offsets[wg], end = a.offsets[wg + 1];
+  const int beg = offsets[wg], end = offsets[wg + 1];
   const int S = a.S, g = a.g;
   const int nblk = S / M;  // 64-row blocks per head
   unsigned long long stall = 0;
   const unsigned long long t_start = __builtin_amdgcn_s_memtime();
+  if (threadIdx.x == 0) *s_flag = 0;
+
+  // Per-lane LDS byte offsets (each access adds only compile-time constants).
+  const int tr_row = 8 * h2 + ((lane & 15) >> 2), tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int o_trq = opaque(tr_row * PQ + tr_col * 2);                  // transposing reads, pitch PQ
+  const int o_trq_h = opaque(tr_row * PQ + (tr_col + hf * DH * 32) * 2);  // ... in this wave's d half
+  const int o_trs = opaque(tr_row * PS + tr_col * 2);                  // transposing reads, pitch PS
+  const int o_rowq = opaque((32 * hf + c32) * PQ + 16 * h2);           // Q / dO rows of this wave's query half
+  const int o_rowt = opaque(kv_local * PS + 16 * h2);                  // P^T / dS^T rows of this lane
+  const int o_rowk = opaque(kv_local * PQ + 16 * h2);                  // K rows of this lane
+  const int o_stt = opaque(kv_local * PS + (32 * hf + 4 * h2) * 2);    // P^T / dS^T stores
+  const int o_stat = opaque((32 * hf + 4 * h2) * 4);                   // LSE / Delta of this lane's rows
 
   // Prefetch registers for the next Q/dO block and one LSE-or-Delta value.
   bf16x8 pq[QCH], pdo[QCH];
@@ -360,20 +430,35 @@ __global__ __launch_bounds__(2 * T, 1) void bwd_kernel(BwdArgs a) {
     if (threadIdx.x < 2 * M) *(LDS float*)(base + OFF_STAT + (buf * 2 * M + threadIdx.x) * 4) = pstat * st_mul;
   };
 
-  bf16x8 kb[DC], vb[DC];
-  f32x16 dk_acc[DB], dv_acc[DB];
+  bf16x8 vb[DC];  // V rows of this pair as MFMA operands (K is read from LDS)
+  f32x16 dk_acc[DH], dv_acc[DH];
   int buf = 0;
-  int* pend_sem = nullptr;  // semaphore to release at the next second barrier
-  int pend_val = 0;
+  // dQ read-modify-write pipelined by one sub-step (deterministic schedules):
+  // the block computed in sub-step s is read (after the wait) at the end of
+  // s, added and written after the S/dP phase of s+1, and its semaphore is
+  // released at the end of s+1, once the writes are complete.
+  f32x16 pdq[TPW], pprev[TPW];
+  // The vector-memory sequence of a sub-step is the same on every path (a
+  // missing prefetch re-reads the current block, a missing write goes to the
+  // dummy tiles), so the compiler's wait counts stay exact and no wait drains
+  // more than the operation it is for.
+  float* p_ws = a.dummy;  // block whose partial is pending (the dummy tiles if none)
+  int* p_sem = nullptr;   // its semaphore, if it is a real block
+  int p_val = 0;
+  bool p_add = false;
+  int* r_sem = nullptr;  // semaphore to release once this wave's writes are complete
+  int r_val = 0;
+  constexpr bool EVEN = (NQT % NW) == 0;  // every wave holds NQT / NW dQ tiles
+  const bool has_tiles = EVEN || w < NQT;
   if (beg < end) {
-    const int4 r0 = a.steps[beg];
+    const int4 r0 = step_at(beg);
     load_block(r0.x, r0.y * T);
     store_block(0);
   }
   bool aborted = false;
 
   for (int i = beg; i < end && !aborted; ++i) {
-    const int4 rec = a.steps[i];
+    const int4 rec = step_at(i);
     const int head = rec.x, qi = rec.y, kj = rec.z, ordf = rec.w;
     const int ord = ordf & ((1 << 28) - 1);
     const bool first = ordf & (1 << 28), last = ordf & (1 << 29);
@@ -382,14 +467,11 @@ __global__ __launch_bounds__(2 * T, 1) void bwd_kernel(BwdArgs a) {
     const __bf16* vh = a.v + ((size_t)kvh * S + (size_t)kj * T) * D;
     if (first) {
 #pragma unroll
-      for (int c = 0; c < DC; ++c) {
-        kb[c] = *(const bf16x8*)(kh + (size_t)(kv0 + c32) * D + 16 * c + 8 * h2);
-        vb[c] = *(const bf16x8*)(vh + (size_t)(kv0 + c32) * D + 16 * c + 8 * h2);
-      }
+      for (int c = 0; c < DC; ++c) vb[c] = *(const bf16x8*)(vh + (size_t)kv_local * D + 16 * c + 8 * h2);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        dk_acc[db] = f32x16{};
-        dv_acc[db] = f32x16{};
+      for (int j = 0; j < DH; ++j) {
+        dk_acc[j] = f32x16{};
+        dv_acc[j] = f32x16{};
       }
       __syncthreads();  // previous chain's dQ contraction is done with sK
       for (int ch = threadIdx.x; ch < T * D / 8; ch += NT) {
@@ -400,116 +482,109 @@ __global__ __launch_bounds__(2 * T, 1) void bwd_kernel(BwdArgs a) {
     const bool diag = a.causal && (qi == kj);
 
     for (int sub = 0; sub < SUBS; ++sub) {
-      __syncthreads();  // B1: Q/dO/LSE/Delta of this block (and sK) visible
-      // Prefetch the next block while this one is computed.
-      int nhead = -1, nrow = 0;
+      __syncthreads();  // B1: Q/dO/LSE/Delta of this block (and sK) visible; P^T, dS^T free
+      if (*s_flag) {    // a wave gave up waiting in the previous sub-step
+        aborted = true;
+        break;
+      }
+      // Prefetch the next block while this one is computed (issued before this
+      // sub-step's dQ writes, so staging it never waits for them).
+      int nhead = head, nrow = qi * T + sub * M;  // no next block: re-read this one
       if (sub + 1 < SUBS) {
-        nhead = head;
         nrow = qi * T + (sub + 1) * M;
       } else if (i + 1 < end) {
-        const int4 nr = a.steps[i + 1];
+        const int4 nr = step_at(i + 1);
         nhead = nr.x;
         nrow = nr.y * T;
       }
-      if (nhead >= 0) load_block(nhead, nrow);
-
+      load_block(nhead, nrow);
       const LDS char* sq = base + OFF_Q + buf * QBUF;
       const LDS char* sdo = base + OFF_DO + buf * QBUF;
       const LDS float* slse = (const LDS float*)(base + OFF_STAT + buf * 2 * M * 4);
       const LDS float* sdel = slse + M;
-      const int kv_local = kv0 + c32;
 
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        // S = Q K^T and dP = dO V^T for 32 query rows x this wave's 32 key/value columns.
-        bf16x8 aq[DC], ado[DC];
-#pragma unroll
-        for (int c = 0; c < DC; ++c) {
-          const int off = (qb * 32 + c32) * PQ + (16 * c + 8 * h2) * 2;
-          aq[c] = lds_row8(sq + off);
-          ado[c] = lds_row8(sdo + off);
-        }
+      {
+        // S = Q K^T and dP = dO V^T for query rows 32*hf .. +31 x this pair's 32 key/value columns.
         f32x16 s = f32x16{}, dp = f32x16{};
+        constexpr int NPART = DC >= 8 ? 4 : 2;  // operands are read in parts to bound register use
+        constexpr int HC = DC / NPART;
 #pragma unroll
-        for (int c = 0; c < DC; ++c) {
-          s = mfma32(aq[c], kb[c], s);
-          dp = mfma32(ado[c], vb[c], dp);
+        for (int half = 0; half < NPART; ++half) {
+          bf16x8 aq[HC], ado[HC], bk[HC];
+#pragma unroll
+          for (int c = 0; c < HC; ++c) {
+            aq[c] = lds_row8(sq + o_rowq + 32 * (half * HC + c));
+            ado[c] = lds_row8(sdo + o_rowq + 32 * (half * HC + c));
+            bk[c] = lds_row8(base + OFF_K + o_rowk + 32 * (half * HC + c));
+          }
+#pragma unroll
+          for (int c = 0; c < HC; ++c) {
+            s = mfma32(aq[c], bk[c], s);
+            dp = mfma32(ado[c], vb[half * HC + c], dp);
+          }
         }
-        // P = exp2(S*scale*log2e - LSE*log2e); dS = P * (dP - Delta).
-        f32x4 l4[4], d4[4];
+        // P = exp2(S*scale*log2e - LSE*log2e); dS = P * (dP - Delta); both to LDS transposed.
+        // On a diagonal tile P is zero where key/value row > query row; the bound is made
+        // opaque so that the comparisons are formed here rather than kept live across the loop.
+        int kv_minus_q = kv_local - (sub * M + 32 * hf + 4 * h2);
+        asm volatile("" : "+v"(kv_minus_q));
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          l4[j] = *(const LDS f32x4*)(slse + qb * 32 + 8 * j + 4 * h2);
-          d4[j] = *(const LDS f32x4*)(sdel + qb * 32 + 8 * j + 4 * h2);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
+          const f32x4 l4 = *(const LDS f32x4*)((const LDS char*)slse + o_stat + 32 * j);
+          const f32x4 d4 = *(const LDS f32x4*)((const LDS char*)sdel + o_stat + 32 * j);
+          bf16x4 tp, ts;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * j + e;
-            float p = __builtin_amdgcn_exp2f(s[r] * a.scale_log2 - l4[j][e]);
-            if (diag && kv_local > sub * M + qb * 32 + 8 * j + 4 * h2 + e) p = 0.f;
-            s[r] = p;
-            dp[r] = p * (dp[r] - d4[j][e]);
+            float p = __builtin_amdgcn_exp2f(s[r] * a.scale_log2 - l4[e]);
+            if (diag && kv_minus_q > 8 * j + e) p = 0.f;
+            tp[e] = (__bf16)p;
+            ts[e] = (__bf16)(p * (dp[r] - d4[e]));
           }
-        // dS^T to LDS for the dQ contraction (4 consecutive query rows per store).
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          bf16x4 t4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) t4[e] = (__bf16)dp[4 * j + e];
-          *(LDS bf16x4*)(base + OFF_DS + kv_local * PS + (qb * 32 + 8 * j + 4 * h2) * 2) = t4;
-        }
-        // dV += P^T dO, dK += dS^T Q over these 32 query rows.
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const bf16x8 ap = pack8(s, 8 * e);
-          const bf16x8 ads = pack8(dp, 8 * e);
-          const int row0 = qb * 32 + 16 * e + 4 * h2;
-          bf16x8 bdo[DB], bq[DB];
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            bdo[db] = lds_tr8_split(sdo, PQ, row0, db * 32, lane);
-            bq[db] = lds_tr8_split(sq, PQ, row0, db * 32, lane);
-          }
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            dv_acc[db] = mfma32(ap, bdo[db], dv_acc[db]);
-            dk_acc[db] = mfma32(ads, bq[db], dk_acc[db]);
-          }
+          *(LDS bf16x4*)(base + OFF_PT + o_stt + 16 * j) = tp;
+          *(LDS bf16x4*)(base + OFF_DS + o_stt + 16 * j) = ts;
         }
       }
-      // The other buffer is free (read before B1): stage the prefetched block.
-      if (nhead >= 0) store_block(buf ^ 1);
-      if constexpr (!ATOMIC) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();  // B2: dS^T complete; previous dQ writes complete
       if constexpr (!ATOMIC) {
-        if (pend_sem != nullptr && threadIdx.x == 0)
-          __hip_atomic_store(pend_sem, pend_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        pend_sem = nullptr;
+        // Finish the pending block: its predecessor's partial has arrived.  The
+        // sum is formed on every path so that no path leaves the reads pending.
+        // (A select, not a multiply by zero: a value read without a predecessor
+        // is arbitrary bits, possibly NaN.)
+        if (has_tiles) {  // compile-time true when the tiles divide evenly over the waves
+#pragma unroll
+          for (int ti = 0; ti < TPW; ++ti) {
+            const int t_idx = w + NW * ti;
+            float* p = ((EVEN || t_idx < NQT) ? p_ws : a.dummy) + t_idx * 1024 + lane;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float sum = pdq[ti][r] + pprev[ti][r];
+              __hip_atomic_store(p + r * 64, p_add ? sum : pdq[ti][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+          }
+        }
+        r_sem = p_sem;
+        r_val = p_val;
       }
+      __syncthreads();  // B2: P^T, dS^T complete
 
-      // dQ partial = dS K over all T key/value rows of the tile.
+      // dQ partial = dS K over all T key/value rows, for this wave's C tiles.
       f32x16 dq[TPW];
       {
-        // tile t = w + NW*ti has d block t % DB; the blocks repeat every NDB tiles
-        constexpr int NDB = (DB / gcd_c(DB, NW)) < TPW ? (DB / gcd_c(DB, NW)) : TPW;
-        static_assert(TPW % NDB == 0 && (NW * NDB) % DB == 0 || NDB == TPW, "tile split");
+        bf16x8 bk[KC];
 #pragma unroll
-        for (int nd = 0; nd < NDB; ++nd) {
-          const int db = (w + NW * nd) % DB;
-          bf16x8 bk[KC];
+        for (int ti = 0; ti < TPW; ++ti) {
+          const int t_idx = w + NW * ti;
+          if (EVEN || t_idx < NQT) {
+            const int qb = t_idx / DB, db = t_idx % DB;
+            if (ti == 0 || !SHARE_K) {
+              const LDS char* pk = base + OFF_K + o_trq + db * 64;
 #pragma unroll
-          for (int c = 0; c < KC; ++c) bk[c] = lds_tr8_consecutive(base + OFF_K, PQ, 16 * c + 8 * h2, db * 32, lane);
-#pragma unroll
-          for (int ti = nd; ti < TPW; ti += NDB) {
-            const int t_idx = w + NW * ti, qb = t_idx / DB;
-            bf16x8 ads[KC];
-#pragma unroll
-            for (int c = 0; c < KC; ++c) ads[c] = lds_tr8_consecutive(base + OFF_DS, PS, 16 * c + 8 * h2, qb * 32, lane);
+              for (int c = 0; c < KC; ++c) bk[c] = lds_tr8_at(pk + 16 * c * PQ, PQ);
+            }
+            const LDS char* pds = base + OFF_DS + o_trs + qb * 64;
             f32x16 acc = f32x16{};
 #pragma unroll
-            for (int c = 0; c < KC; ++c) acc = mfma32(ads[c], bk[c], acc);
+            for (int c = 0; c < KC; ++c) acc = mfma32(lds_tr8_at(pds + 16 * c * PS, PS), bk[c], acc);
             dq[ti] = acc;
           }
         }
@@ -520,78 +595,120 @@ __global__ __launch_bounds__(2 * T, 1) void bwd_kernel(BwdArgs a) {
       if constexpr (ATOMIC) {
 #pragma unroll
         for (int ti = 0; ti < TPW; ++ti) {
-          float* p = wsb + (w + NW * ti) * 1024 + lane;
+          const int t_idx = w + NW * ti;
+          if (EVEN || t_idx < NQT) {
+            float* p = wsb + t_idx * 1024 + lane;
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            __hip_atomic_fetch_add(p + r * 64, dq[ti][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      } else {
-        int* semp = a.sem + (size_t)head * nblk + blk;
-        if (threadIdx.x == 0) {
-          int ab = 0;
-          if (ord > 0) {
-            const unsigned long long t0 = __builtin_amdgcn_s_memtime();
-            const long long deadline = (long long)__builtin_amdgcn_s_memrealtime() + a.spin_ticks;
-            while (__hip_atomic_load(semp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != ord) {
-              if (__hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) { ab = 1; break; }
-              if ((long long)__builtin_amdgcn_s_memrealtime() > deadline) {
-                __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                ab = 1;
-                break;
-              }
-              __builtin_amdgcn_s_sleep(1);
-            }
-            stall += __builtin_amdgcn_s_memtime() - t0;
+            for (int r = 0; r < 16; ++r)
+              __hip_atomic_fetch_add(p + r * 64, dq[ti][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
-          *s_flag = ab;
         }
-        __syncthreads();  // B3: the predecessor's dQ writes are complete at device scope
-        if (*s_flag) {
-          aborted = true;
-          break;
+      }
+
+      // dV += P^T dO, dK += dS^T Q over the block's 64 query rows, d half hf.
+#pragma unroll
+      for (int c = 0; c < QC; ++c) {
+        const bf16x8 ap = lds_row8(base + OFF_PT + o_rowt + 32 * c);
+        const bf16x8 ads = lds_row8(base + OFF_DS + o_rowt + 32 * c);
+        bf16x8 bdo[DH], bq[DH];
+#pragma unroll
+        for (int j = 0; j < DH; ++j) {
+          bdo[j] = lds_tr8_at(sdo + o_trq_h + 16 * c * PQ + 64 * j, PQ);
+          bq[j] = lds_tr8_at(sq + o_trq_h + 16 * c * PQ + 64 * j, PQ);
         }
-        if (ord > 0) {
-          f32x16 prev[TPW];
+#pragma unroll
+        for (int j = 0; j < DH; ++j) {
+          dv_acc[j] = mfma32(ap, bdo[j], dv_acc[j]);
+          dk_acc[j] = mfma32(ads, bq[j], dk_acc[j]);
+        }
+      }
+      // The other buffer is free (read before B1): stage the prefetched block.
+      store_block(buf ^ 1);
+      buf ^= 1;
+
+      if constexpr (!ATOMIC) {
+        // Release the block finished in this sub-step once its writes are complete.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (r_sem != nullptr && lane == 0) __hip_atomic_store(r_sem, r_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        r_sem = nullptr;
+        // Wait for this block's predecessor, then start reading its partial.
+        int* semp = a.sem + ((size_t)head * nblk + blk) * kSemPerBlock + w;
+        bool give_up = false;
+        if (has_tiles && ord > 0) {
+          const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+          const long long deadline = (long long)__builtin_amdgcn_s_memrealtime() + a.spin_ticks;
+          while (__builtin_amdgcn_readfirstlane(__hip_atomic_load(semp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != ord) {
+            if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0) {
+              give_up = true;
+              break;
+            }
+            if ((long long)__builtin_amdgcn_s_memrealtime() > deadline) {
+              if (lane == 0) __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              give_up = true;
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+          }
+          stall += __builtin_amdgcn_s_memtime() - t0;
+        }
+        // The reads are issued on every path of a wave holding tiles (an ordinal
+        // of zero or a wave that gave up reads its tiles and ignores them), so that
+        // no path merge copies the registers before the loads complete.
+        if (has_tiles) {
 #pragma unroll
           for (int ti = 0; ti < TPW; ++ti) {
-            float* p = wsb + (w + NW * ti) * 1024 + lane;
+            const int t_idx = w + NW * ti;
+            const float* p = wsb + (t_idx < NQT ? t_idx : t_idx % NQT) * 1024 + lane;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) prev[ti][r] = __hip_atomic_load(p + r * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int r = 0; r < 16; ++r)
+              pprev[ti][r] = __hip_atomic_load(p + r * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
-#pragma unroll
-          for (int ti = 0; ti < TPW; ++ti) dq[ti] += prev[ti];
         }
 #pragma unroll
-        for (int ti = 0; ti < TPW; ++ti) {
-          float* p = wsb + (w + NW * ti) * 1024 + lane;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) __hip_atomic_store(p + r * 64, dq[ti][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        pend_sem = semp;
-        pend_val = ord + 1;
+        for (int ti = 0; ti < TPW; ++ti) pdq[ti] = dq[ti];
+        const bool real = has_tiles && !give_up;
+        p_ws = real ? wsb : a.dummy;
+        p_sem = real ? semp : nullptr;
+        p_val = ord + 1;
+        p_add = ord > 0;
+        if (give_up && lane == 0) *s_flag = 1;  // everybody leaves after the next first barrier
       }
-      buf ^= 1;
     }
 
     if (last && !aborted) {
-      // Chain epilogue: single writer of dK (scaled) and dV for this tile.
-      __bf16* dkh = a.dk + ((size_t)kvh * S + (size_t)kj * T) * D;
-      __bf16* dvh = a.dv + ((size_t)kvh * S + (size_t)kj * T) * D;
+      // Chain epilogue: single writer of dK (scaled) and dV for this wave's rows and d half.
+      const size_t o_lane = (size_t)opaque((kv0 + 4 * h2) * D + hf * DH * 32 + c32);
+      __bf16* dkh = a.dk + ((size_t)kvh * S + (size_t)kj * T) * D + o_lane;
+      __bf16* dvh = a.dv + ((size_t)kvh * S + (size_t)kj * T) * D + o_lane;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int j = 0; j < DH; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = kv0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-          dkh[(size_t)row * D + db * 32 + c32] = (__bf16)(dk_acc[db][r] * a.scale);
-          dvh[(size_t)row * D + db * 32 + c32] = (__bf16)dv_acc[db][r];
+          const int off = (8 * (r >> 2) + (r & 3)) * D + j * 32;
+          dkh[off] = (__bf16)(dk_acc[j][r] * a.scale);
+          dvh[off] = (__bf16)dv_acc[j][r];
         }
     }
   }
   if constexpr (!ATOMIC) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (pend_sem != nullptr && !aborted && threadIdx.x == 0)
-      __hip_atomic_store(pend_sem, pend_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (*s_flag) aborted = true;
+    if (!aborted && p_sem != nullptr) {
+      // Drain: the last block of this wave.
+#pragma unroll
+      for (int ti = 0; ti < TPW; ++ti) {
+        const int t_idx = w + NW * ti;
+        if (EVEN || t_idx < NQT) {
+          if (p_add) pdq[ti] += pprev[ti];
+          float* p = p_ws + t_idx * 1024 + lane;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            __hip_atomic_store(p + r * 64, pdq[ti][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (lane == 0) __hip_atomic_store(p_sem, p_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   if (a.stall && threadIdx.x == 0) {
     a.stall[2 * wg] = stall;
@@ -671,6 +788,7 @@ hipError_t launch_bwd(const BwdLaunch& L, hipStream_t st) {
   a.ws = L.ws;
   a.sem = L.sem;
   a.err = L.err;
+  a.dummy = L.dummy;
   a.dk = (__bf16*)L.dk;
   a.dv = (__bf16*)L.dv;
   a.steps = (const int4*)L.steps;
@@ -685,8 +803,9 @@ hipError_t launch_bwd(const BwdLaunch& L, hipStream_t st) {
   dim3 grid(L.P);
 #define DASH_BWD_CASE(D_, T_)                                                                     \
   if (L.D == D_ && L.T == T_) {                                                                   \
-    if (L.atomic) hipLaunchKernelGGL((bwd_kernel<D_, T_, true>), grid, dim3(2 * T_), 0, st, a);   \
-    else hipLaunchKernelGGL((bwd_kernel<D_, T_, false>), grid, dim3(2 * T_), 0, st, a);           \
+    const dim3 block(bwd_threads<T_>());                                                          \
+    if (L.atomic) hipLaunchKernelGGL((bwd_kernel<D_, T_, true>), grid, block, 0, st, a);          \
+    else hipLaunchKernelGGL((bwd_kernel<D_, T_, false>), grid, block, 0, st, a);                  \
     return hipGetLastError();                                                                     \
   }
   DASH_BWD_CASE(128, 128)
@@ -702,8 +821,8 @@ hipError_t bwd_kernel_fits(int D, int T, bool atomic, int num_cu, int P, bool* f
   hipError_t e = hipErrorInvalidValue;
 #define DASH_OCC_CASE(D_, T_)                                                                                  \
   if (D == D_ && T == T_)                                                                                      \
-    e = atomic ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_kernel<D_, T_, true>, 2 * T_, 0)    \
-               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_kernel<D_, T_, false>, 2 * T_, 0);
+    e = atomic ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_kernel<D_, T_, true>, bwd_threads<T_>(), 0) \
+               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_kernel<D_, T_, false>, bwd_threads<T_>(), 0);
   DASH_OCC_CASE(128, 128)
   DASH_OCC_CASE(64, 128)
   DASH_OCC_CASE(128, 64)

@@ -17,6 +17,7 @@ struct BwdLaunch {
   float* ws;           // fp32 dQ accumulator, fragment order
   int* sem;            // one per (query head, 64-row block)
   int* err;            // error word (non-zero: a wait timed out)
+  float* dummy;        // 8 x 1024 floats absorbing writes with no destination
   void* dk;
   void* dv;
   const int32_t* steps;    // 4 ints per step

@@ -73,7 +73,8 @@ def test_result_independent_of_workgroup_count(sched, causal, wgs):
 
 
 def test_semaphores_count_every_contribution():
-    # After the kernel each 64-row block's semaphore equals its contributor count.
+    # After the kernel every semaphore word of each 64-row block (one per wave
+    # holding dQ tiles: 8 for D=128 and 128-row tiles) equals its contributor count.
     from scheduling_persistent_fa_amd.attention import workspace_bytes
     B, Hq, S, D, T = 1, 2, 1024, 128, 128
     pb = DeviceProblem(B, Hq, Hq, S, D, True)
@@ -85,9 +86,9 @@ def test_semaphores_count_every_contribution():
     align = lambda x: (x + 255) // 256 * 256
     rows = B * Hq * S
     sem_off = align(align(rows * D * 4) + rows * 4) // 4  # after the fp32 dQ accumulator and Delta
-    sem = ws[sem_off: sem_off + rows // 64].cpu().numpy().reshape(B * Hq, S // 64)
+    sem = ws[sem_off: sem_off + rows // 64 * 8].cpu().numpy().reshape(B * Hq, S // 64, 8)
     expect = np.array([(blk * 64) // T + 1 for blk in range(S // 64)])
-    assert (sem == expect[None, :]).all()
+    assert (sem == expect[None, :, None]).all()
 
 
 @pytest.mark.parametrize("causal", [False, True])
