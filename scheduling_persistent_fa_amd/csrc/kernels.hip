@@ -592,6 +592,12 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
 
       const int blk = qi * SUBS + sub;
       float* wsb = a.ws + ((size_t)head * nblk + blk) * (size_t)(M * D);
+      int* semp = a.sem + ((size_t)head * nblk + blk) * kSemPerBlock + w;
+      // First look at this block's semaphore now, so that its latency is hidden
+      // behind the dK/dV contraction (in the lockstep schedules the predecessor
+      // has usually released it by now); the wait below only polls if not.
+      int sem_seen = 0;
+      if constexpr (!ATOMIC) sem_seen = __hip_atomic_load(semp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if constexpr (ATOMIC) {
 #pragma unroll
         for (int ti = 0; ti < TPW; ++ti) {
@@ -631,10 +637,11 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         if (r_sem != nullptr && lane == 0) __hip_atomic_store(r_sem, r_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         r_sem = nullptr;
-        // Wait for this block's predecessor, then start reading its partial.
-        int* semp = a.sem + ((size_t)head * nblk + blk) * kSemPerBlock + w;
+        // Wait for this block's predecessor, then start reading its partial.  (The
+        // early value is consumed on every path, so it is never left pending.)
+        const bool ready = __builtin_amdgcn_readfirstlane(sem_seen) == ord;
         bool give_up = false;
-        if (has_tiles && ord > 0) {
+        if (has_tiles && ord > 0 && !ready) {
           const unsigned long long t0 = __builtin_amdgcn_s_memtime();
           const long long deadline = (long long)__builtin_amdgcn_s_memrealtime() + a.spin_ticks;
           while (__builtin_amdgcn_readfirstlane(__hip_atomic_load(semp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != ord) {
