@@ -366,7 +366,8 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
   constexpr int OFF_FLAG = OFF_STAT + 4 * M * 4;
   constexpr int SMEM = OFF_FLAG + 16;
   constexpr int QCH = M * D / 8 / NT;            // 16-byte chunks per thread of one Q (or dO) block
-  static_assert(QCH >= 1 && (M * D / 8) % NT == 0, "tile split");
+  constexpr int KCH = T * D / 8 / NT;            // 16-byte chunks per thread of one K tile
+  static_assert(QCH >= 1 && (M * D / 8) % NT == 0 && KCH >= 1 && (T * D / 8) % NT == 0, "tile split");
   static_assert(NT >= 2 * M, "one statistic per thread");
   static_assert(DH >= 1 && SUBS >= 1, "shape");
   static_assert(SMEM <= 160 * 1024, "LDS");
@@ -432,6 +433,22 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
 
   bf16x8 vb[DC];  // V rows of this pair as MFMA operands (K is read from LDS)
   f32x16 dk_acc[DH], dv_acc[DH];
+  // Chain epilogue: single writer of dK (scaled) and dV for this wave's rows and d half.
+  bool epi_pending = false;
+  int epi_kvh = 0, epi_kj = 0;
+  auto write_dkdv = [&](int kvh_, int kj_) {
+    const size_t o_lane = (size_t)opaque((kv0 + 4 * h2) * D + hf * DH * 32 + c32);
+    __bf16* dkh = a.dk + ((size_t)kvh_ * S + (size_t)kj_ * T) * D + o_lane;
+    __bf16* dvh = a.dv + ((size_t)kvh_ * S + (size_t)kj_ * T) * D + o_lane;
+#pragma unroll
+    for (int j = 0; j < DH; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = (8 * (r >> 2) + (r & 3)) * D + j * 32;
+        dkh[off] = (__bf16)(dk_acc[j][r] * a.scale);
+        dvh[off] = (__bf16)dv_acc[j][r];
+      }
+  };
   int buf = 0;
   // dQ read-modify-write pipelined by one sub-step (deterministic schedules):
   // the block computed in sub-step s is read (after the wait) at the end of
@@ -466,17 +483,29 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
     const __bf16* kh = a.k + ((size_t)kvh * S + (size_t)kj * T) * D;
     const __bf16* vh = a.v + ((size_t)kvh * S + (size_t)kj * T) * D;
     if (first) {
+      // New chain: its V rows to registers and its K tile to LDS.  The previous
+      // chain's dK/dV are written only after that, so that waiting for these
+      // loads never waits for those writes to drain.
 #pragma unroll
       for (int c = 0; c < DC; ++c) vb[c] = *(const bf16x8*)(vh + (size_t)kv_local * D + 16 * c + 8 * h2);
+      bf16x8 kt[KCH];
+#pragma unroll
+      for (int u = 0; u < KCH; ++u) {
+        const int ch = threadIdx.x + u * NT, row = ch / (D / 8), col = (ch % (D / 8)) * 8;
+        kt[u] = *(const bf16x8*)(kh + (size_t)row * D + col);
+      }
+      __syncthreads();  // previous chain's dQ contraction is done with sK
+#pragma unroll
+      for (int u = 0; u < KCH; ++u) {
+        const int ch = threadIdx.x + u * NT, row = ch / (D / 8), col = (ch % (D / 8)) * 8;
+        *(LDS bf16x8*)(base + OFF_K + row * PQ + col * 2) = kt[u];
+      }
+      if (epi_pending) write_dkdv(epi_kvh, epi_kj);
+      epi_pending = false;
 #pragma unroll
       for (int j = 0; j < DH; ++j) {
         dk_acc[j] = f32x16{};
         dv_acc[j] = f32x16{};
-      }
-      __syncthreads();  // previous chain's dQ contraction is done with sK
-      for (int ch = threadIdx.x; ch < T * D / 8; ch += NT) {
-        const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-        *(LDS bf16x8*)(base + OFF_K + row * PQ + col * 2) = *(const bf16x8*)(kh + (size_t)row * D + col);
       }
     }
     const bool diag = a.causal && (qi == kj);
@@ -682,21 +711,13 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
       }
     }
 
-    if (last && !aborted) {
-      // Chain epilogue: single writer of dK (scaled) and dV for this wave's rows and d half.
-      const size_t o_lane = (size_t)opaque((kv0 + 4 * h2) * D + hf * DH * 32 + c32);
-      __bf16* dkh = a.dk + ((size_t)kvh * S + (size_t)kj * T) * D + o_lane;
-      __bf16* dvh = a.dv + ((size_t)kvh * S + (size_t)kj * T) * D + o_lane;
-#pragma unroll
-      for (int j = 0; j < DH; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int off = (8 * (r >> 2) + (r & 3)) * D + j * 32;
-          dkh[off] = (__bf16)(dk_acc[j][r] * a.scale);
-          dvh[off] = (__bf16)dv_acc[j][r];
-        }
+    if (last && !aborted) {  // written at the next chain's start, or after the loop
+      epi_pending = true;
+      epi_kvh = kvh;
+      epi_kj = kj;
     }
   }
+  if (epi_pending && !aborted) write_dkdv(epi_kvh, epi_kj);
   if constexpr (!ATOMIC) {
     __syncthreads();
     if (*s_flag) aborted = true;
