@@ -34,15 +34,31 @@ def _one(pattern: str) -> str:
     return hits[0]
 
 
-def stats_table(prof_dir: str, out_md: str, command: str) -> None:
+def _steady_average_us(prof_dir: str, name: str, skip: int):
+    """Average duration of a kernel's dispatches after the first ``skip`` (warm-up) ones."""
+    try:
+        trace = _one(os.path.join(prof_dir, "**", "*kernel_trace.csv"))
+    except FileNotFoundError:
+        return None
+    durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in csv.DictReader(open(trace))
+            if r["Kernel_Name"] == name]
+    durs = durs[skip:]
+    return sum(durs) / len(durs) / 1e3 if durs else None
+
+
+def stats_table(prof_dir: str, out_md: str, command: str, skip: int = 3) -> None:
     rows = list(csv.DictReader(open(_one(os.path.join(prof_dir, "**", "*kernel_stats.csv")))))
     lines = [f"# Kernel times — `{os.path.basename(out_md)}`", "", "Command:", "", "```", command, "```", "",
-             "| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
+             f"`steady` averages the dispatches after the first {skip} of each kernel (the warm-up calls).", "",
+             "| kernel | calls | average (us) | steady (us) | min (us) | max (us) | share |",
+             "|---|---|---|---|---|---|---|"]
     for r in rows:
+        steady = _steady_average_us(prof_dir, r["Name"], skip)
         name = r["Name"].replace("dash::(anonymous namespace)::", "").replace("|", "/")
         if len(name) > 90:
             name = name[:87] + "..."
-        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+        st = f"{steady:.1f}" if steady is not None else "-"
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {st} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
     open(out_md, "w").write("\n".join(lines) + "\n")
 
