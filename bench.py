@@ -70,6 +70,9 @@ def main():
     ap.add_argument("--no-atomic", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (calibrates HBM counters)")
+    ap.add_argument("--block", action="store_true",
+                    help="instead: fwd+bwd of a synthetic transformer block around the attention op "
+                         "(deterministic vs atomic backward); prints its own JSON line")
     args = ap.parse_args()
     if args.copy_probe:
         import torch
@@ -84,6 +87,9 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                                    "(the path shards by (batch, kv head) with no exchange; see DESIGN.md)"}))
         sys.exit(2)
+    if args.block:
+        block_bench(args)
+        return
 
     import torch
     from scheduling_persistent_fa_amd import _lib
@@ -119,6 +125,7 @@ def main():
             attn_bwd(q, k, v, o, do, lse, causal, sched, dq=dq, dk=dk, dv=dv, opts=make_opts(**base_opts))
         ref_bits = dq.view(torch.int16).clone(), dk.view(torch.int16).clone(), dv.view(torch.int16).clone()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        calls = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
         for a_, b_ in evs:  # materialise the underlying HIP events
             a_.record(stream)
             b_.record(stream)
@@ -127,20 +134,35 @@ def main():
         torch.cuda.synchronize()
         t_beg.record(stream)
         for i in range(args.steps):
+            calls[i][0].record(stream)
             attn_bwd(q, k, v, o, do, lse, causal, sched, dq=dq, dk=dk, dv=dv, opts=opts[i])
+            calls[i][1].record(stream)
         t_end.record(stream)
         torch.cuda.synchronize()
         ms = t_beg.elapsed_time(t_end) / args.steps
-        kms = sum(a_.elapsed_time(b_) for a_, b_ in evs) / args.steps
+        kms_each = [a_.elapsed_time(b_) for a_, b_ in evs]
+        step_each = sorted(a_.elapsed_time(b_) for a_, b_ in calls)
+        kms = sum(kms_each) / args.steps
         same = all(torch.equal(x.view(torch.int16), r) for x, r in zip((dq, dk, dv), ref_bits))
+        pct = lambda xs, p: xs[min(len(xs) - 1, max(0, int(round(p * (len(xs) - 1)))))]
         rec = {"ms_per_step": ms, "tflops": fl / (ms * 1e-3) / 1e12, "kernel_ms": kms,
-               "kernel_tflops": fl / (kms * 1e-3) / 1e12, "repeat_bitwise": bool(same)}
+               "kernel_tflops": fl / (kms * 1e-3) / 1e12, "repeat_bitwise": bool(same),
+               # per-step call times: the median and the 10th / 90th percentiles as TFLOP/s
+               "tflops_p50": fl / (pct(step_each, 0.5) * 1e-3) / 1e12,
+               "tflops_p10": fl / (pct(step_each, 0.9) * 1e-3) / 1e12,
+               "tflops_p90": fl / (pct(step_each, 0.1) * 1e-3) / 1e12}
         if sched != _lib.ATOMIC:
             stall = torch.zeros(2 * info["num_cu"], dtype=torch.int64, device="cuda")
+            ke = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            ke[0].record(stream)  # materialise the underlying HIP events
+            ke[1].record(stream)
             attn_bwd(q, k, v, o, do, lse, causal, sched, dq=dq, dk=dk, dv=dv,
-                     opts=make_opts(stall=stall, sync_check=True, **base_opts))
-            st = stall.view(-1, 2).double().sum(0).tolist()
+                     opts=make_opts(stall=stall, sync_check=True, events=ke, **base_opts))
+            x_ = stall.view(-1, 2).double()
+            st = x_.sum(0).tolist()
             rec["sem_stall_frac"] = st[0] / max(st[1], 1.0)
+            # shader clock under this load: in-kernel s_memtime cycles over the launch's event time
+            rec["sclk_ghz_est"] = x_[:, 1].max().item() / (ke[0].elapsed_time(ke[1]) * 1e6)
         results[name] = rec
         print(f"[bench]   {ms:.3f} ms/step  {rec['tflops']:.1f} TFLOP/s  kernel {kms:.3f} ms", file=sys.stderr, flush=True)
 
@@ -166,6 +188,7 @@ def main():
         except Exception:
             traffic = None
     kt = det[best]["kernel_tflops"]
+    sclk = det[best].get("sclk_ghz_est")
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -183,6 +206,8 @@ def main():
                    "mask": "causal" if causal else "full", "tile": tile, "schedule": best,
                    "workgroups": info["num_cu"]},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "tflops_p10_p50_p90": [round(det[best][k], 2) for k in ("tflops_p10", "tflops_p50", "tflops_p90")],
+        "sclk_ghz_est": None if sclk is None else round(sclk, 3),
         "ratio_vs_atomic": None if ratio is None else round(ratio, 4),
         "fastest_atomic": best_atomic,
         "roofline": {"bound": "mfma", "achieved": round(kt, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -195,6 +220,65 @@ def main():
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(line), flush=True)
+
+
+def block_bench(args):
+    """Forward + backward of one synthetic transformer layer around the attention op.
+
+    Llama-3-8B-shaped (hidden 4096, 32 query heads, 8 key/value heads, head dim
+    128, SwiGLU MLP 14336), one sequence of 8192 tokens, causal, random-init
+    weights, bf16.  The layer's matrix products are plain torch 2-D products;
+    attention forward and backward are the library's.  Timed with the
+    deterministic backward (adaptive schedule) and with the atomic one, to show
+    the block-level share of the backward difference.
+    """
+    import torch
+    from scheduling_persistent_fa_amd.attention import ATOMIC, AUTO
+    from scheduling_persistent_fa_amd.autograd import dash_attention
+
+    S, hidden, Hq, Hkv, D, ffn = 8192, 4096, 32, 8, 128, 14336
+    torch.cuda.set_device(0)
+    g = torch.Generator(device="cuda").manual_seed(0)
+    def w(i, o):
+        return (torch.randn(i, o, device="cuda", generator=g) / math.sqrt(i)).to(torch.bfloat16).requires_grad_(True)
+    Wqkv, Wo, W1, W3, W2 = w(hidden, (Hq + 2 * Hkv) * D), w(Hq * D, hidden), w(hidden, ffn), w(hidden, ffn), w(ffn, hidden)
+    x = torch.randn(S, hidden, device="cuda", generator=g).to(torch.bfloat16).requires_grad_(True)
+
+    def heads(t, h):  # [S, h*D] -> [1, h, S, D] contiguous
+        return t.view(S, h, D).transpose(0, 1).contiguous().unsqueeze(0)
+
+    def step(schedule):
+        qkv = torch.mm(x, Wqkv)
+        q = heads(qkv[:, :Hq * D], Hq)
+        k = heads(qkv[:, Hq * D:(Hq + Hkv) * D], Hkv)
+        v = heads(qkv[:, (Hq + Hkv) * D:], Hkv)
+        a = dash_attention(q, k, v, causal=True, schedule=schedule)
+        a2 = a.squeeze(0).transpose(0, 1).reshape(S, Hq * D)
+        h = x + torch.mm(a2, Wo)
+        m = torch.mm(torch.nn.functional.silu(torch.mm(h, W1)) * torch.mm(h, W3), W2)
+        out = h + m
+        out.float().square().mean().backward()
+
+    res = {}
+    for name, sched in (("deterministic", AUTO), ("atomic", ATOMIC)):
+        for _ in range(args.warmup):
+            step(sched)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step(sched)
+        torch.cuda.synchronize()
+        res[name] = (time.perf_counter() - t0) / args.steps * 1e3
+        print(f"[bench] block {name}: {res[name]:.3f} ms/step", file=sys.stderr, flush=True)
+    print(json.dumps({
+        "metric": "transformer-layer fwd+bwd time with the library's attention (1 GPU)",
+        "unit": "ms", "higher_is_better": False, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "llama3_8b_shaped_layer_s8192", "S": S, "hidden": hidden, "Hq": Hq, "Hkv": Hkv,
+                   "D": D, "ffn": ffn, "mask": "causal"},
+        "ms_per_step": {k: round(v, 4) for k, v in res.items()},
+        "block_speedup_det_vs_atomic": round(res["atomic"] / res["deterministic"], 4),
+    }), flush=True)
 
 
 if __name__ == "__main__":

@@ -73,7 +73,8 @@ enum dash_schedule_kind {
   DASH_SCHED_DESC_Q = 1,
   DASH_SCHED_SHIFT = 2,
   DASH_SCHED_SYM_SHIFT = 3,
-  DASH_SCHED_ATOMIC = 4
+  DASH_SCHED_ATOMIC = 4,
+  DASH_SCHED_AUTO = 5      /* deterministic; the library picks one with dash_schedule_choose */
 };
 
 /* Optional knobs of dash_attn_bwd.  Zero-initialise, then set struct_size. */
@@ -107,7 +108,9 @@ int dash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
 
 /*
  * Backward pass: dQ, dK, dV (bfloat16) from Q, K, V, O, dO (bfloat16) and
- * lse (float32).  Runs the Delta = rowsum(dO * O) preprocess, the persistent
+ * lse (float32).  schedule is a dash_schedule_kind; DASH_SCHED_AUTO runs
+ * the one dash_schedule_choose picks (with its gang cap unless opts sets
+ * max_gang).  Runs the Delta = rowsum(dO * O) preprocess, the persistent
  * backward kernel (one workgroup per compute unit; each key/value tile's
  * chain stays on one workgroup with dK/dV in registers, [summary] §2.1), and
  * the dQ fp32 -> bf16 finalize.  For the deterministic schedules the result
@@ -162,6 +165,22 @@ int dash_schedule_simulate(const dash_schedule* s, double c, double r, double* m
                            double* total_wait);
 
 void dash_schedule_free(dash_schedule* s);
+
+/* Adaptive choice among the deterministic schedules for one problem shape:
+ * N tiles per sequence, head dim D, g query heads per key/value head, P
+ * workgroups.  The rule comes from measurements on MI355X, where the gang
+ * schedules beat SERIAL and DESC_Q on every measured shape (full and causal,
+ * D = 64 and 128, g = 1 and 4); the pages' H800 preference for DESC_Q at
+ * D > 64 ([summary] §3, register spilling) does not carry over, because
+ * dK/dV never spill in this kernel.  So:
+ *   full mask                 -> SHIFT
+ *   causal mask, N even       -> SYM_SHIFT
+ *   causal mask, N odd        -> DESC_Q
+ * and a gang larger than P (N, or N/2, > P) is capped at P (*max_gang = P,
+ * the gang takes its tiles in rounds); otherwise *max_gang = 0.  D and g are
+ * part of the key but do not change the choice on this hardware.
+ * DASH_ERR_INVALID_ARG for non-positive sizes or an unknown mask. */
+int dash_schedule_choose(int mask, int N, int D, int g, int P, int* schedule, int* max_gang);
 
 /* ---- misc -------------------------------------------------------------- */
 

@@ -22,8 +22,9 @@ ERR_TIMEOUT = -5
 ERR_WORKSPACE = -6
 
 MASK_FULL, MASK_CAUSAL = 0, 1
-SERIAL, DESC_Q, SHIFT, SYM_SHIFT, ATOMIC = 0, 1, 2, 3, 4
-SCHEDULE_NAMES = {SERIAL: "serial", DESC_Q: "desc_q", SHIFT: "shift", SYM_SHIFT: "sym_shift", ATOMIC: "atomic"}
+SERIAL, DESC_Q, SHIFT, SYM_SHIFT, ATOMIC, AUTO = 0, 1, 2, 3, 4, 5
+SCHEDULE_NAMES = {SERIAL: "serial", DESC_Q: "desc_q", SHIFT: "shift", SYM_SHIFT: "sym_shift", ATOMIC: "atomic",
+                  AUTO: "auto"}
 FIRST_FLAG = 1 << 28
 LAST_FLAG = 1 << 29
 ORD_MASK = FIRST_FLAG - 1
@@ -32,7 +33,8 @@ ORD_MASK = FIRST_FLAG - 1
 EXPORTS = (
     "dash_attn_fwd", "dash_attn_bwd", "dash_attn_bwd_workspace_bytes", "dash_attn_bwd_delta",
     "dash_schedule_build", "dash_schedule_num_workgroups", "dash_schedule_num_steps", "dash_schedule_export",
-    "dash_schedule_validate", "dash_schedule_simulate", "dash_schedule_free", "dash_status_string",
+    "dash_schedule_validate", "dash_schedule_simulate", "dash_schedule_free", "dash_schedule_choose",
+    "dash_status_string",
     "dash_last_error", "dash_device_info",
 )
 
@@ -81,6 +83,7 @@ def _declare(lib):
                                            ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
     lib.dash_schedule_free.argtypes = [vp]
     lib.dash_schedule_free.restype = None
+    lib.dash_schedule_choose.argtypes = [i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
     lib.dash_status_string.argtypes = [i]
     lib.dash_status_string.restype = ctypes.c_char_p
     lib.dash_last_error.argtypes = []

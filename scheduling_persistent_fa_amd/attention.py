@@ -10,7 +10,7 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import ATOMIC, DESC_Q, MASK_CAUSAL, MASK_FULL, SERIAL, SHIFT, SYM_SHIFT  # noqa: F401
+from ._lib import ATOMIC, AUTO, DESC_Q, MASK_CAUSAL, MASK_FULL, SERIAL, SHIFT, SYM_SHIFT  # noqa: F401
 
 
 def _ptr(t: torch.Tensor) -> ctypes.c_void_p:

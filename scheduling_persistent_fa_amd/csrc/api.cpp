@@ -187,6 +187,12 @@ int dash_schedule_simulate(const dash_schedule* s, double c, double r, double* m
 
 void dash_schedule_free(dash_schedule* s) { delete s; }
 
+int dash_schedule_choose(int mask, int N, int D, int g, int P, int* schedule, int* max_gang) {
+  if (!schedule || !max_gang) return fail(DASH_ERR_INVALID_ARG, "null output");
+  std::string err = dash::choose_schedule(mask, N, D, g, P, schedule, max_gang);
+  return err.empty() ? DASH_OK : fail(DASH_ERR_INVALID_ARG, err);
+}
+
 int dash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int S,
                   int D, float softmax_scale, int mask, void* stream) {
   const void* ptrs[] = {q, k, v, o, lse};
@@ -219,7 +225,7 @@ int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
   const void* ptrs[] = {q, k, v, o, dO, lse, dq, dk, dv};
   int st = check_common(ptrs, 9, B, Hq, Hkv, S, D, mask);
   if (st) return st;
-  if (schedule < DASH_SCHED_SERIAL || schedule > DASH_SCHED_ATOMIC) return fail(DASH_ERR_INVALID_ARG, "unknown schedule");
+  if (schedule < DASH_SCHED_SERIAL || schedule > DASH_SCHED_AUTO) return fail(DASH_ERR_INVALID_ARG, "unknown schedule");
   dash_bwd_opts op;
   std::memset(&op, 0, sizeof(op));
   if (opts) {
@@ -243,6 +249,12 @@ int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
   if (op.num_workgroups < 0) return fail(DASH_ERR_INVALID_ARG, "negative workgroup count");
   if (op.max_gang < 0) return fail(DASH_ERR_INVALID_ARG, "negative gang cap");
   const int g = Hq / Hkv;
+  if (schedule == DASH_SCHED_AUTO) {
+    int cap = 0;
+    std::string err = dash::choose_schedule(mask, N, D, g, P, &schedule, &cap);
+    if (!err.empty()) return fail(DASH_ERR_INVALID_ARG, err);
+    if (op.max_gang == 0) op.max_gang = cap;
+  }
   const int groups = B * Hkv;
   const bool atomic = schedule == DASH_SCHED_ATOMIC;
   const int xcd = op.xcd_local >= 0 ? 1 : 0;

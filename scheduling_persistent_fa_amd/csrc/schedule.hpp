@@ -43,6 +43,8 @@ std::string build_schedule(int mask, int kind, int N, int g, int groups, int P, 
                            int atomic_walk, int max_gang, Schedule* out);
 // Empty string if valid, else the first violation found.
 std::string validate_schedule(const Schedule& s);
+// The deterministic schedule (and gang cap) chosen for a shape; empty string on success.
+std::string choose_schedule(int mask, int N, int D, int g, int P, int* kind, int* max_gang);
 // Unit-cost DAG simulation; returns false on deadlock.
 bool simulate_schedule(const Schedule& s, double c, double r, double* makespan, double* total_wait);
 

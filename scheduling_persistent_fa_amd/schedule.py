@@ -8,6 +8,13 @@ import numpy as np
 from . import _lib
 
 
+def choose(mask: int, N: int, D: int, g: int, P: int):
+    """(schedule, max_gang) the library's adaptive rule picks for a shape."""
+    kind, cap = ctypes.c_int(), ctypes.c_int()
+    _lib.check(_lib.lib().dash_schedule_choose(mask, N, D, g, P, ctypes.byref(kind), ctypes.byref(cap)))
+    return kind.value, cap.value
+
+
 class Schedule:
     """Per-workgroup step lists built by ``dash_schedule_build``.
 

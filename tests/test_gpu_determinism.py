@@ -110,3 +110,26 @@ def test_capped_gangs_deterministic_and_correct(causal):
     ref = A.backward(pb.f64("q"), pb.f64("k"), pb.f64("v"), pb.f64("do"), pb.scale, causal)
     for got, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
         assert rel_err(to_f64(got), ref[name]) <= TOL
+
+
+@pytest.mark.parametrize("causal,S,wgs", [(False, 2048, 8), (True, 2048, 0), (True, 1920, 0)])
+def test_auto_schedule_runs_the_chosen_schedule(causal, S, wgs):
+    # AUTO must give the bits of the schedule (and gang cap) the adaptive rule names.
+    from oracle import attention as A
+    from scheduling_persistent_fa_amd.attention import AUTO, device_info
+    from scheduling_persistent_fa_amd.schedule import choose
+    B, H, D, T = 1, 2, 128, 128
+    pb = DeviceProblem(B, H, H, S, D, causal)
+    o, lse = attn_fwd(pb.q, pb.k, pb.v, causal)
+    P = wgs or device_info()["num_cu"]
+    kind, cap = choose(1 if causal else 0, S // T, D, 1, P)
+    say(f"[auto] causal={causal} S={S} P={P} -> {_lib.SCHEDULE_NAMES[kind]} cap {cap}")
+    got = attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, causal, AUTO,
+                   opts=make_opts(num_workgroups=wgs, sync_check=True))
+    d_auto = _digest(*got)
+    want = attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, causal, kind,
+                    opts=make_opts(num_workgroups=wgs, max_gang=cap, sync_check=True))
+    assert _digest(*want) == d_auto
+    ref = A.backward(pb.f64("q"), pb.f64("k"), pb.f64("v"), pb.f64("do"), pb.scale, causal)
+    for t, name in zip(got, ("dq", "dk", "dv")):
+        assert rel_err(to_f64(t), ref[name]) <= TOL

@@ -138,3 +138,21 @@ def test_wait_budget_exhaustion_is_reported_and_recovers():
     dq, dk, dv = attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, False, SERIAL, opts=make_opts(sync_check=True))
     torch.cuda.synchronize()
     assert rel_err(to_f64(dq), ref["dq"]) <= TOL and rel_err(to_f64(dk), ref["dk"]) <= TOL
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_autograd_op_gradients_match_oracle(causal):
+    # loss = sum(O * W) makes dO = W; the autograd op's gradients are the
+    # library's backward, checked against the float64 oracle.
+    from scheduling_persistent_fa_amd.autograd import dash_attention
+    B, Hq, Hkv, S, D = 1, 4, 2, 512, 64
+    pb = DeviceProblem(B, Hq, Hkv, S, D, causal)
+    say(f"[autograd] causal={causal}")
+    q, k, v = (t.clone().requires_grad_(True) for t in (pb.q, pb.k, pb.v))
+    o = dash_attention(q, k, v, causal=causal)
+    (o.float() * pb.do.float()).sum().backward()
+    torch.cuda.synchronize()
+    ref = A.backward(pb.f64("q"), pb.f64("k"), pb.f64("v"), pb.f64("do"), pb.scale, causal)
+    assert rel_err(to_f64(o), ref["o"]) <= TOL
+    for t, name in ((q, "dq"), (k, "dk"), (v, "dv")):
+        assert rel_err(to_f64(t.grad), ref[name]) <= TOL

@@ -113,3 +113,45 @@ def test_bwd_argument_errors_need_no_gpu():
     n = ctypes.c_size_t()
     assert L.dash_attn_bwd_workspace_bytes(2, 24, 24, 4096, 64, ctypes.byref(n)) == 0
     assert n.value >= 2 * 24 * 4096 * 64 * 4
+
+
+# Fastest deterministic schedule per workload, measured on MI355X (every
+# schedule of every workload timed on one device): the adaptive rule must
+# reproduce these choices.
+MEASURED_BEST = [  # (mask, N, D, g, P, schedule)
+    (Sch.FULL, 4, 64, 1, 4, _lib.SHIFT),           # B1 H1 S256 D64, tile 64, 4 workgroups
+    (Sch.CAUSAL, 16, 128, 1, 256, _lib.SYM_SHIFT),  # B4 H16 S2048 D128
+    (Sch.FULL, 32, 64, 1, 256, _lib.SHIFT),         # B2 H24 S4096 D64
+    (Sch.FULL, 128, 128, 1, 256, _lib.SHIFT),       # B1 H16 S16384 D128
+    (Sch.CAUSAL, 128, 128, 1, 256, _lib.SYM_SHIFT),  # same, causal
+    (Sch.CAUSAL, 64, 128, 4, 256, _lib.SYM_SHIFT),  # B1 Hq32 Hkv8 S8192 D128
+]
+
+
+@pytest.mark.parametrize("mask,N,D,g,P,best", MEASURED_BEST)
+def test_adaptive_choice_matches_measured_best(mask, N, D, g, P, best):
+    from scheduling_persistent_fa_amd.schedule import choose
+    assert choose(mask, N, D, g, P) == (best, 0)
+
+
+def test_adaptive_choice_rules():
+    from scheduling_persistent_fa_amd.schedule import choose
+    assert choose(Sch.CAUSAL, 5, 128, 1, 256) == (_lib.DESC_Q, 0)       # odd N: no symmetric shift
+    assert choose(Sch.FULL, 512, 128, 1, 256) == (_lib.SHIFT, 256)      # gang of 512 capped to the grid
+    assert choose(Sch.CAUSAL, 1024, 128, 1, 256) == (_lib.SYM_SHIFT, 256)
+    assert choose(Sch.CAUSAL, 512, 128, 1, 256) == (_lib.SYM_SHIFT, 0)  # N/2 = 256 fits exactly
+    for bad in [(Sch.FULL, 0, 128, 1, 256), (2, 8, 128, 1, 256), (Sch.FULL, 8, 128, 1, 0)]:
+        with pytest.raises(_lib.DashError) as ei:
+            choose(*bad)
+        assert ei.value.status == _lib.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("mask,N,g,groups,P", [(Sch.FULL, 512, 1, 2, 256), (Sch.CAUSAL, 1024, 1, 1, 256),
+                                               (Sch.CAUSAL, 7, 4, 3, 16), (Sch.FULL, 24, 2, 5, 8)])
+def test_adaptive_choice_builds_valid_schedules(mask, N, g, groups, P):
+    from scheduling_persistent_fa_amd.schedule import choose
+    kind, cap = choose(mask, N, 128, g, P)
+    s = Schedule(mask, kind, N, g, groups, P, max_gang=cap)
+    s.validate()
+    lists = Sch.build(mask, kind, N, g, groups, P, max_gang=cap)
+    assert sum(len(x) for x in lists) == s.num_steps
