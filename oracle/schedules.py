@@ -74,14 +74,22 @@ def _flagged(chain: list[tuple[int, int, int, int]]) -> list[Step]:
     return [Step(h, qi, kj, o, i == 0, i == n - 1) for i, (h, qi, kj, o) in enumerate(chain)]
 
 
-def gang_slot(gang: int, p: int, n_gangs: int, gang_size: int, xcd_local: bool) -> int:
-    """Workgroup index of member p of a gang.
+def gang_slot(gang: int, p: int, n_gangs: int, gang_size: int, xcd_local: bool,
+              P: int = 0, shift: bool = False) -> int:
+    """Workgroup index of member p of a gang (a placement choice: it does not
+    change what any workgroup computes, only which compute unit runs it).
 
-    With ``xcd_local`` members of one gang get indices congruent modulo the
-    number of gangs, which the round-robin dispatch of workgroups over the
-    chiplets keeps together when the gang count is a multiple of 8.
+    Workgroup w runs on chiplet w % 8.  With ``xcd_local``, shift gangs on a
+    grid that is a multiple of 128 put runs of 16 consecutive members on one
+    chiplet; otherwise members get indices congruent modulo the gang count.
+    Without it each gang takes a contiguous index range.
     """
-    return p * n_gangs + gang if xcd_local else gang * gang_size + p
+    if not xcd_local:
+        return gang * gang_size + p
+    if shift and P % 128 == 0:
+        m = gang * gang_size + p
+        return (m // 16) % 8 + 8 * ((m // 128) * 16 + m % 16)
+    return p * n_gangs + gang
 
 
 def build(mask: int, sched: int, N: int, g: int, groups: int, P: int, xcd_local: bool = True,
@@ -152,7 +160,7 @@ def build(mask: int, sched: int, N: int, g: int, groups: int, P: int, xcd_local:
             for o, (_, kj) in enumerate(sorted(lst)):
                 rank[(h, qi, kj)] = o
         for p, chains in enumerate(members):
-            w = gang_slot(gang, p, n_gangs, gang_size, xcd_local)
+            w = gang_slot(gang, p, n_gangs, gang_size, xcd_local, P, sched == SHIFT)
             for ch in chains:
                 out[w].extend(_flagged([(h, qi, kj, rank[(h, qi, kj)]) for (h, qi, kj) in ch]))
     return out

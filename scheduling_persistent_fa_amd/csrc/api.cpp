@@ -369,7 +369,7 @@ int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
     e = hipEventRecord((hipEvent_t)op.event_stop, strm);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord(stop)");
   }
-  e = dash::launch_dq_finalize(ws_dq, dq, rows * D, D, scale, strm);
+  e = dash::launch_dq_finalize(ws_dq, dq, rows * D, D, scale, atomic, strm);
   if (e != hipSuccess) return hip_fail(e, "finalize launch");
 
   if (op.sync_check) {

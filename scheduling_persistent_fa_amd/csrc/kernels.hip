@@ -80,6 +80,14 @@ __device__ __forceinline__ bf16x8 lds_tr8_at(const LDS char* p, int pitch_bytes)
   return cat8(lds_tr4(p), lds_tr4(p + 4 * pitch_bytes));
 }
 
+// Device-scope (sc1) 16-byte accesses to one dQ workspace tile of 4 KiB.
+// sc1 makes a load or store coherent across the chiplets: it bypasses the
+// chiplet-local caches that other chiplets cannot see.
+constexpr int kDeviceScope = 16;  // cache-policy operand of the buffer intrinsics: sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ws_rsrc(const float* tile) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(tile), (short)0, 4096, 0x00020000);
+}
+
 // Keeps a value opaque to the optimiser, so that addresses formed from it
 // fold their constant parts into instruction offsets instead of being
 // precomputed and held in registers.
@@ -291,8 +299,11 @@ __global__ __launch_bounds__(256) void delta_kernel(const __bf16* __restrict__ o
 // spread over the waves.
 //
 // Workspace dQ layout: per (query head, 64-row block) a 64 x D fp32 block
-// stored as 32 x 32 MFMA C tiles (tile = qb * D/32 + db), each tile as
-// [register][lane], so one wave access covers 256 contiguous bytes.
+// stored as 32 x 32 MFMA C tiles (tile = qb * D/32 + db).  The deterministic
+// schedules keep a tile as [register / 4][lane][register % 4], so one wave
+// access is a 16-byte-per-lane, 1 KiB contiguous transfer; the atomic variant
+// keeps [register][lane] (256 contiguous bytes per wave access), because
+// fp32 atomics are per element.
 //
 // Ordering protocol of the deterministic schedules.  The workspace and the
 // semaphores are only touched with device-scope relaxed atomic loads and
@@ -583,11 +594,16 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
 #pragma unroll
           for (int ti = 0; ti < TPW; ++ti) {
             const int t_idx = w + NW * ti;
-            float* p = ((EVEN || t_idx < NQT) ? p_ws : a.dummy) + t_idx * 1024 + lane;
+            const __amdgpu_buffer_rsrc_t rs = ws_rsrc(((EVEN || t_idx < NQT) ? p_ws : a.dummy) + t_idx * 1024);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const float sum = pdq[ti][r] + pprev[ti][r];
-              __hip_atomic_store(p + r * 64, p_add ? sum : pdq[ti][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int q4 = 0; q4 < 4; ++q4) {
+              f32x4 v4;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int r = 4 * q4 + e;
+                v4[e] = p_add ? pdq[ti][r] + pprev[ti][r] : pdq[ti][r];
+              }
+              __builtin_amdgcn_raw_buffer_store_b128(v4, rs, (q4 * 64 + lane) * 16, 0, kDeviceScope);
             }
           }
         }
@@ -694,10 +710,14 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
 #pragma unroll
           for (int ti = 0; ti < TPW; ++ti) {
             const int t_idx = w + NW * ti;
-            const float* p = wsb + (t_idx < NQT ? t_idx : t_idx % NQT) * 1024 + lane;
+            asm volatile("" ::: "memory");  // the reads stay after the wait above
+            const __amdgpu_buffer_rsrc_t rs = ws_rsrc(wsb + (t_idx < NQT ? t_idx : t_idx % NQT) * 1024);
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              pprev[ti][r] = __hip_atomic_load(p + r * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const f32x4 v4 = __builtin_amdgcn_raw_buffer_load_b128(rs, (q4 * 64 + lane) * 16, 0, kDeviceScope);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) pprev[ti][4 * q4 + e] = v4[e];
+            }
           }
         }
 #pragma unroll
@@ -728,10 +748,12 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
         const int t_idx = w + NW * ti;
         if (EVEN || t_idx < NQT) {
           if (p_add) pdq[ti] += pprev[ti];
-          float* p = p_ws + t_idx * 1024 + lane;
+          const __amdgpu_buffer_rsrc_t rs = ws_rsrc(p_ws + t_idx * 1024);
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            __hip_atomic_store(p + r * 64, pdq[ti][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 v4 = {pdq[ti][4 * q4], pdq[ti][4 * q4 + 1], pdq[ti][4 * q4 + 2], pdq[ti][4 * q4 + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(v4, rs, (q4 * 64 + lane) * 16, 0, kDeviceScope);
+          }
         }
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -746,7 +768,9 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
 
 // dQ = bf16(scale * workspace), undoing the fragment order.  One thread per
 // (block, tile, register group of four, lane): four rows of one column.
-template <int D>
+// Deterministic layout (X4): tile as [register / 4][lane][register % 4]; the
+// atomic layout: tile as [register][lane].
+template <int D, bool X4>
 __global__ __launch_bounds__(256) void dq_finalize_kernel(const float* __restrict__ ws, __bf16* __restrict__ dq,
                                                           long long n_groups, float scale) {
   const long long f = (long long)blockIdx.x * 256 + threadIdx.x;
@@ -756,12 +780,19 @@ __global__ __launch_bounds__(256) void dq_finalize_kernel(const float* __restric
   const int rem = (int)(f % GROUPS_PER_BLOCK);
   const int tile = rem / 256, j = (rem % 256) / 64, l = rem % 64;
   const int qb = tile / (D / 32), db = tile % (D / 32);
-  const float* src = ws + (size_t)blk * 64 * D + tile * 1024 + (4 * j) * 64 + l;
   const int col = db * 32 + (l & 31);
   const int row0 = qb * 32 + 8 * j + 4 * (l >> 5);
   __bf16* out = dq + (size_t)blk * 64 * D;
+  f32x4 v;
+  if constexpr (X4) {
+    v = *(const f32x4*)(ws + (size_t)blk * 64 * D + tile * 1024 + j * 256 + l * 4);
+  } else {
+    const float* src = ws + (size_t)blk * 64 * D + tile * 1024 + (4 * j) * 64 + l;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) out[(size_t)(row0 + e) * D + col] = (__bf16)(src[e * 64] * scale);
+    for (int e = 0; e < 4; ++e) v[e] = src[e * 64];
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) out[(size_t)(row0 + e) * D + col] = (__bf16)(v[e] * scale);
 }
 
 }  // namespace
@@ -861,11 +892,19 @@ hipError_t bwd_kernel_fits(int D, int T, bool atomic, int num_cu, int P, bool* f
   return hipSuccess;
 }
 
-hipError_t launch_dq_finalize(const float* ws, void* dq, long long elems, int D, float scale, hipStream_t st) {
+hipError_t launch_dq_finalize(const float* ws, void* dq, long long elems, int D, float scale, bool atomic_layout,
+                              hipStream_t st) {
   const long long n_f4 = elems / 4;
   const unsigned blocks = (unsigned)((n_f4 + 255) / 256);
-  if (D == 128) hipLaunchKernelGGL((dq_finalize_kernel<128>), dim3(blocks), dim3(256), 0, st, ws, (__bf16*)dq, n_f4, scale);
-  else hipLaunchKernelGGL((dq_finalize_kernel<64>), dim3(blocks), dim3(256), 0, st, ws, (__bf16*)dq, n_f4, scale);
+#define DASH_FIN(D_, X4_) hipLaunchKernelGGL((dq_finalize_kernel<D_, X4_>), dim3(blocks), dim3(256), 0, st, ws, (__bf16*)dq, n_f4, scale)
+  if (D == 128) {
+    if (atomic_layout) DASH_FIN(128, false);
+    else DASH_FIN(128, true);
+  } else {
+    if (atomic_layout) DASH_FIN(64, false);
+    else DASH_FIN(64, true);
+  }
+#undef DASH_FIN
   return hipGetLastError();
 }
 

@@ -35,6 +35,7 @@ hipError_t launch_delta(const void* o, const void* dO, float* delta, long long r
                         long long n_zero_i32, float* zero_f32, long long n_zero_f32, hipStream_t st);
 hipError_t launch_bwd(const BwdLaunch& L, hipStream_t st);
 hipError_t bwd_kernel_fits(int D, int T, bool atomic, int num_cu, int P, bool* fits);
-hipError_t launch_dq_finalize(const float* ws, void* dq, long long elems, int D, float scale, hipStream_t st);
+hipError_t launch_dq_finalize(const float* ws, void* dq, long long elems, int D, float scale, bool atomic_layout,
+                              hipStream_t st);
 
 }  // namespace dash
