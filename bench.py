@@ -27,9 +27,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "bwd_kernel_counters.json")
 
 
-def flops(B, Hq, S, D, causal):
-    f = 10.0 * B * Hq * S * S * D
-    return f / 2 if causal else f
+def flops(B, Hq, S, D, causal, Sk=None):
+    """Nominal backward FLOPs: 10 * B * Hq * D per visible (query, key) pair,
+    counting S * Sk pairs, minus S^2 / 2 under the causal mask (which for
+    Sk = S is the usual halving)."""
+    Sk = S if Sk is None else Sk
+    pairs = S * Sk - (S * S / 2 if causal else 0)
+    return 10.0 * B * Hq * D * pairs
 
 
 def cpu_baseline(wl, min_seconds=10.0, max_heads=8):
@@ -44,18 +48,19 @@ def cpu_baseline(wl, min_seconds=10.0, max_heads=8):
     except Exception:  # pragma: no cover - threadpoolctl missing
         cores = int(os.environ.get("OMP_NUM_THREADS", "1"))
     S, D, causal = wl["S"], wl["D"], wl["causal"]
+    Sk = wl.get("Sk", S)
     f64 = lambda x: bf16_bits_to_f32(x).astype(np.float64)
     heads, dt = 0, 0.0
     while heads < max_heads and (heads == 0 or dt < min_seconds):
-        inp = make_inputs(1, 1, 1, S, D, seed=heads, std=wl["std"])
+        inp = make_inputs(1, 1, 1, S, D, seed=heads, std=wl["std"], Sk=Sk)
         q, k, v, do = (f64(x) for x in (inp.q, inp.k, inp.v, inp.do))
         t0 = time.perf_counter()
         A.backward(q, k, v, do, 1.0 / math.sqrt(D), causal)
         dt += time.perf_counter() - t0
         heads += 1
-    return {"value": heads * flops(1, 1, S, D, causal) / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
+    return {"value": heads * flops(1, 1, S, D, causal, Sk) / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"{heads} (batch, head) slices of the workload (S={S} D={D} "
+            "sample": f"{heads} (batch, head) slices of the workload (S={S} Sk={Sk} D={D} "
                       f"{'causal' if causal else 'full'}), float64 forward+backward, {dt:.1f} s"}
 
 
@@ -98,22 +103,27 @@ def main():
 
     wl = dict(WORKLOADS[args.workload])
     B, Hq, Hkv, S, D, causal, tile = wl["B"], wl["Hq"], wl["Hkv"], wl["S"], wl["D"], wl["causal"], wl["tile"]
+    Sk = wl.get("Sk", S)
     torch.cuda.set_device(0)
     info = device_info(0)
-    inp = make_inputs(B, Hq, Hkv, S, D, seed=0, std=wl["std"])
+    inp = make_inputs(B, Hq, Hkv, S, D, seed=0, std=wl["std"], Sk=Sk)
     q, k, v, do = (bf16_from_bits(getattr(inp, n)) for n in ("q", "k", "v", "do"))
     o, lse = attn_fwd(q, k, v, causal)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     torch.cuda.synchronize()
-    fl = flops(B, Hq, S, D, causal)
+    fl = flops(B, Hq, S, D, causal, Sk)
 
-    det_names = ["serial", "desc_q"] + (["sym_shift"] if causal else ["shift"])
+    square = Sk == S
+    # Symmetric shift pairs query tile p with N-1-p and needs a square grid;
+    # shift needs a full mask, so a causal rectangle has only the list walks.
+    fast = ["shift"] if not causal else (["sym_shift"] if square else [])
+    det_names = ["serial", "desc_q"] + fast
     if args.schedules:
         det_names = [s for s in args.schedules.split(",") if s]
     ids = {"serial": _lib.SERIAL, "desc_q": _lib.DESC_Q, "shift": _lib.SHIFT, "sym_shift": _lib.SYM_SHIFT}
     runs = [(n, ids[n], -1) for n in det_names]
     if not args.no_atomic:
-        walks = ["serial", "desc_q"] + (["sym_shift"] if causal else ["shift"])
+        walks = ["serial", "desc_q"] + fast
         runs += [(f"atomic[{w}]", _lib.ATOMIC, ids[w]) for w in walks]
 
     stream = torch.cuda.current_stream()
@@ -202,7 +212,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "B": B, "Hq": Hq, "Hkv": Hkv, "S": S, "D": D,
+        "config": {"workload": args.workload, "B": B, "Hq": Hq, "Hkv": Hkv, "S": S, "Sk": Sk, "D": D,
                    "mask": "causal" if causal else "full", "tile": tile, "schedule": best,
                    "workgroups": info["num_cu"]},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),

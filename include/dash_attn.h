@@ -107,6 +107,17 @@ int dash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
                   void* stream);
 
 /*
+ * Forward pass with Sq query rows and Sk key/value rows: Q, O bfloat16
+ * [B,Hq,Sq,D], K, V bfloat16 [B,Hkv,Sk,D], lse float32 [B,Hq,Sq].  The causal
+ * mask is aligned at the bottom right (query row i sees keys 0 .. i + Sk - Sq)
+ * and needs Sk >= Sq (DASH_ERR_INVALID_ARG otherwise).  Sq and Sk are multiples
+ * of 64.  dash_attn_fwd is the case Sq = Sk = S.
+ */
+int dash_attn_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int Hq, int Hkv, int Sq, int Sk, int D, float softmax_scale, int mask,
+                     void* stream);
+
+/*
  * Backward pass: dQ, dK, dV (bfloat16) from Q, K, V, O, dO (bfloat16) and
  * lse (float32).  schedule is a dash_schedule_kind; DASH_SCHED_AUTO runs
  * the one dash_schedule_choose picks (with its gang cap unless opts sets
@@ -121,6 +132,19 @@ int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
                   const float* lse, void* dq, void* dk, void* dv,
                   int B, int Hq, int Hkv, int S, int D, float softmax_scale, int mask,
                   int schedule, const dash_bwd_opts* opts, void* stream);
+
+/*
+ * Backward pass with Sq query rows and Sk key/value rows (shapes and mask as
+ * in dash_attn_fwd_qk; dQ like Q, dK/dV like K).  Sq and Sk are multiples of
+ * the tile.  Schedules over the Nq x Nk tile grid: SERIAL and DESC_Q walk the
+ * query tiles that see each key/value tile; SHIFT (full mask) runs a gang of
+ * Nk workgroups, member p visiting query tiles (p + t) mod Nq; SYM_SHIFT needs
+ * Sq = Sk.  The workspace is sized with S = Sq.
+ */
+int dash_attn_bwd_qk(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                     const float* lse, void* dq, void* dk, void* dv,
+                     int B, int Hq, int Hkv, int Sq, int Sk, int D, float softmax_scale, int mask,
+                     int schedule, const dash_bwd_opts* opts, void* stream);
 
 /* Bytes of device workspace dash_attn_bwd needs for these sizes (fp32 dQ
  * accumulator, Delta, semaphores, error word).  Returns DASH_OK or an error. */
@@ -144,6 +168,11 @@ typedef struct dash_schedule dash_schedule;
  * receives a schedule to free with dash_schedule_free. */
 int dash_schedule_build(int mask, int schedule, int N, int g, int groups, int P, int xcd_local,
                         int atomic_walk, int max_gang, dash_schedule** out);
+
+/* Same for Nq query tiles and Nk key/value tiles (causal: Nk >= Nq, aligned
+ * at the bottom right; symmetric shift: Nq = Nk). */
+int dash_schedule_build_qk(int mask, int schedule, int Nq, int Nk, int g, int groups, int P, int xcd_local,
+                           int atomic_walk, int max_gang, dash_schedule** out);
 
 int dash_schedule_num_workgroups(const dash_schedule* s);
 long long dash_schedule_num_steps(const dash_schedule* s);
@@ -181,6 +210,10 @@ void dash_schedule_free(dash_schedule* s);
  * part of the key but do not change the choice on this hardware.
  * DASH_ERR_INVALID_ARG for non-positive sizes or an unknown mask. */
 int dash_schedule_choose(int mask, int N, int D, int g, int P, int* schedule, int* max_gang);
+
+/* Same for Nq query tiles and Nk key/value tiles: full mask -> SHIFT (gang of
+ * Nk, capped at P); causal -> SYM_SHIFT when Nq = Nk is even, else DESC_Q. */
+int dash_schedule_choose_qk(int mask, int Nq, int Nk, int D, int g, int P, int* schedule, int* max_gang);
 
 /* ---- misc -------------------------------------------------------------- */
 

@@ -8,7 +8,7 @@ definition.  [summary] §1 and §2.1 fix what the backward pass produces (the
 gradients, with dQ accumulated over KV tiles); the formulas below are the
 textbook chain rule for
 
-    S = scale * Q K^T            (causal: S_ij = -inf for j > i)
+    S = scale * Q K^T            (causal: S_ij = -inf for j > i + Sk - Sq)
     P = softmax_rows(S),  LSE_i = log sum_j exp(S_ij)
     O = P V
 
@@ -19,6 +19,12 @@ given dO:
     Delta_i = sum_d dO_id O_id           (= sum_j P_ij dP_ij)
     dS = P * (dP - Delta[:, None])
     dQ = scale * dS K,   dK = scale * dS^T Q.
+
+Queries and keys may differ in length (Sq query rows, Sk key rows).  The
+causal mask is then aligned at the bottom right: query row i sees keys
+0 .. i + Sk - Sq, so the last query row sees every key (the usual convention
+for queries that continue a longer key sequence); with Sq = Sk it is the
+ordinary lower triangle.
 
 Grouped-query attention: query head hq reads key/value head hq // g with
 g = Hq / Hkv (contiguous groups); dK/dV of a key/value head sum over its g
@@ -33,14 +39,15 @@ import numpy as np
 
 
 def _scores(qrows: np.ndarray, k: np.ndarray, scale: float, row0: int, causal: bool,
-            bias: np.ndarray | None = None) -> np.ndarray:
+            bias: np.ndarray | None = None, offset: int = 0) -> np.ndarray:
+    """Scores of query rows row0.. against all keys; ``offset`` = Sk - Sq."""
     s = scale * (qrows @ k.T)
     if bias is not None:
         s = s + bias
     if causal:
         i = np.arange(row0, row0 + qrows.shape[0])[:, None]
         j = np.arange(k.shape[0])[None, :]
-        s = np.where(j > i, -np.inf, s)
+        s = np.where(j > i + offset, -np.inf, s)
     return s
 
 
@@ -60,6 +67,7 @@ def forward(q, k, v, scale: float, causal: bool, row_block: int = 1024, bias=Non
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
     B, Hq, S, D = q.shape
     g = Hq // k.shape[1]
+    off = k.shape[2] - S
     o = np.zeros_like(q)
     lse = np.zeros((B, Hq, S))
     for b in range(B):
@@ -68,7 +76,7 @@ def forward(q, k, v, scale: float, causal: bool, row_block: int = 1024, bias=Non
             for r0 in range(0, S, row_block):
                 r1 = min(S, r0 + row_block)
                 s = _scores(q[b, hq, r0:r1], k[b, hk], scale, r0, causal,
-                            None if bias is None else bias[r0:r1])
+                            None if bias is None else bias[r0:r1], off)
                 p, l_ = _softmax_rows(s)
                 o[b, hq, r0:r1] = p @ v[b, hk]
                 lse[b, hq, r0:r1] = l_
@@ -81,6 +89,7 @@ def backward(q, k, v, do, scale: float, causal: bool, row_block: int = 1024, bia
     B, Hq, S, D = q.shape
     Hkv = k.shape[1]
     g = Hq // Hkv
+    off = k.shape[2] - S
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
@@ -94,7 +103,7 @@ def backward(q, k, v, do, scale: float, causal: bool, row_block: int = 1024, bia
                 r1 = min(S, r0 + row_block)
                 qr, dor = q[b, hq, r0:r1], do[b, hq, r0:r1]
                 s = _scores(qr, k[b, hk], scale, r0, causal,
-                            None if bias is None else bias[r0:r1])
+                            None if bias is None else bias[r0:r1], off)
                 p, l_ = _softmax_rows(s)
                 orow = p @ v[b, hk]
                 dlt = (dor * orow).sum(axis=1)
@@ -118,11 +127,12 @@ def head_stats(q, k, v, do, b: int, hq: int, scale: float, causal: bool, row_blo
     g = q.shape[1] // k.shape[1]
     hk = hq // g
     S = q.shape[2]
+    off = k.shape[2] - S
     lse = np.zeros(S)
     delta = np.zeros(S)
     for r0 in range(0, S, row_block):
         r1 = min(S, r0 + row_block)
-        s = _scores(q[b, hq, r0:r1], k[b, hk], scale, r0, causal)
+        s = _scores(q[b, hq, r0:r1], k[b, hk], scale, r0, causal, None, off)
         p, l_ = _softmax_rows(s)
         lse[r0:r1] = l_
         delta[r0:r1] = (do[b, hq, r0:r1] * (p @ v[b, hk])).sum(axis=1)
@@ -134,9 +144,10 @@ def dq_rows(q, k, v, do, b: int, hq: int, rows, scale: float, causal: bool):
     q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
     g = q.shape[1] // k.shape[1]
     hk = hq // g
+    off = k.shape[2] - q.shape[2]
     out = []
     for i in rows:
-        s = _scores(q[b, hq, i:i + 1], k[b, hk], scale, i, causal)
+        s = _scores(q[b, hq, i:i + 1], k[b, hk], scale, i, causal, None, off)
         p, _ = _softmax_rows(s)
         o_i = p @ v[b, hk]
         dp = do[b, hq, i:i + 1] @ v[b, hk].T
@@ -154,6 +165,7 @@ def dkdv_rows(q, k, v, do, b: int, hk: int, cols, scale: float, causal: bool, st
     q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
     Hq, S = q.shape[1], q.shape[2]
     g = Hq // k.shape[1]
+    off = k.shape[2] - S
     dk_out, dv_out = [], []
     heads = list(range(hk * g, hk * g + g))
     if stats is None:
@@ -167,7 +179,7 @@ def dkdv_rows(q, k, v, do, b: int, hk: int, cols, scale: float, causal: bool, st
             s = scale * (q[b, hq] @ k[b, hk, j])
             p = np.exp(s - lse)
             if causal:
-                p = np.where(i >= j, p, 0.0)
+                p = np.where(i + off >= j, p, 0.0)
             dp = do[b, hq] @ v[b, hk, j]
             ds = p * (dp - delta)
             dvj += p @ do[b, hq]
@@ -178,9 +190,9 @@ def dkdv_rows(q, k, v, do, b: int, hk: int, cols, scale: float, causal: bool, st
 
 
 def head_matrices(q_head, k_head, v_head, do_head, scale: float, causal: bool):
-    """P, dP and dS of one head, float64 ([S, S] each); used by the row-identity tests."""
+    """P, dP and dS of one head, float64 ([Sq, Sk] each); used by the row-identity tests."""
     q_head, k_head, v_head, do_head = (np.asarray(x, dtype=np.float64) for x in (q_head, k_head, v_head, do_head))
-    s = _scores(q_head, k_head, scale, 0, causal)
+    s = _scores(q_head, k_head, scale, 0, causal, None, k_head.shape[0] - q_head.shape[0])
     p, _ = _softmax_rows(s)
     o = p @ v_head
     dp = do_head @ v_head.T

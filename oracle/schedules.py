@@ -58,9 +58,15 @@ class ScheduleError(ValueError):
     pass
 
 
-def kv_walk(mask: int, sched: int, N: int, kj: int) -> list[int]:
-    """Query tiles visited by key/value tile kj for the serial/descending walks."""
-    lo = kj if mask == CAUSAL else 0
+def kv_walk(mask: int, sched: int, N: int, kj: int, Nk: int | None = None) -> list[int]:
+    """Query tiles visited by key/value tile kj for the serial/descending walks.
+
+    N query tiles, Nk key/value tiles (default N).  Under the causal mask,
+    aligned at the bottom right, query tile qi sees key/value tiles
+    0 .. qi + Nk - N.
+    """
+    off = (N if Nk is None else Nk) - N
+    lo = max(0, kj - off) if mask == CAUSAL else 0
     tiles = list(range(lo, N))
     return tiles[::-1] if sched == DESC_Q else tiles
 
@@ -93,15 +99,24 @@ def gang_slot(gang: int, p: int, n_gangs: int, gang_size: int, xcd_local: bool,
 
 
 def build(mask: int, sched: int, N: int, g: int, groups: int, P: int, xcd_local: bool = True,
-          max_gang: int = 0) -> list[list[Step]]:
-    """Per-workgroup step lists for ``groups`` kv groups of g query heads, N tiles, P workgroups.
+          max_gang: int = 0, Nk: int | None = None) -> list[list[Step]]:
+    """Per-workgroup step lists for ``groups`` kv groups of g query heads, N query
+    tiles, Nk key/value tiles (default N), P workgroups.
+
+    With Nk != N the schedules generalise as follows: a serial or descending
+    chain of key/value tile kj walks the query tiles that see it; a shift gang
+    has Nk members and member p visits query tiles (p + t) mod N; symmetric
+    shift needs N == Nk.
 
     ``max_gang`` > 0 caps a gang schedule's gang below its natural size (N for
     shift, N/2 for symmetric shift); member p then takes the units (key/value
     tiles, or tile pairs) p, p + gang, p + 2*gang, ... one after another.
     """
-    if N < 1 or g < 1 or groups < 1 or P < 1:
+    Nk = N if Nk is None else Nk
+    if N < 1 or Nk < 1 or g < 1 or groups < 1 or P < 1:
         raise ScheduleError("sizes must be positive")
+    if mask == CAUSAL and Nk < N:
+        raise ScheduleError("a causal mask needs at least as many key/value tiles as query tiles")
     out: list[list[Step]] = [[] for _ in range(P)]
     if sched in (SERIAL, DESC_Q):
         # Chains in (group, kj) order go to the least-loaded workgroup (unit
@@ -109,8 +124,8 @@ def build(mask: int, sched: int, N: int, g: int, groups: int, P: int, xcd_local:
         # in-order dispatch of the baseline's one-block-per-KV-tile launch.
         load = [0] * P
         for grp in range(groups):
-            for kj in range(N):
-                walk = kv_walk(mask, sched, N, kj)
+            for kj in range(Nk):
+                walk = kv_walk(mask, sched, N, kj, Nk)
                 w = min(range(P), key=lambda x: (load[x], x))
                 # ordinal = kj: every dQ tile accumulates key/value tiles in ascending order
                 out[w].extend(_flagged([(h, qi, k, k) for (h, qi, k) in _chain(grp, g, kj, walk)]))
@@ -119,12 +134,14 @@ def build(mask: int, sched: int, N: int, g: int, groups: int, P: int, xcd_local:
     if sched == SHIFT:
         if mask != FULL:
             raise ScheduleError("shift scheduling needs a full mask")
-        units = N
+        units = Nk
     elif sched == SYM_SHIFT:
         if mask != CAUSAL:
             raise ScheduleError("symmetric shift needs a causal mask")
         if N % 2:
             raise ScheduleError("symmetric shift needs an even tile count")
+        if Nk != N:
+            raise ScheduleError("symmetric shift needs as many key/value tiles as query tiles")
         units = N // 2
     else:
         raise ScheduleError(f"unknown schedule {sched}")
@@ -166,26 +183,29 @@ def build(mask: int, sched: int, N: int, g: int, groups: int, P: int, xcd_local:
     return out
 
 
-def contributors(mask: int, N: int, qi: int) -> int:
-    """Number of key/value tiles that add into dQ tile qi."""
-    return qi + 1 if mask == CAUSAL else N
+def contributors(mask: int, N: int, qi: int, Nk: int | None = None) -> int:
+    """Number of key/value tiles that add into dQ tile qi (N query tiles, Nk
+    key/value tiles, causal aligned at the bottom right)."""
+    Nk = N if Nk is None else Nk
+    return qi + Nk - N + 1 if mask == CAUSAL else Nk
 
 
-def validate(lists: list[list[Step]], mask: int, N: int, g: int, groups: int) -> None:
+def validate(lists: list[list[Step]], mask: int, N: int, g: int, groups: int, Nk: int | None = None) -> None:
     """Raise ScheduleError unless the lists are a complete, contiguous, well-ordered, deadlock-free schedule."""
+    Nk = N if Nk is None else Nk
     heads = g * groups
     seen = set()
     for lst in lists:
         for s in lst:
-            if not (0 <= s.head < heads and 0 <= s.qi < N and 0 <= s.kj < N):
+            if not (0 <= s.head < heads and 0 <= s.qi < N and 0 <= s.kj < Nk):
                 raise ScheduleError(f"index out of range: {s}")
-            if mask == CAUSAL and s.kj > s.qi:
+            if mask == CAUSAL and s.kj > s.qi + Nk - N:
                 raise ScheduleError(f"masked tile scheduled: {s}")
             key = (s.head, s.qi, s.kj)
             if key in seen:
                 raise ScheduleError(f"tile pair scheduled twice: {key}")
             seen.add(key)
-    expect = sum(contributors(mask, N, qi) for qi in range(N)) * heads
+    expect = sum(contributors(mask, N, qi, Nk) for qi in range(N)) * heads
     if len(seen) != expect:
         raise ScheduleError(f"coverage {len(seen)} != {expect}")
     # chain contiguity: each (group, kj) appears as exactly one run, flagged first..last
@@ -209,7 +229,7 @@ def validate(lists: list[list[Step]], mask: int, N: int, g: int, groups: int) ->
                 run = None
         if lst and not lst[-1].last:
             raise ScheduleError("list ends inside a chain")
-    if len(chain_owner) != groups * N:
+    if len(chain_owner) != groups * Nk:
         raise ScheduleError("chain count mismatch")
     # ordinals: a permutation of 0..count-1 per dQ tile
     ords: dict[tuple[int, int], list[int]] = {}
@@ -217,7 +237,7 @@ def validate(lists: list[list[Step]], mask: int, N: int, g: int, groups: int) ->
         for s in lst:
             ords.setdefault((s.head, s.qi), []).append(s.ord)
     for (h, qi), o in ords.items():
-        if sorted(o) != list(range(contributors(mask, N, qi))):
+        if sorted(o) != list(range(contributors(mask, N, qi, Nk))):
             raise ScheduleError(f"ordinals of dQ tile {(h, qi)} are {sorted(o)}")
     simulate(lists, 1.0, 1.0)  # raises on deadlock
 

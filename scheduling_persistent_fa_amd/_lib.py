@@ -31,9 +31,10 @@ ORD_MASK = FIRST_FLAG - 1
 
 # Every symbol include/dash_attn.h declares.
 EXPORTS = (
-    "dash_attn_fwd", "dash_attn_bwd", "dash_attn_bwd_workspace_bytes", "dash_attn_bwd_delta",
-    "dash_schedule_build", "dash_schedule_num_workgroups", "dash_schedule_num_steps", "dash_schedule_export",
+    "dash_attn_fwd", "dash_attn_fwd_qk", "dash_attn_bwd", "dash_attn_bwd_qk", "dash_attn_bwd_workspace_bytes",
+    "dash_attn_bwd_delta", "dash_schedule_build", "dash_schedule_build_qk", "dash_schedule_num_workgroups", "dash_schedule_num_steps", "dash_schedule_export",
     "dash_schedule_validate", "dash_schedule_simulate", "dash_schedule_free", "dash_schedule_choose",
+    "dash_schedule_choose_qk",
     "dash_status_string",
     "dash_last_error", "dash_device_info",
 )
@@ -70,10 +71,13 @@ _lib = None
 def _declare(lib):
     vp, i, f, i32p = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.POINTER(ctypes.c_int32)
     lib.dash_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.dash_attn_fwd_qk.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
     lib.dash_attn_bwd.argtypes = [vp] * 9 + [i, i, i, i, i, f, i, i, ctypes.POINTER(BwdOpts), vp]
+    lib.dash_attn_bwd_qk.argtypes = [vp] * 9 + [i, i, i, i, i, i, f, i, i, ctypes.POINTER(BwdOpts), vp]
     lib.dash_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, ctypes.POINTER(ctypes.c_size_t)]
     lib.dash_attn_bwd_delta.argtypes = [vp, vp, vp, i, i, i, i, vp]
     lib.dash_schedule_build.argtypes = [i, i, i, i, i, i, i, i, i, ctypes.POINTER(vp)]
+    lib.dash_schedule_build_qk.argtypes = [i, i, i, i, i, i, i, i, i, i, ctypes.POINTER(vp)]
     lib.dash_schedule_num_workgroups.argtypes = [vp]
     lib.dash_schedule_num_steps.argtypes = [vp]
     lib.dash_schedule_num_steps.restype = ctypes.c_longlong
@@ -84,6 +88,7 @@ def _declare(lib):
     lib.dash_schedule_free.argtypes = [vp]
     lib.dash_schedule_free.restype = None
     lib.dash_schedule_choose.argtypes = [i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
+    lib.dash_schedule_choose_qk.argtypes = [i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
     lib.dash_status_string.argtypes = [i]
     lib.dash_status_string.restype = ctypes.c_char_p
     lib.dash_last_error.argtypes = []

@@ -29,18 +29,21 @@ def _check_bhsd(name, t, shape):
 
 
 def attn_fwd(q, k, v, causal: bool, scale: float = 0.0, out=None, lse=None, stream=None):
-    """O [B,Hq,S,D] bf16 and LSE [B,Hq,S] fp32 from the library's forward kernel."""
-    B, Hq, S, D = q.shape
-    Hkv = k.shape[1]
-    _check_bhsd("q", q, (B, Hq, S, D))
-    _check_bhsd("k", k, (B, Hkv, S, D))
-    _check_bhsd("v", v, (B, Hkv, S, D))
+    """O [B,Hq,Sq,D] bf16 and LSE [B,Hq,Sq] fp32 from the library's forward kernel.
+
+    K and V are [B,Hkv,Sk,D]; with Sq != Sk the causal mask is aligned at the
+    bottom right (query row i sees keys 0 .. i + Sk - Sq)."""
+    B, Hq, Sq, D = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    _check_bhsd("q", q, (B, Hq, Sq, D))
+    _check_bhsd("k", k, (B, Hkv, Sk, D))
+    _check_bhsd("v", v, (B, Hkv, Sk, D))
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
-        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
-    _lib.check(_lib.lib().dash_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, S, D,
-                                        float(scale), MASK_CAUSAL if causal else MASK_FULL, _stream(stream)))
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    _lib.check(_lib.lib().dash_attn_fwd_qk(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Sk, D,
+                                           float(scale), MASK_CAUSAL if causal else MASK_FULL, _stream(stream)))
     return out, lse
 
 
@@ -70,21 +73,22 @@ def make_opts(num_workgroups: int = 0, tile: int = 0, atomic_walk: int = -1, xcd
 
 def attn_bwd(q, k, v, o, do, lse, causal: bool, schedule: int, scale: float = 0.0, dq=None, dk=None, dv=None,
              opts: _lib.BwdOpts | None = None, stream=None):
-    """dQ, dK, dV (bf16) from the library's persistent backward kernel."""
-    B, Hq, S, D = q.shape
-    Hkv = k.shape[1]
-    for name, t, shp in (("q", q, (B, Hq, S, D)), ("k", k, (B, Hkv, S, D)), ("v", v, (B, Hkv, S, D)),
-                         ("o", o, (B, Hq, S, D)), ("do", do, (B, Hq, S, D))):
+    """dQ, dK, dV (bf16) from the library's persistent backward kernel (Sq query
+    rows from q, Sk key/value rows from k)."""
+    B, Hq, Sq, D = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    for name, t, shp in (("q", q, (B, Hq, Sq, D)), ("k", k, (B, Hkv, Sk, D)), ("v", v, (B, Hkv, Sk, D)),
+                         ("o", o, (B, Hq, Sq, D)), ("do", do, (B, Hq, Sq, D))):
         _check_bhsd(name, t, shp)
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, S) or not lse.is_contiguous():
-        raise ValueError("lse: expected contiguous float32 [B,Hq,S]")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Sq) or not lse.is_contiguous():
+        raise ValueError("lse: expected contiguous float32 [B,Hq,Sq]")
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     op = ctypes.byref(opts) if opts is not None else None
-    _lib.check(_lib.lib().dash_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
-                                        _ptr(dv), B, Hq, Hkv, S, D, float(scale),
-                                        MASK_CAUSAL if causal else MASK_FULL, schedule, op, _stream(stream)))
+    _lib.check(_lib.lib().dash_attn_bwd_qk(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                                           _ptr(dk), _ptr(dv), B, Hq, Hkv, Sq, Sk, D, float(scale),
+                                           MASK_CAUSAL if causal else MASK_FULL, schedule, op, _stream(stream)))
     return dq, dk, dv
 
 

@@ -67,7 +67,7 @@ struct DevSchedule {
   int32_t* offsets = nullptr;
   long long num_steps = 0;
 };
-using SchedKey = std::tuple<int, int, int, int, int, int, int, int, int, int>;  // dev, mask, kind, N, g, groups, P, xcd, walk, cap
+using SchedKey = std::tuple<int, int, int, int, int, int, int, int, int, int, int>;  // dev, mask, kind, Nq, Nk, g, groups, P, xcd, walk, cap
 std::map<SchedKey, DevSchedule> g_sched;
 
 struct Workspace {
@@ -103,17 +103,19 @@ WsLayout ws_layout(int B, int Hq, int S, int D) {
   return L;
 }
 
-int check_common(const void* const* ptrs, int nptr, int B, int Hq, int Hkv, int S, int D, int mask) {
+int check_common(const void* const* ptrs, int nptr, int B, int Hq, int Hkv, int Sq, int Sk, int D, int mask) {
   for (int i = 0; i < nptr; ++i) {
     if (!ptrs[i]) return fail(DASH_ERR_INVALID_ARG, "null tensor pointer (argument " + std::to_string(i) + ")");
     if (reinterpret_cast<uintptr_t>(ptrs[i]) % 16) return fail(DASH_ERR_INVALID_ARG, "tensor pointer not 16-byte aligned");
   }
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || D <= 0) return fail(DASH_ERR_INVALID_ARG, "sizes must be positive");
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Sk <= 0 || D <= 0) return fail(DASH_ERR_INVALID_ARG, "sizes must be positive");
   if (Hq % Hkv) return fail(DASH_ERR_INVALID_ARG, "Hq must be a multiple of Hkv");
   if (mask != DASH_MASK_FULL && mask != DASH_MASK_CAUSAL) return fail(DASH_ERR_INVALID_ARG, "unknown mask");
+  if (mask == DASH_MASK_CAUSAL && Sk < Sq)
+    return fail(DASH_ERR_INVALID_ARG, "a causal mask needs Sk >= Sq (it is aligned at the bottom right)");
   if (D != 64 && D != 128) return fail(DASH_ERR_UNSUPPORTED, "head dimension must be 64 or 128");
-  if (S % 64) return fail(DASH_ERR_UNSUPPORTED, "sequence length must be a multiple of 64");
-  if ((long long)B * Hq * S * D >= (1LL << 40)) return fail(DASH_ERR_UNSUPPORTED, "problem too large");
+  if (Sq % 64 || Sk % 64) return fail(DASH_ERR_UNSUPPORTED, "sequence lengths must be multiples of 64");
+  if ((long long)B * Hq * std::max(Sq, Sk) * D >= (1LL << 40)) return fail(DASH_ERR_UNSUPPORTED, "problem too large");
   return DASH_OK;
 }
 
@@ -150,13 +152,19 @@ int dash_device_info(int device, int* num_cu, int* lds_bytes, int* clock_khz) {
 
 int dash_schedule_build(int mask, int schedule, int N, int g, int groups, int P, int xcd_local, int atomic_walk,
                         int max_gang, dash_schedule** out) {
+  return dash_schedule_build_qk(mask, schedule, N, N, g, groups, P, xcd_local, atomic_walk, max_gang, out);
+}
+
+int dash_schedule_build_qk(int mask, int schedule, int Nq, int Nk, int g, int groups, int P, int xcd_local,
+                           int atomic_walk, int max_gang, dash_schedule** out) {
   if (!out) return fail(DASH_ERR_INVALID_ARG, "null output");
   *out = nullptr;
   auto s = std::make_unique<dash_schedule>();
   if (max_gang < 0) return fail(DASH_ERR_INVALID_ARG, "negative gang cap");
-  std::string err = dash::build_schedule(mask, schedule, N, g, groups, P, xcd_local != 0, atomic_walk, max_gang, &s->s);
+  std::string err = dash::build_schedule(mask, schedule, Nq, Nk, g, groups, P, xcd_local != 0, atomic_walk, max_gang, &s->s);
   if (!err.empty()) {
-    const bool bad = (N < 1 || g < 1 || groups < 1 || P < 1 || (mask != 0 && mask != 1) || schedule < 0 || schedule > 4);
+    const bool bad = (Nq < 1 || Nk < 1 || g < 1 || groups < 1 || P < 1 || (mask != 0 && mask != 1) || schedule < 0 ||
+                      schedule > 4 || (mask == 1 && Nk < Nq));
     return fail(bad ? DASH_ERR_INVALID_ARG : DASH_ERR_UNSUPPORTED, err);
   }
   *out = s.release();
@@ -187,21 +195,30 @@ int dash_schedule_simulate(const dash_schedule* s, double c, double r, double* m
 
 void dash_schedule_free(dash_schedule* s) { delete s; }
 
-int dash_schedule_choose(int mask, int N, int D, int g, int P, int* schedule, int* max_gang) {
+int dash_schedule_choose_qk(int mask, int Nq, int Nk, int D, int g, int P, int* schedule, int* max_gang) {
   if (!schedule || !max_gang) return fail(DASH_ERR_INVALID_ARG, "null output");
-  std::string err = dash::choose_schedule(mask, N, D, g, P, schedule, max_gang);
+  std::string err = dash::choose_schedule(mask, Nq, Nk, D, g, P, schedule, max_gang);
   return err.empty() ? DASH_OK : fail(DASH_ERR_INVALID_ARG, err);
+}
+
+int dash_schedule_choose(int mask, int N, int D, int g, int P, int* schedule, int* max_gang) {
+  return dash_schedule_choose_qk(mask, N, N, D, g, P, schedule, max_gang);
+}
+
+int dash_attn_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                     int Sq, int Sk, int D, float softmax_scale, int mask, void* stream) {
+  const void* ptrs[] = {q, k, v, o, lse};
+  int st = check_common(ptrs, 5, B, Hq, Hkv, Sq, Sk, D, mask);
+  if (st) return st;
+  if ((long long)B * Hq > 65535) return fail(DASH_ERR_UNSUPPORTED, "B*Hq exceeds the grid limit");
+  hipError_t e = dash::launch_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, default_scale(softmax_scale, D), mask,
+                                  (hipStream_t)stream);
+  return e == hipSuccess ? DASH_OK : hip_fail(e, "forward launch");
 }
 
 int dash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int S,
                   int D, float softmax_scale, int mask, void* stream) {
-  const void* ptrs[] = {q, k, v, o, lse};
-  int st = check_common(ptrs, 5, B, Hq, Hkv, S, D, mask);
-  if (st) return st;
-  if ((long long)B * Hq > 65535) return fail(DASH_ERR_UNSUPPORTED, "B*Hq exceeds the grid limit");
-  hipError_t e = dash::launch_fwd(q, k, v, o, lse, B, Hq, Hkv, S, D, default_scale(softmax_scale, D), mask,
-                                  (hipStream_t)stream);
-  return e == hipSuccess ? DASH_OK : hip_fail(e, "forward launch");
+  return dash_attn_fwd_qk(q, k, v, o, lse, B, Hq, Hkv, S, S, D, softmax_scale, mask, stream);
 }
 
 int dash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D, size_t* bytes) {
@@ -213,7 +230,7 @@ int dash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D, size_t* 
 
 int dash_attn_bwd_delta(const void* o, const void* dO, float* delta, int B, int H, int S, int D, void* stream) {
   const void* ptrs[] = {o, dO, delta};
-  int st = check_common(ptrs, 3, B, H, H, S, D, DASH_MASK_FULL);
+  int st = check_common(ptrs, 3, B, H, H, S, S, D, DASH_MASK_FULL);
   if (st) return st;
   hipError_t e = dash::launch_delta(o, dO, delta, (long long)B * H * S, D, nullptr, 0, nullptr, 0, (hipStream_t)stream);
   return e == hipSuccess ? DASH_OK : hip_fail(e, "delta launch");
@@ -222,8 +239,15 @@ int dash_attn_bwd_delta(const void* o, const void* dO, float* delta, int B, int 
 int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
                   void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int S, int D, float softmax_scale, int mask,
                   int schedule, const dash_bwd_opts* opts, void* stream) {
+  return dash_attn_bwd_qk(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, S, S, D, softmax_scale, mask, schedule, opts,
+                          stream);
+}
+
+int dash_attn_bwd_qk(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                     void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk, int D, float softmax_scale,
+                     int mask, int schedule, const dash_bwd_opts* opts, void* stream) {
   const void* ptrs[] = {q, k, v, o, dO, lse, dq, dk, dv};
-  int st = check_common(ptrs, 9, B, Hq, Hkv, S, D, mask);
+  int st = check_common(ptrs, 9, B, Hq, Hkv, Sq, Sk, D, mask);
   if (st) return st;
   if (schedule < DASH_SCHED_SERIAL || schedule > DASH_SCHED_AUTO) return fail(DASH_ERR_INVALID_ARG, "unknown schedule");
   dash_bwd_opts op;
@@ -241,17 +265,17 @@ int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
   st = device_info(dev, &di);
   if (st) return st;
 
-  const int T = op.tile ? op.tile : (S < 512 ? 64 : 128);
+  const int T = op.tile ? op.tile : (std::min(Sq, Sk) < 512 ? 64 : 128);
   if (T != 64 && T != 128) return fail(DASH_ERR_UNSUPPORTED, "tile must be 64 or 128");
-  if (S % T) return fail(DASH_ERR_UNSUPPORTED, "sequence length must be a multiple of the tile");
-  const int N = S / T;
+  if (Sq % T || Sk % T) return fail(DASH_ERR_UNSUPPORTED, "sequence lengths must be multiples of the tile");
+  const int Nq = Sq / T, Nk = Sk / T;
   const int P = op.num_workgroups > 0 ? op.num_workgroups : di.num_cu;
   if (op.num_workgroups < 0) return fail(DASH_ERR_INVALID_ARG, "negative workgroup count");
   if (op.max_gang < 0) return fail(DASH_ERR_INVALID_ARG, "negative gang cap");
   const int g = Hq / Hkv;
   if (schedule == DASH_SCHED_AUTO) {
     int cap = 0;
-    std::string err = dash::choose_schedule(mask, N, D, g, P, &schedule, &cap);
+    std::string err = dash::choose_schedule(mask, Nq, Nk, D, g, P, &schedule, &cap);
     if (!err.empty()) return fail(DASH_ERR_INVALID_ARG, err);
     if (op.max_gang == 0) op.max_gang = cap;
   }
@@ -273,11 +297,11 @@ int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
   DevSchedule ds;
   {
     std::lock_guard<std::mutex> lk(g_mu);
-    SchedKey key{dev, mask, schedule, N, g, groups, P, xcd, atomic ? (walk < 0 ? -1 : walk) : -1, op.max_gang};
+    SchedKey key{dev, mask, schedule, Nq, Nk, g, groups, P, xcd, atomic ? (walk < 0 ? -1 : walk) : -1, op.max_gang};
     auto it = g_sched.find(key);
     if (it == g_sched.end()) {
       dash::Schedule s;
-      std::string err = dash::build_schedule(mask, schedule, N, g, groups, P, xcd != 0, walk, op.max_gang, &s);
+      std::string err = dash::build_schedule(mask, schedule, Nq, Nk, g, groups, P, xcd != 0, walk, op.max_gang, &s);
       if (!err.empty()) return fail(DASH_ERR_UNSUPPORTED, err);
       err = dash::validate_schedule(s);
       if (!err.empty()) return fail(DASH_ERR_INVALID_SCHEDULE, err);
@@ -297,7 +321,7 @@ int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
   }
 
   // Workspace.
-  const WsLayout L = ws_layout(B, Hq, S, D);
+  const WsLayout L = ws_layout(B, Hq, Sq, D);
   char* ws = nullptr;
   if (op.workspace) {
     if (reinterpret_cast<uintptr_t>(op.workspace) % 256) return fail(DASH_ERR_WORKSPACE, "workspace not 256-byte aligned");
@@ -325,7 +349,7 @@ int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
   float* delta = (float*)(ws + L.delta);
   int* sem = (int*)(ws + L.sem);
   int* err = (int*)(ws + L.err);
-  const long long rows = (long long)B * Hq * S;
+  const long long rows = (long long)B * Hq * Sq;
   const long long n_sem = (long long)((L.err - L.sem) / 4) + 4;  // semaphores, padding and the error word
 
   e = dash::launch_delta(o, dO, delta, rows, D, sem, n_sem, atomic ? ws_dq : nullptr, atomic ? rows * D : 0, strm);
@@ -352,7 +376,8 @@ int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
   bl.spin_ticks = (long long)((double)budget_cycles * 1e5 / std::max(1, di.clock_khz));
   if (bl.spin_ticks < 1) bl.spin_ticks = 1;
   bl.scale = scale;
-  bl.S = S;
+  bl.Sq = Sq;
+  bl.Sk = Sk;
   bl.D = D;
   bl.T = T;
   bl.g = g;

@@ -118,7 +118,7 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                                          const __bf16* __restrict__ v, __bf16* __restrict__ o,
-                                                         float* __restrict__ lse, int Hq, int g, int S,
+                                                         float* __restrict__ lse, int Hq, int g, int Sq, int Sk,
                                                          float scale_log2, int causal) {
   constexpr int KVT = 64;               // key/value rows per LDS tile
   constexpr int PITCH = 2 * D + 48;     // bytes per LDS row: 16-byte row reads and transposing reads conflict-free
@@ -136,15 +136,16 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const __bf16* __restric
   const int kvh = head / g;
   const int q_base = blockIdx.x * 32 * NW;
   const int q_row = q_base + 32 * w + c32;  // this lane's query row
-  const __bf16* qh = q + (size_t)head * S * D;
-  const __bf16* kh = k + (size_t)kvh * S * D;
-  const __bf16* vh = v + (size_t)kvh * S * D;
+  const __bf16* qh = q + (size_t)head * Sq * D;
+  const __bf16* kh = k + (size_t)kvh * Sk * D;
+  const __bf16* vh = v + (size_t)kvh * Sk * D;
+  const int off = Sk - Sq;  // causal, aligned at the bottom right: query row i sees keys 0 .. i + off
 
   bf16x8 qb[DC];
 #pragma unroll
   for (int c = 0; c < DC; ++c) qb[c] = *(const bf16x8*)(qh + (size_t)q_row * D + 16 * c + 8 * h2);
 
-  const int n_tiles = causal ? (q_base + 32 * NW - 1) / KVT + 1 : S / KVT;
+  const int n_tiles = causal ? (q_base + 32 * NW - 1 + off) / KVT + 1 : Sk / KVT;
 
   bf16x8 pk[CPT], pv[CPT];
   auto load_tile = [&](int t) {
@@ -192,7 +193,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const __bf16* __restric
         float x = s[kb][r] * scale_log2;
         if (causal) {
           const int kv = t * KVT + kb * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-          if (kv > q_row) x = -INFINITY;
+          if (kv > q_row + off) x = -INFINITY;
         }
         s[kb][r] = x;
         mt = fmaxf(mt, x);
@@ -231,7 +232,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const __bf16* __restric
   }
   const float l_tot = l_part + __shfl_xor(l_part, 32);
   const float inv = 1.f / l_tot;
-  __bf16* oh = o + (size_t)head * S * D + (size_t)q_row * D;
+  __bf16* oh = o + (size_t)head * Sq * D + (size_t)q_row * D;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -241,7 +242,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const __bf16* __restric
       for (int i = 0; i < 4; ++i) out[i] = (__bf16)(acc[db][4 * j + i] * inv);
       *(bf16x4*)(oh + db * 32 + 8 * j + 4 * h2) = out;
     }
-  if (h2 == 0) lse[(size_t)head * S + q_row] = (m_run + __log2f(l_tot)) * kLn2;
+  if (h2 == 0) lse[(size_t)head * Sq + q_row] = (m_run + __log2f(l_tot)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -339,7 +340,7 @@ struct BwdArgs {
   long long spin_ticks;
   float scale;       // softmax scale
   float scale_log2;  // softmax scale * log2(e)
-  int S, g, causal;
+  int Sq, Sk, g, causal;
 };
 
 // Semaphore words per 64-row dQ block: one per wave that holds dQ tiles.
@@ -398,8 +399,9 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
   auto step_at = [&](int i) { return make_int4(steps[4 * i], steps[4 * i + 1], steps[4 * i + 2], steps[4 * i + 3]); };
   const int wg = blockIdx.x;
   const int beg = offsets[wg], end = offsets[wg + 1];
-  const int S = a.S, g = a.g;
-  const int nblk = S / M;  // 64-row blocks per head
+  const int Sq = a.Sq, Sk = a.Sk, g = a.g;
+  const int nblk = Sq / M;  // 64-row blocks per head
+  const int diag_off = (Sk - Sq) / T;  // causal: tile pair (qi, qi + diag_off) straddles the diagonal
   unsigned long long stall = 0;
   const unsigned long long t_start = __builtin_amdgcn_s_memtime();
   if (threadIdx.x == 0) *s_flag = 0;
@@ -421,8 +423,8 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
   const int st_tid = threadIdx.x < 2 * M ? threadIdx.x : 0;
   const float st_mul = st_tid < M ? kLog2e : 1.f;
   auto load_block = [&](int head, int row0) {
-    const __bf16* qh = a.q + ((size_t)head * S + row0) * D;
-    const __bf16* doh = a.dO + ((size_t)head * S + row0) * D;
+    const __bf16* qh = a.q + ((size_t)head * Sq + row0) * D;
+    const __bf16* doh = a.dO + ((size_t)head * Sq + row0) * D;
 #pragma unroll
     for (int i = 0; i < QCH; ++i) {
       const int ch = threadIdx.x + i * NT;
@@ -430,7 +432,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
       pdo[i] = *(const bf16x8*)(doh + (size_t)ch * 8);
     }
     const float* src = st_tid < M ? a.lse : a.delta;
-    pstat = src[(size_t)head * S + row0 + (st_tid & (M - 1))];
+    pstat = src[(size_t)head * Sq + row0 + (st_tid & (M - 1))];
   };
   auto store_block = [&](int buf) {
 #pragma unroll
@@ -449,8 +451,8 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
   int epi_kvh = 0, epi_kj = 0;
   auto write_dkdv = [&](int kvh_, int kj_) {
     const size_t o_lane = (size_t)opaque((kv0 + 4 * h2) * D + hf * DH * 32 + c32);
-    __bf16* dkh = a.dk + ((size_t)kvh_ * S + (size_t)kj_ * T) * D + o_lane;
-    __bf16* dvh = a.dv + ((size_t)kvh_ * S + (size_t)kj_ * T) * D + o_lane;
+    __bf16* dkh = a.dk + ((size_t)kvh_ * Sk + (size_t)kj_ * T) * D + o_lane;
+    __bf16* dvh = a.dv + ((size_t)kvh_ * Sk + (size_t)kj_ * T) * D + o_lane;
 #pragma unroll
     for (int j = 0; j < DH; ++j)
 #pragma unroll
@@ -491,8 +493,8 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
     const int ord = ordf & ((1 << 28) - 1);
     const bool first = ordf & (1 << 28), last = ordf & (1 << 29);
     const int kvh = head / g;
-    const __bf16* kh = a.k + ((size_t)kvh * S + (size_t)kj * T) * D;
-    const __bf16* vh = a.v + ((size_t)kvh * S + (size_t)kj * T) * D;
+    const __bf16* kh = a.k + ((size_t)kvh * Sk + (size_t)kj * T) * D;
+    const __bf16* vh = a.v + ((size_t)kvh * Sk + (size_t)kj * T) * D;
     if (first) {
       // New chain: its V rows to registers and its K tile to LDS.  The previous
       // chain's dK/dV are written only after that, so that waiting for these
@@ -519,7 +521,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
         dv_acc[j] = f32x16{};
       }
     }
-    const bool diag = a.causal && (qi == kj);
+    const bool diag = a.causal && (kj == qi + diag_off);
 
     for (int sub = 0; sub < SUBS; ++sub) {
       __syncthreads();  // B1: Q/dO/LSE/Delta of this block (and sK) visible; P^T, dS^T free
@@ -801,21 +803,21 @@ __global__ __launch_bounds__(256) void dq_finalize_kernel(const float* __restric
 // Host launchers.
 // ---------------------------------------------------------------------------
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
-                      int S, int D, float scale, int causal, hipStream_t st) {
+                      int Sq, int Sk, int D, float scale, int causal, hipStream_t st) {
   const int g = Hq / Hkv;
   const float sl2 = scale * kLog2e;
-  const bool big = (S % 128) == 0;
-  dim3 grid(S / (big ? 128 : 64), B * Hq);
+  const bool big = (Sq % 128) == 0;
+  dim3 grid(Sq / (big ? 128 : 64), B * Hq);
   auto qp = (const __bf16*)q;
   auto kp = (const __bf16*)k;
   auto vp = (const __bf16*)v;
   auto op = (__bf16*)o;
   if (D == 128) {
-    if (big) hipLaunchKernelGGL((fwd_kernel<128, 4>), grid, dim3(256), 0, st, qp, kp, vp, op, lse, Hq, g, S, sl2, causal);
-    else hipLaunchKernelGGL((fwd_kernel<128, 2>), grid, dim3(128), 0, st, qp, kp, vp, op, lse, Hq, g, S, sl2, causal);
+    if (big) hipLaunchKernelGGL((fwd_kernel<128, 4>), grid, dim3(256), 0, st, qp, kp, vp, op, lse, Hq, g, Sq, Sk, sl2, causal);
+    else hipLaunchKernelGGL((fwd_kernel<128, 2>), grid, dim3(128), 0, st, qp, kp, vp, op, lse, Hq, g, Sq, Sk, sl2, causal);
   } else {
-    if (big) hipLaunchKernelGGL((fwd_kernel<64, 4>), grid, dim3(256), 0, st, qp, kp, vp, op, lse, Hq, g, S, sl2, causal);
-    else hipLaunchKernelGGL((fwd_kernel<64, 2>), grid, dim3(128), 0, st, qp, kp, vp, op, lse, Hq, g, S, sl2, causal);
+    if (big) hipLaunchKernelGGL((fwd_kernel<64, 4>), grid, dim3(256), 0, st, qp, kp, vp, op, lse, Hq, g, Sq, Sk, sl2, causal);
+    else hipLaunchKernelGGL((fwd_kernel<64, 2>), grid, dim3(128), 0, st, qp, kp, vp, op, lse, Hq, g, Sq, Sk, sl2, causal);
   }
   return hipGetLastError();
 }
@@ -856,7 +858,8 @@ hipError_t launch_bwd(const BwdLaunch& L, hipStream_t st) {
   a.spin_ticks = L.spin_ticks;
   a.scale = L.scale;
   a.scale_log2 = L.scale * kLog2e;
-  a.S = L.S;
+  a.Sq = L.Sq;
+  a.Sk = L.Sk;
   a.g = L.g;
   a.causal = L.causal;
   dim3 grid(L.P);

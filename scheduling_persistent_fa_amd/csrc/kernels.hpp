@@ -25,12 +25,12 @@ struct BwdLaunch {
   unsigned long long* stall;
   long long spin_ticks;    // wait budget in 100 MHz real-time ticks
   float scale;
-  int S, D, T, g, causal, P;
+  int Sq, Sk, D, T, g, causal, P;
   bool atomic;
 };
 
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
-                      int S, int D, float scale, int causal, hipStream_t st);
+                      int Sq, int Sk, int D, float scale, int causal, hipStream_t st);
 hipError_t launch_delta(const void* o, const void* dO, float* delta, long long rows, int D, int* zero_i32,
                         long long n_zero_i32, float* zero_f32, long long n_zero_f32, hipStream_t st);
 hipError_t launch_bwd(const BwdLaunch& L, hipStream_t st);

@@ -8,6 +8,8 @@
 //            workgroup keeping key/value tile p visits query tiles
 //            p, p+1, ..., N-1, 0, ..., p-1, so the t-th contribution to every
 //            dQ tile arrives at step t and no two workgroups meet (§2.2.B).
+//            With Nq query and Nk key/value tiles: Nk members, member p
+//            visits query tiles (p + t) mod Nq.
 //  SYM_SHIFT causal mask: a gang of N/2 workgroups; member p keeps tile p
 //            through a dense rectangle phase (query tiles N/2..N-1, shifted)
 //            and its own triangle part, then tile N-1-p through the folded
@@ -50,13 +52,14 @@ std::string build_list_scheduled(const Schedule& s, std::vector<std::vector<Step
   std::vector<Triple> chain;
   std::vector<int32_t> ords;
   for (int grp = 0; grp < s.groups; ++grp) {
-    for (int kj = 0; kj < s.N; ++kj) {
-      const int lo = (s.mask == kMaskCausal) ? kj : 0;
+    for (int kj = 0; kj < s.Nk; ++kj) {
+      // causal, bottom-right aligned: the query tiles that see kv tile kj
+      const int lo = (s.mask == kMaskCausal) ? std::max(0, kj - (s.Nk - s.Nq)) : 0;
       chain.clear();
       ords.clear();
       for (int u = 0; u < s.g; ++u) {
-        for (int t = 0; t < s.N - lo; ++t) {
-          const int qi = (s.walk == kDescQ) ? (s.N - 1 - t) : (lo + t);
+        for (int t = 0; t < s.Nq - lo; ++t) {
+          const int qi = (s.walk == kDescQ) ? (s.Nq - 1 - t) : (lo + t);
           chain.push_back({grp * s.g + u, qi, kj});
           ords.push_back(kj);  // ascending key/value order for every dQ tile
         }
@@ -90,9 +93,9 @@ int gang_slot(int gi, int p, int n_gangs, int gang, const Schedule& s) {
 }
 
 std::string build_gang(const Schedule& s, std::vector<std::vector<StepRec>>& per_wg) {
-  const int N = s.N;
+  const int N = s.Nq;  // query tiles (== Nk for symmetric shift)
   // units: key/value tiles (shift) or tile pairs i, N-1-i (symmetric shift)
-  const int units = (s.walk == kShift) ? N : N / 2;
+  const int units = (s.walk == kShift) ? s.Nk : N / 2;
   const int gang = (s.max_gang > 0 && s.max_gang < units) ? s.max_gang : units;
   const int n_gangs = s.P / gang;
   if (n_gangs < 1) return "gang of " + std::to_string(gang) + " workgroups exceeds " + std::to_string(s.P);
@@ -125,13 +128,13 @@ std::string build_gang(const Schedule& s, std::vector<std::vector<StepRec>>& per
       for (int u = 0; u < s.g; ++u)
         for (int qi : ch.second) bucket[static_cast<size_t>(u) * N + qi].push_back({pos++, ch.first});
   }
-  std::vector<int32_t> rank(static_cast<size_t>(s.g) * N * N, -1);  // [u][qi][kj]
+  std::vector<int32_t> rank(static_cast<size_t>(s.g) * N * s.Nk, -1);  // [u][qi][kj]
   for (int u = 0; u < s.g; ++u)
     for (int qi = 0; qi < N; ++qi) {
       auto& v = bucket[static_cast<size_t>(u) * N + qi];
       std::sort(v.begin(), v.end());
       for (size_t r = 0; r < v.size(); ++r)
-        rank[(static_cast<size_t>(u) * N + qi) * N + v[r].second] = static_cast<int32_t>(r);
+        rank[(static_cast<size_t>(u) * N + qi) * s.Nk + v[r].second] = static_cast<int32_t>(r);
     }
   std::vector<Triple> chain;
   std::vector<int32_t> ords;
@@ -145,7 +148,7 @@ std::string build_gang(const Schedule& s, std::vector<std::vector<StepRec>>& per
         for (int u = 0; u < s.g; ++u)
           for (int qi : ch.second) {
             chain.push_back({grp * s.g + u, qi, ch.first});
-            ords.push_back(rank[(static_cast<size_t>(u) * N + qi) * N + ch.first]);
+            ords.push_back(rank[(static_cast<size_t>(u) * N + qi) * s.Nk + ch.first]);
           }
         push_chain(per_wg[w], chain, ords);
       }
@@ -156,9 +159,11 @@ std::string build_gang(const Schedule& s, std::vector<std::vector<StepRec>>& per
 
 }  // namespace
 
-std::string choose_schedule(int mask, int N, int D, int g, int P, int* kind, int* max_gang) {
-  if (N < 1 || D < 1 || g < 1 || P < 1) return "sizes must be positive";
+std::string choose_schedule(int mask, int Nq, int Nk, int D, int g, int P, int* kind, int* max_gang) {
+  if (Nq < 1 || Nk < 1 || D < 1 || g < 1 || P < 1) return "sizes must be positive";
   if (mask != kMaskFull && mask != kMaskCausal) return "unknown mask";
+  if (mask == kMaskCausal && Nk < Nq) return "a causal mask needs Sk >= Sq";
+  const int N = Nq;
   // Measured on MI355X: the gang schedules are the fastest deterministic ones
   // for every shape tried, whatever D and g; D and g are kept in the key.
   (void)D;
@@ -166,8 +171,8 @@ std::string choose_schedule(int mask, int N, int D, int g, int P, int* kind, int
   int units = 0;
   if (mask == kMaskFull) {
     *kind = kShift;
-    units = N;
-  } else if (N % 2 == 0) {
+    units = Nk;
+  } else if (N % 2 == 0 && Nk == Nq) {
     *kind = kSymShift;
     units = N / 2;
   } else {
@@ -177,12 +182,13 @@ std::string choose_schedule(int mask, int N, int D, int g, int P, int* kind, int
   return "";
 }
 
-std::string build_schedule(int mask, int kind, int N, int g, int groups, int P, bool xcd_local,
+std::string build_schedule(int mask, int kind, int Nq, int Nk, int g, int groups, int P, bool xcd_local,
                            int atomic_walk, int max_gang, Schedule* out) {
-  if (N < 1 || g < 1 || groups < 1 || P < 1) return "sizes must be positive";
+  if (Nq < 1 || Nk < 1 || g < 1 || groups < 1 || P < 1) return "sizes must be positive";
   if (mask != kMaskFull && mask != kMaskCausal) return "unknown mask";
   if (kind < kSerial || kind > kAtomic) return "unknown schedule";
-  if (N > 32767) return "too many tiles";
+  if (Nq > 32767 || Nk > 32767) return "too many tiles";
+  if (mask == kMaskCausal && Nk < Nq) return "a causal mask needs at least as many key/value tiles as query tiles";
   int walk = kind;
   if (kind == kAtomic) {
     walk = (atomic_walk < 0) ? (mask == kMaskCausal ? kDescQ : kSerial) : atomic_walk;
@@ -190,12 +196,14 @@ std::string build_schedule(int mask, int kind, int N, int g, int groups, int P, 
   }
   if (walk == kShift && mask != kMaskFull) return "shift scheduling needs a full mask";
   if (walk == kSymShift && mask != kMaskCausal) return "symmetric shift needs a causal mask";
-  if (walk == kSymShift && (N % 2)) return "symmetric shift needs an even tile count";
+  if (walk == kSymShift && (Nq % 2)) return "symmetric shift needs an even tile count";
+  if (walk == kSymShift && Nk != Nq) return "symmetric shift needs as many key/value tiles as query tiles";
   Schedule s;
   s.mask = mask;
   s.kind = kind;
   s.walk = walk;
-  s.N = N;
+  s.Nq = Nq;
+  s.Nk = Nk;
   s.g = g;
   s.groups = groups;
   s.P = P;
@@ -218,7 +226,7 @@ std::string build_schedule(int mask, int kind, int N, int g, int groups, int P, 
 }
 
 bool simulate_schedule(const Schedule& s, double c, double r, double* makespan, double* total_wait) {
-  const size_t tiles = static_cast<size_t>(s.g) * s.groups * s.N;
+  const size_t tiles = static_cast<size_t>(s.g) * s.groups * s.Nq;
   std::vector<int32_t> count(tiles, 0);
   std::vector<double> done_at(tiles, 0.0);
   std::vector<int32_t> idx(s.P, 0);
@@ -231,7 +239,7 @@ bool simulate_schedule(const Schedule& s, double c, double r, double* makespan, 
       const int32_t end = s.offsets[w + 1];
       while (s.offsets[w] + idx[w] < end) {
         const StepRec& st = s.steps[s.offsets[w] + idx[w]];
-        const size_t key = static_cast<size_t>(st.head) * s.N + st.qi;
+        const size_t key = static_cast<size_t>(st.head) * s.Nq + st.qi;
         const int32_t ord = st.ordflags & kOrdMask;
         if (count[key] != ord) break;
         const double ready = t[w] + c;
@@ -255,26 +263,26 @@ bool simulate_schedule(const Schedule& s, double c, double r, double* makespan, 
 }
 
 std::string validate_schedule(const Schedule& s) {
-  const int N = s.N;
+  const int Nq = s.Nq, Nk = s.Nk, off = Nk - Nq;  // causal: query tile qi sees kv tiles 0 .. qi + off
   const long long heads = static_cast<long long>(s.g) * s.groups;
   if (static_cast<int>(s.offsets.size()) != s.P + 1) return "offset table size";
   if (s.offsets[0] != 0 || s.offsets[s.P] != static_cast<int32_t>(s.steps.size())) return "offset table bounds";
-  std::vector<uint8_t> seen(static_cast<size_t>(heads) * N * N, 0);
-  std::vector<int32_t> owner(static_cast<size_t>(s.groups) * N, -1);
+  std::vector<uint8_t> seen(static_cast<size_t>(heads) * Nq * Nk, 0);
+  std::vector<int32_t> owner(static_cast<size_t>(s.groups) * Nk, -1);
   long long covered = 0;
   for (int w = 0; w < s.P; ++w) {
     if (s.offsets[w + 1] < s.offsets[w]) return "offsets decrease";
-    long long run = -1;  // chain key (group * N + kj) of the open chain
+    long long run = -1;  // chain key (group * Nk + kj) of the open chain
     for (int32_t i = s.offsets[w]; i < s.offsets[w + 1]; ++i) {
       const StepRec& st = s.steps[i];
-      if (st.head < 0 || st.head >= heads || st.qi < 0 || st.qi >= N || st.kj < 0 || st.kj >= N)
+      if (st.head < 0 || st.head >= heads || st.qi < 0 || st.qi >= Nq || st.kj < 0 || st.kj >= Nk)
         return "step index out of range";
-      if (s.mask == kMaskCausal && st.kj > st.qi) return "masked tile pair scheduled";
-      const size_t pair = (static_cast<size_t>(st.head) * N + st.qi) * N + st.kj;
+      if (s.mask == kMaskCausal && st.kj > st.qi + off) return "masked tile pair scheduled";
+      const size_t pair = (static_cast<size_t>(st.head) * Nq + st.qi) * Nk + st.kj;
       if (seen[pair]) return "tile pair scheduled twice";
       seen[pair] = 1;
       ++covered;
-      const long long ck = static_cast<long long>(st.head / s.g) * N + st.kj;
+      const long long ck = static_cast<long long>(st.head / s.g) * Nk + st.kj;
       if (st.ordflags & kFirstFlag) {
         if (run >= 0) return "chain not closed before the next starts";
         if (owner[ck] >= 0) return "chain split";
@@ -287,18 +295,17 @@ std::string validate_schedule(const Schedule& s) {
     if (run >= 0) return "list ends inside a chain";
   }
   long long expect = 0;
-  for (int qi = 0; qi < N; ++qi) expect += (s.mask == kMaskCausal) ? qi + 1 : N;
+  for (int qi = 0; qi < Nq; ++qi) expect += (s.mask == kMaskCausal) ? qi + off + 1 : Nk;
   if (covered != expect * heads) return "coverage mismatch";
   for (int32_t o : owner)
     if (o < 0) return "missing chain";
   // ordinals of each dQ tile: exactly 0..count-1
-  std::vector<int32_t> cnt(static_cast<size_t>(heads) * N, 0);
-  std::vector<uint8_t> ordseen(static_cast<size_t>(heads) * N * N, 0);
+  std::vector<uint8_t> ordseen(static_cast<size_t>(heads) * Nq * Nk, 0);
   for (const StepRec& st : s.steps) {
     const int32_t ord = st.ordflags & kOrdMask;
-    const int32_t lim = (s.mask == kMaskCausal) ? st.qi + 1 : N;
+    const int32_t lim = (s.mask == kMaskCausal) ? st.qi + off + 1 : Nk;
     if (ord < 0 || ord >= lim) return "ordinal out of range";
-    const size_t k = (static_cast<size_t>(st.head) * N + st.qi) * N + ord;
+    const size_t k = (static_cast<size_t>(st.head) * Nq + st.qi) * Nk + ord;
     if (ordseen[k]) return "ordinal repeated";
     ordseen[k] = 1;
   }

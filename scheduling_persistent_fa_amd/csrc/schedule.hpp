@@ -31,7 +31,8 @@ struct StepRec {
 
 struct Schedule {
   int mask = 0, kind = 0, walk = 0;  // walk: the ordering schedule (== kind unless kind is ATOMIC)
-  int N = 0, g = 1, groups = 1, P = 1;
+  int Nq = 0, Nk = 0;                // query tiles and key/value tiles per sequence
+  int g = 1, groups = 1, P = 1;
   bool xcd_local = true;
   int max_gang = 0;                  // 0: natural gang size (N for shift, N/2 for symmetric shift)
   std::vector<int32_t> offsets;  // P + 1
@@ -39,12 +40,14 @@ struct Schedule {
 };
 
 // Returns an empty string on success, else the reason (unsupported combination).
-std::string build_schedule(int mask, int kind, int N, int g, int groups, int P, bool xcd_local,
+// Nq query tiles, Nk key/value tiles.  The causal mask is aligned at the
+// bottom right: query tile qi sees key/value tiles 0 .. qi + Nk - Nq.
+std::string build_schedule(int mask, int kind, int Nq, int Nk, int g, int groups, int P, bool xcd_local,
                            int atomic_walk, int max_gang, Schedule* out);
 // Empty string if valid, else the first violation found.
 std::string validate_schedule(const Schedule& s);
 // The deterministic schedule (and gang cap) chosen for a shape; empty string on success.
-std::string choose_schedule(int mask, int N, int D, int g, int P, int* kind, int* max_gang);
+std::string choose_schedule(int mask, int Nq, int Nk, int D, int g, int P, int* kind, int* max_gang);
 // Unit-cost DAG simulation; returns false on deadlock.
 bool simulate_schedule(const Schedule& s, double c, double r, double* makespan, double* total_wait);
 

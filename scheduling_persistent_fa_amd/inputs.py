@@ -7,7 +7,7 @@ and the GPU path use it without sharing any computation.
 Recipe: numpy ``default_rng(seed)``; fp32 standard normals drawn in the order
 Q, K, V, dO, multiplied by ``std``; then rounded to bfloat16 with
 round-to-nearest-even.  Q and dO have shape [B, Hq, S, D]; K and V have shape
-[B, Hkv, S, D]; all contiguous row-major (BHSD).
+[B, Hkv, Sk, D] (Sk = S unless given); all contiguous row-major (BHSD).
 """
 from __future__ import annotations
 
@@ -40,21 +40,24 @@ class AttnInputs:
     Hkv: int
     S: int
     D: int
+    Sk: int = 0
 
     def as_f64(self, name: str) -> np.ndarray:
         return bf16_bits_to_f32(getattr(self, name)).astype(np.float64)
 
 
-def make_inputs(B: int, Hq: int, Hkv: int, S: int, D: int, seed: int = 0, std: float = 1.0) -> AttnInputs:
+def make_inputs(B: int, Hq: int, Hkv: int, S: int, D: int, seed: int = 0, std: float = 1.0,
+                Sk: int | None = None) -> AttnInputs:
+    Sk = S if Sk is None else Sk
     rng = np.random.default_rng(seed)
-    shapes = {"q": (B, Hq, S, D), "k": (B, Hkv, S, D), "v": (B, Hkv, S, D), "do": (B, Hq, S, D)}
+    shapes = {"q": (B, Hq, S, D), "k": (B, Hkv, Sk, D), "v": (B, Hkv, Sk, D), "do": (B, Hq, S, D)}
     out = {}
     for name in ("q", "k", "v", "do"):
         x = rng.standard_normal(size=shapes[name], dtype=np.float32)
         if std != 1.0:
             x *= np.float32(std)
         out[name] = f32_to_bf16_bits(x)
-    return AttnInputs(B=B, Hq=Hq, Hkv=Hkv, S=S, D=D, **out)
+    return AttnInputs(B=B, Hq=Hq, Hkv=Hkv, S=S, D=D, Sk=Sk, **out)
 
 
 # The five workloads: (name, B, Hq, Hkv, S, D, causal, tile, std).
@@ -65,4 +68,9 @@ WORKLOADS = {
     "c4_full_s16384_d128": dict(B=1, Hq=16, Hkv=16, S=16384, D=128, causal=False, tile=128, std=1.0),
     "c4_causal_s16384_d128": dict(B=1, Hq=16, Hkv=16, S=16384, D=128, causal=True, tile=128, std=1.0),
     "c5_gqa_causal_s8192_d128": dict(B=1, Hq=32, Hkv=8, S=8192, D=128, causal=True, tile=128, std=0.5),
+    # queries and keys of different lengths (S query rows, Sk key rows): cross
+    # attention, and a causal continuation aligned at the bottom right
+    "x1_cross_q4096_k16384_d128": dict(B=1, Hq=16, Hkv=16, S=4096, Sk=16384, D=128, causal=False, tile=128, std=1.0),
+    "x2_causal_q4096_k16384_d128": dict(B=1, Hq=16, Hkv=16, S=4096, Sk=16384, D=128, causal=True, tile=128,
+                                        std=1.0),
 }

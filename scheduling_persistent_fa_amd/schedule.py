@@ -8,10 +8,12 @@ import numpy as np
 from . import _lib
 
 
-def choose(mask: int, N: int, D: int, g: int, P: int):
-    """(schedule, max_gang) the library's adaptive rule picks for a shape."""
+def choose(mask: int, N: int, D: int, g: int, P: int, Nk: int | None = None):
+    """(schedule, max_gang) the library's adaptive rule picks for a shape (N query
+    tiles, Nk key/value tiles, default N)."""
     kind, cap = ctypes.c_int(), ctypes.c_int()
-    _lib.check(_lib.lib().dash_schedule_choose(mask, N, D, g, P, ctypes.byref(kind), ctypes.byref(cap)))
+    _lib.check(_lib.lib().dash_schedule_choose_qk(mask, N, N if Nk is None else Nk, D, g, P, ctypes.byref(kind),
+                                                  ctypes.byref(cap)))
     return kind.value, cap.value
 
 
@@ -23,11 +25,11 @@ class Schedule:
     """
 
     def __init__(self, mask: int, schedule: int, N: int, g: int, groups: int, P: int,
-                 xcd_local: bool = True, atomic_walk: int = -1, max_gang: int = 0):
+                 xcd_local: bool = True, atomic_walk: int = -1, max_gang: int = 0, Nk: int | None = None):
         L = _lib.lib()
         h = ctypes.c_void_p()
-        _lib.check(L.dash_schedule_build(mask, schedule, N, g, groups, P, int(bool(xcd_local)), atomic_walk,
-                                         max_gang, ctypes.byref(h)))
+        _lib.check(L.dash_schedule_build_qk(mask, schedule, N, N if Nk is None else Nk, g, groups, P,
+                                            int(bool(xcd_local)), atomic_walk, max_gang, ctypes.byref(h)))
         self._h = h
         self.P = L.dash_schedule_num_workgroups(h)
         self.num_steps = L.dash_schedule_num_steps(h)

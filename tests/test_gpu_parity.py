@@ -156,3 +156,41 @@ def test_autograd_op_gradients_match_oracle(causal):
     assert rel_err(to_f64(o), ref["o"]) <= TOL
     for t, name in ((q, "dq"), (k, "dk"), (v, "dv")):
         assert rel_err(to_f64(t.grad), ref[name]) <= TOL
+
+
+RECT = [  # name, B, Hq, Hkv, Sq, Sk, D, causal, tile
+    ("full_q256_k768_d64", 1, 2, 1, 256, 768, 64, False, 128),
+    ("full_q768_k256_d128", 1, 2, 2, 768, 256, 128, False, 128),
+    ("causal_q256_k768_d128", 1, 4, 2, 256, 768, 128, True, 128),
+    ("causal_q384_k640_d64_t64", 2, 2, 1, 384, 640, 64, True, 64),
+]
+
+
+@pytest.mark.parametrize("case", RECT, ids=[c[0] for c in RECT])
+def test_rectangular_shapes_match_oracle(case):
+    from scheduling_persistent_fa_amd.attention import AUTO
+    name, B, Hq, Hkv, Sq, Sk, D, causal, tile = case
+    say(f"[parity-rect] {name}")
+    inp_q = DeviceProblem(B, Hq, Hkv, Sq, D, causal, seed=1)   # Q, dO of Sq rows
+    inp_k = DeviceProblem(B, Hq, Hkv, Sk, D, causal, seed=2)   # K, V of Sk rows
+    q, do, k, v = inp_q.q, inp_q.do, inp_k.k, inp_k.v
+    q64, do64, k64, v64 = inp_q.f64("q"), inp_q.f64("do"), inp_k.f64("k"), inp_k.f64("v")
+    scale = 1.0 / np.sqrt(D)
+    ref = A.backward(q64, k64, v64, do64, scale, causal)
+    o, lse = attn_fwd(q, k, v, causal)
+    torch.cuda.synchronize()
+    assert rel_err(to_f64(o), ref["o"]) <= TOL
+    assert np.abs(to_f64(lse) - ref["lse"]).max() <= TOL * max(1.0, np.abs(ref["lse"]).max())
+    scheds = [SERIAL, DESC_Q] + ([] if causal else [SHIFT]) + [ATOMIC, AUTO]
+    for sched in scheds:
+        say(f"  schedule {_lib.SCHEDULE_NAMES[sched]}")
+        opts = make_opts(tile=tile, sync_check=True)
+        dq, dk, dv = attn_bwd(q, k, v, o, do, lse, causal, sched, opts=opts)
+        torch.cuda.synchronize()
+        for nm, got in (("dq", dq), ("dk", dk), ("dv", dv)):
+            e = rel_err(to_f64(got), ref[nm])
+            assert e <= TOL, (name, _lib.SCHEDULE_NAMES[sched], nm, e)
+        if sched != ATOMIC:
+            again = attn_bwd(q, k, v, o, do, lse, causal, sched, opts=opts)
+            for a_, b_ in zip((dq, dk, dv), again):
+                assert torch.equal(a_.view(torch.int16), b_.view(torch.int16))

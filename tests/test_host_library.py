@@ -155,3 +155,40 @@ def test_adaptive_choice_builds_valid_schedules(mask, N, g, groups, P):
     s.validate()
     lists = Sch.build(mask, kind, N, g, groups, P, max_gang=cap)
     assert sum(len(x) for x in lists) == s.num_steps
+
+
+# ---- rectangular tile grids (Nq query tiles x Nk key/value tiles) ----
+
+RECT_CASES = [  # mask, sched, Nq, Nk, g, groups, P, cap
+    (Sch.FULL, Sch.SERIAL, 4, 6, 1, 2, 5, 0), (Sch.FULL, Sch.DESC_Q, 6, 3, 2, 3, 7, 0),
+    (Sch.FULL, Sch.SHIFT, 4, 6, 1, 2, 12, 0), (Sch.FULL, Sch.SHIFT, 6, 4, 2, 3, 8, 0),
+    (Sch.CAUSAL, Sch.SERIAL, 3, 7, 1, 2, 6, 0), (Sch.CAUSAL, Sch.DESC_Q, 4, 9, 2, 2, 5, 0),
+    (Sch.FULL, Sch.SHIFT, 8, 32, 1, 16, 256, 0), (Sch.FULL, Sch.SHIFT, 16, 40, 1, 3, 64, 16),
+]
+
+
+@pytest.mark.parametrize("mask,sched,Nq,Nk,g,groups,P,cap", RECT_CASES)
+@pytest.mark.parametrize("xcd", [True, False])
+def test_rectangular_schedules_match_oracle_exactly(mask, sched, Nq, Nk, g, groups, P, cap, xcd):
+    lib_s = Schedule(mask, sched, Nq, g, groups, P, xcd_local=xcd, max_gang=cap, Nk=Nk)
+    lib_s.validate()
+    ora = Sch.build(mask, sched, Nq, g, groups, P, xcd_local=xcd, max_gang=cap, Nk=Nk)
+    Sch.validate(ora, mask, Nq, g, groups, Nk=Nk)
+    assert lib_s.lists() == _oracle_tuples(ora)
+
+
+def test_rectangular_rejections():
+    for args in [(Sch.CAUSAL, Sch.SERIAL, 5, 4), (Sch.CAUSAL, Sch.SYM_SHIFT, 4, 6), (Sch.CAUSAL, Sch.SHIFT, 4, 6)]:
+        mask, sched, nq, nk = args
+        with pytest.raises(_lib.DashError):
+            Schedule(mask, sched, nq, 1, 1, 16, Nk=nk)
+
+
+def test_adaptive_choice_on_rectangles():
+    from scheduling_persistent_fa_amd.schedule import choose
+    assert choose(Sch.FULL, 16, 128, 1, 256, Nk=64) == (_lib.SHIFT, 0)
+    assert choose(Sch.FULL, 16, 128, 1, 256, Nk=300) == (_lib.SHIFT, 256)   # gang of Nk capped to the grid
+    assert choose(Sch.CAUSAL, 16, 128, 1, 256, Nk=64) == (_lib.DESC_Q, 0)   # no symmetric shift on rectangles
+    assert choose(Sch.CAUSAL, 16, 128, 1, 256, Nk=16) == (_lib.SYM_SHIFT, 0)
+    with pytest.raises(_lib.DashError):
+        choose(Sch.CAUSAL, 16, 128, 1, 256, Nk=8)

@@ -202,3 +202,85 @@ def test_input_recipe_is_bf16_round_to_nearest_even():
     assert inp.q.shape == (1, 2, 8, 4) and inp.k.shape == (1, 1, 8, 4) and inp.q.dtype == np.uint16
     again = make_inputs(1, 2, 1, 8, 4, seed=0)
     assert np.array_equal(inp.do, again.do)
+
+
+# ---- queries and keys of different lengths (bottom-right causal alignment) ----
+
+def _loss_rect(q, k, v, do, scale, causal):
+    o, _ = A.forward(q, k, v, scale, causal)
+    return float((o * do).sum())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Sq,Sk,D,g", [(2, 5, 3, 1), (4, 7, 4, 2), (5, 5, 2, 1)] + [(6, 3, 3, 1)])
+def test_rectangular_gradients_match_central_differences(Sq, Sk, D, g, causal):
+    if causal and Sk < Sq:
+        pytest.skip("a causal mask needs Sk >= Sq (every query row sees a key)")
+    q, do = _rand((1, g, Sq, D), 101), _rand((1, g, Sq, D), 102)
+    k, v = _rand((1, 1, Sk, D), 103), _rand((1, 1, Sk, D), 104)
+    scale = 1.0 / math.sqrt(D)
+    res = A.backward(q, k, v, do, scale, causal)
+    h = 1e-6
+    for name, x in (("dq", q), ("dk", k), ("dv", v)):
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            xp = x.copy(); xp[idx] += h
+            xm = x.copy(); xm[idx] -= h
+            key = {"dq": "q", "dk": "k", "dv": "v"}[name]
+            ap = {"q": q, "k": k, "v": v}; ap[key] = xp
+            am = {"q": q, "k": k, "v": v}; am[key] = xm
+            num[idx] = (_loss_rect(ap["q"], ap["k"], ap["v"], do, scale, causal)
+                        - _loss_rect(am["q"], am["k"], am["v"], do, scale, causal)) / (2 * h)
+        err = np.abs(num - res[name]).max() / max(1e-12, np.abs(num).max())
+        assert err < 1e-6, (name, err)
+
+
+def test_bottom_right_causal_row_equals_full_attention_over_its_keys():
+    # Query row i of Sq rows against Sk keys sees keys 0 .. i + Sk - Sq.
+    Sq, Sk, D = 10, 26, 8
+    q, do = _rand((1, 1, Sq, D), 110), _rand((1, 1, Sq, D), 111)
+    k, v = _rand((1, 1, Sk, D), 112), _rand((1, 1, Sk, D), 113)
+    c = A.backward(q, k, v, do, 0.4, True)
+    for i in (0, 3, Sq - 1):
+        n = i + Sk - Sq + 1
+        pre = A.backward(q[:, :, i:i + 1], k[:, :, :n], v[:, :, :n], do[:, :, i:i + 1], 0.4, False)
+        assert np.allclose(pre["o"][0, 0, 0], c["o"][0, 0, i], rtol=1e-12, atol=1e-12)
+        assert abs(pre["lse"][0, 0, 0] - c["lse"][0, 0, i]) < 1e-12
+        assert np.allclose(pre["dq"][0, 0, 0], c["dq"][0, 0, i], rtol=1e-12, atol=1e-12)
+    # the last query row sees every key: it equals the full-mask row
+    f = A.backward(q, k, v, do, 0.4, False)
+    assert np.allclose(f["o"][0, 0, -1], c["o"][0, 0, -1], atol=1e-12)
+
+
+def test_rectangular_sampled_rows_match_full_backward():
+    B, Hq, Hkv, Sq, Sk, D = 1, 4, 2, 24, 40, 8
+    q, do = _rand((B, Hq, Sq, D), 120), _rand((B, Hq, Sq, D), 121)
+    k, v = _rand((B, Hkv, Sk, D), 122), _rand((B, Hkv, Sk, D), 123)
+    for causal in (False, True):
+        full = A.backward(q, k, v, do, 0.35, causal, row_block=7)
+        assert np.allclose(A.dq_rows(q, k, v, do, 0, 3, [0, 11, 23], 0.35, causal), full["dq"][0, 3, [0, 11, 23]],
+                           atol=1e-12)
+        dk, dv = A.dkdv_rows(q, k, v, do, 0, 1, [0, 17, 39], 0.35, causal)
+        assert np.allclose(dk, full["dk"][0, 1, [0, 17, 39]], atol=1e-12)
+        assert np.allclose(dv, full["dv"][0, 1, [0, 17, 39]], atol=1e-12)
+
+
+def test_rectangular_matches_torch_autograd_float64():
+    torch = pytest.importorskip("torch")
+    B, Hq, Hkv, Sq, Sk, D = 1, 2, 1, 13, 29, 16
+    q, do = _rand((B, Hq, Sq, D), 130), _rand((B, Hq, Sq, D), 131)
+    k, v = _rand((B, Hkv, Sk, D), 132), _rand((B, Hkv, Sk, D), 133)
+    scale = 1 / math.sqrt(D)
+    for causal in (False, True):
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        s = scale * tq @ tk.repeat_interleave(Hq // Hkv, dim=1).transpose(-1, -2)
+        if causal:  # key j hidden from query i when j > i + Sk - Sq
+            s = s.masked_fill(torch.ones(Sq, Sk, dtype=torch.bool).triu(Sk - Sq + 1), float("-inf"))
+        o = torch.softmax(s, dim=-1) @ tv.repeat_interleave(Hq // Hkv, dim=1)
+        o.backward(torch.tensor(do))
+        r = A.backward(q, k, v, do, scale, causal)
+        assert np.allclose(r["o"], o.detach().numpy(), atol=1e-13)
+        for got, t in ((r["dq"], tq), (r["dk"], tk), (r["dv"], tv)):
+            assert np.allclose(got, t.grad.numpy(), atol=1e-12)

@@ -204,3 +204,27 @@ def test_shift_placement_keeps_runs_of_16_members_on_one_chiplet():
     # other walks and grids keep the congruent mapping
     assert Sch.gang_slot(1, 3, 4, 64, True, 256, False) == 3 * 4 + 1
     assert Sch.gang_slot(1, 3, 2, 50, True, 100, True) == 3 * 2 + 1
+
+
+@pytest.mark.parametrize("mask,sched", [(FULL, SERIAL), (FULL, DESC_Q), (FULL, SHIFT), (CAUSAL, SERIAL),
+                                        (CAUSAL, DESC_Q)])
+def test_rectangular_schedules_valid_exhaustively(mask, sched):
+    # Every Nq x Nk grid up to 6 x 6 (causal: Nk >= Nq), two groups, several grid sizes.
+    for nq in range(1, 7):
+        for nk in range(1, 7):
+            if mask == CAUSAL and nk < nq:
+                continue
+            for P in {max(1, nk if sched == SHIFT else 1), nk + 3, 2 * nk}:
+                lists = Sch.build(mask, sched, nq, 2, 2, P, Nk=nk)
+                Sch.validate(lists, mask, nq, 2, 2, Nk=nk)
+
+
+def test_rectangular_shift_contributions_are_one_per_step_when_nk_le_nq():
+    # Latin rectangle: with Nk <= Nq no two members of a shift gang touch one
+    # dQ tile at the same step, and tile qi gets its t-th contribution at step t.
+    nq, nk = 7, 5
+    lists = Sch.build(FULL, SHIFT, nq, 1, 1, nk, Nk=nk)
+    for lst in lists:
+        for t, s in enumerate(lst):
+            assert s.qi == (s.kj + t) % nq
+    assert Sch.monotone_in_lockstep(lists, 1)
