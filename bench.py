@@ -113,10 +113,8 @@ def main():
     torch.cuda.synchronize()
     fl = flops(B, Hq, S, D, causal, Sk)
 
-    square = Sk == S
-    # Symmetric shift pairs query tile p with N-1-p and needs a square grid;
-    # shift needs a full mask, so a causal rectangle has only the list walks.
-    fast = ["shift"] if not causal else (["sym_shift"] if square else [])
+    # shift needs a full mask; symmetric shift pairs query tiles p, N-1-p and needs N even
+    fast = ["shift"] if not causal else (["sym_shift"] if (S // tile) % 2 == 0 else [])
     det_names = ["serial", "desc_q"] + fast
     if args.schedules:
         det_names = [s for s in args.schedules.split(",") if s]

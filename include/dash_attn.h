@@ -138,8 +138,11 @@ int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
  * in dash_attn_fwd_qk; dQ like Q, dK/dV like K).  Sq and Sk are multiples of
  * the tile.  Schedules over the Nq x Nk tile grid: SERIAL and DESC_Q walk the
  * query tiles that see each key/value tile; SHIFT (full mask) runs a gang of
- * Nk workgroups, member p visiting query tiles (p + t) mod Nq; SYM_SHIFT needs
- * Sq = Sk.  The workspace is sized with S = Sq.
+ * min(Nq, Nk) workgroups, the member holding key/value tile i visiting query
+ * tiles (i + t) mod Nq (with Nk > Nq member p holds tiles p, p + Nq, ... in
+ * turn); SYM_SHIFT (causal, Nq even) runs the square schedule on the last Nq
+ * key/value tiles and hands the Nk - Nq fully visible ones to the same N/2
+ * members in shifted rounds.  The workspace is sized with S = Sq.
  */
 int dash_attn_bwd_qk(const void* q, const void* k, const void* v, const void* o, const void* dO,
                      const float* lse, void* dq, void* dk, void* dv,
@@ -170,7 +173,7 @@ int dash_schedule_build(int mask, int schedule, int N, int g, int groups, int P,
                         int atomic_walk, int max_gang, dash_schedule** out);
 
 /* Same for Nq query tiles and Nk key/value tiles (causal: Nk >= Nq, aligned
- * at the bottom right; symmetric shift: Nq = Nk). */
+ * at the bottom right; gang schedules extended as in dash_attn_bwd_qk). */
 int dash_schedule_build_qk(int mask, int schedule, int Nq, int Nk, int g, int groups, int P, int xcd_local,
                            int atomic_walk, int max_gang, dash_schedule** out);
 
@@ -212,7 +215,7 @@ void dash_schedule_free(dash_schedule* s);
 int dash_schedule_choose(int mask, int N, int D, int g, int P, int* schedule, int* max_gang);
 
 /* Same for Nq query tiles and Nk key/value tiles: full mask -> SHIFT (gang of
- * Nk, capped at P); causal -> SYM_SHIFT when Nq = Nk is even, else DESC_Q. */
+ * min(Nq, Nk), capped at P); causal -> SYM_SHIFT when Nq is even, else DESC_Q. */
 int dash_schedule_choose_qk(int mask, int Nq, int Nk, int D, int g, int P, int* schedule, int* max_gang);
 
 /* ---- misc -------------------------------------------------------------- */

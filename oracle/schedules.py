@@ -30,6 +30,7 @@ Schedules ([summary] §2.2; [news] §2.3):
                formulas are this implementation's reading of that sentence.
 Gang schedules rank each dQ tile's contributors by their lock-step time key
 (position in the workgroup's list for that group), ties broken by kj.
+``build`` states how each schedule extends to Nq != Nk grids.
 
 Parity status: pinned by the four-tile example of [news] §2.3, the closed-form
 times of [news] §2.3, coverage/Latin/monotonicity properties ([summary]
@@ -103,14 +104,27 @@ def build(mask: int, sched: int, N: int, g: int, groups: int, P: int, xcd_local:
     """Per-workgroup step lists for ``groups`` kv groups of g query heads, N query
     tiles, Nk key/value tiles (default N), P workgroups.
 
-    With Nk != N the schedules generalise as follows: a serial or descending
-    chain of key/value tile kj walks the query tiles that see it; a shift gang
-    has Nk members and member p visits query tiles (p + t) mod N; symmetric
-    shift needs N == Nk.
+    With Nk != N the schedules generalise as follows (this implementation's
+    reading; the pages describe square grids only):
+    * serial / descending: the chain of key/value tile kj walks the query
+      tiles that see it.
+    * shift: a gang of min(N, Nk) members -- more would meet on a query tile
+      at the same step -- and the member holding key/value tile i visits
+      query tiles (i + t) mod N.  With Nk > N member p holds key/value tiles
+      p, p + N, p + 2N, ... one after another, which keeps the gang a Latin
+      rectangle: at every lock-step position its members sit on distinct
+      query tiles.
+    * symmetric shift (causal, N even, Nk >= N): the key/value tiles
+      0 .. R-1, R = Nk - N, see every query tile (a dense block); tiles
+      R .. Nk-1 with the N query tiles form the square causal triangle.  The
+      gang has N/2 members; member p first runs the square's tile pair
+      (R + p, R + N-1-p) exactly as in the square schedule, then the dense
+      key/value tiles p, p + N/2, p + N, ... each visiting query tiles
+      (tile + t) mod N.
 
-    ``max_gang`` > 0 caps a gang schedule's gang below its natural size (N for
-    shift, N/2 for symmetric shift); member p then takes the units (key/value
-    tiles, or tile pairs) p, p + gang, p + 2*gang, ... one after another.
+    ``max_gang`` > 0 caps a gang schedule's gang below its natural size;
+    member p then takes the units (key/value tiles, or tile pairs)
+    p, p + gang, p + 2*gang, ... one after another.
     """
     Nk = N if Nk is None else Nk
     if N < 1 or Nk < 1 or g < 1 or groups < 1 or P < 1:
@@ -134,14 +148,12 @@ def build(mask: int, sched: int, N: int, g: int, groups: int, P: int, xcd_local:
     if sched == SHIFT:
         if mask != FULL:
             raise ScheduleError("shift scheduling needs a full mask")
-        units = Nk
+        units = min(N, Nk)  # natural gang size; the gang holds all Nk key/value tiles
     elif sched == SYM_SHIFT:
         if mask != CAUSAL:
             raise ScheduleError("symmetric shift needs a causal mask")
         if N % 2:
             raise ScheduleError("symmetric shift needs an even tile count")
-        if Nk != N:
-            raise ScheduleError("symmetric shift needs as many key/value tiles as query tiles")
         units = N // 2
     else:
         raise ScheduleError(f"unknown schedule {sched}")
@@ -149,19 +161,25 @@ def build(mask: int, sched: int, N: int, g: int, groups: int, P: int, xcd_local:
     n_gangs = P // gang_size
     if n_gangs < 1:
         raise ScheduleError("gang larger than the workgroup count")
-    M = units
+    M = N // 2   # symmetric shift: tile pairs of the square causal part
+    R = Nk - N   # symmetric shift: dense key/value tiles in front of that square
     for grp in range(groups):
         gang = grp % n_gangs
         members = []  # per member: list of chains, each a list of (head, qi, kj)
         for p in range(gang_size):
             chains = []
-            for i in range(p, units, gang_size):
-                if sched == SHIFT:
+            if sched == SHIFT:
+                for i in range(p, Nk, gang_size):
                     chains.append(_chain(grp, g, i, [(i + t) % N for t in range(N)]))
-                else:
+            else:
+                for i in range(p, M, gang_size):
+                    # square part, local tile i: query tiles M..N-1 shifted, then i..M-1;
+                    # local tile N-1-i: query tiles N-1 down to N-1-i
                     a_walk = [M + (i + t) % M for t in range(M)] + [i + s for s in range(M - i)]
                     b_walk = [N - 1 - s + M - i for s in range(M - i, M + 1)]
-                    chains += [_chain(grp, g, i, a_walk), _chain(grp, g, N - 1 - i, b_walk)]
+                    chains += [_chain(grp, g, R + i, a_walk), _chain(grp, g, R + N - 1 - i, b_walk)]
+                for d in range(p, R, gang_size):
+                    chains.append(_chain(grp, g, d, [(d + t) % N for t in range(N)]))
             members.append(chains)
         # ordinal = rank of (time key, kj) among each dQ tile's contributors,
         # where the time key is the step's position in its member's list

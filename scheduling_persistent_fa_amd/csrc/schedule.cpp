@@ -8,12 +8,18 @@
 //            workgroup keeping key/value tile p visits query tiles
 //            p, p+1, ..., N-1, 0, ..., p-1, so the t-th contribution to every
 //            dQ tile arrives at step t and no two workgroups meet (§2.2.B).
-//            With Nq query and Nk key/value tiles: Nk members, member p
-//            visits query tiles (p + t) mod Nq.
+//            With Nq query and Nk key/value tiles: min(Nq, Nk) members (more
+//            would meet on a query tile); the member holding kv tile i visits
+//            query tiles (i + t) mod Nq, and with Nk > Nq member p holds kv
+//            tiles p, p + Nq, ... in turn.
 //  SYM_SHIFT causal mask: a gang of N/2 workgroups; member p keeps tile p
 //            through a dense rectangle phase (query tiles N/2..N-1, shifted)
 //            and its own triangle part, then tile N-1-p through the folded
 //            triangle, N+1 steps per member (§2.2.B, symmetric shift).
+//            With Nk > Nq (bottom-right causal) that runs on the square of kv
+//            tiles R..Nk-1, R = Nk - Nq; member p then takes the dense kv
+//            tiles p, p + N/2, ... < R, each visiting query tiles
+//            (tile + t) mod Nq.
 // Gang schedules order each dQ tile's contributions by lock-step time (the
 // step's position in its workgroup's list for that group), ties by kj.  A
 // gang may be capped below its natural size (N, or N/2): its members then
@@ -93,31 +99,37 @@ int gang_slot(int gi, int p, int n_gangs, int gang, const Schedule& s) {
 }
 
 std::string build_gang(const Schedule& s, std::vector<std::vector<StepRec>>& per_wg) {
-  const int N = s.Nq;  // query tiles (== Nk for symmetric shift)
-  // units: key/value tiles (shift) or tile pairs i, N-1-i (symmetric shift)
-  const int units = (s.walk == kShift) ? s.Nk : N / 2;
-  const int gang = (s.max_gang > 0 && s.max_gang < units) ? s.max_gang : units;
+  const int N = s.Nq;
+  const int M = N / 2;        // symmetric shift: tile pairs of the square causal part
+  const int R = s.Nk - s.Nq;  // symmetric shift: dense kv tiles in front of that square
+  // natural gang: one member per key/value tile up to one per query tile
+  // (shift), one per tile pair (symmetric shift)
+  const int natural = (s.walk == kShift) ? std::min(s.Nk, N) : M;
+  const int gang = (s.max_gang > 0 && s.max_gang < natural) ? s.max_gang : natural;
   const int n_gangs = s.P / gang;
   if (n_gangs < 1) return "gang of " + std::to_string(gang) + " workgroups exceeds " + std::to_string(s.P);
-  // Per member: its chains as (kj, walk of one head).  A capped gang runs
-  // its units in rounds: member p keeps units p, p + gang, p + 2*gang, ...
+  // Per member: its chains as (kj, walk of one head), units taken in rounds:
+  // member p keeps units p, p + gang, p + 2*gang, ...
   std::vector<std::vector<std::pair<int, std::vector<int>>>> member(gang);
+  auto shifted = [N](int kj) {
+    std::vector<int> w(N);
+    for (int t = 0; t < N; ++t) w[t] = (kj + t) % N;
+    return std::make_pair(kj, std::move(w));
+  };
   for (int p = 0; p < gang; ++p) {
-    for (int i = p; i < units; i += gang) {
-      if (s.walk == kShift) {
-        std::vector<int> w(N);
-        for (int t = 0; t < N; ++t) w[t] = (i + t) % N;
-        member[p].push_back({i, std::move(w)});
-      } else {
-        const int M = units;
-        std::vector<int> a, b;
-        for (int t = 0; t < M; ++t) a.push_back(M + (i + t) % M);   // dense rectangle
-        for (int q = i; q < M; ++q) a.push_back(q);                  // own triangle part
-        for (int q = N - 1; q >= N - 1 - i; --q) b.push_back(q);     // folded triangle
-        member[p].push_back({i, std::move(a)});
-        member[p].push_back({N - 1 - i, std::move(b)});
-      }
+    if (s.walk == kShift) {
+      for (int i = p; i < s.Nk; i += gang) member[p].push_back(shifted(i));
+      continue;
     }
+    for (int i = p; i < M; i += gang) {
+      std::vector<int> a, b;
+      for (int t = 0; t < M; ++t) a.push_back(M + (i + t) % M);   // dense rectangle
+      for (int q = i; q < M; ++q) a.push_back(q);                  // own triangle part
+      for (int q = N - 1; q >= N - 1 - i; --q) b.push_back(q);     // folded triangle
+      member[p].push_back({R + i, std::move(a)});
+      member[p].push_back({R + N - 1 - i, std::move(b)});
+    }
+    for (int d = p; d < R; d += gang) member[p].push_back(shifted(d));
   }
   // Ordinals: rank of (position, kj) among the contributors of each
   // (head-in-group u, qi).  Identical for every group, so computed once.
@@ -168,11 +180,11 @@ std::string choose_schedule(int mask, int Nq, int Nk, int D, int g, int P, int* 
   // for every shape tried, whatever D and g; D and g are kept in the key.
   (void)D;
   (void)g;
-  int units = 0;
+  int units = 0;  // natural gang size
   if (mask == kMaskFull) {
     *kind = kShift;
-    units = Nk;
-  } else if (N % 2 == 0 && Nk == Nq) {
+    units = std::min(Nq, Nk);
+  } else if (N % 2 == 0) {
     *kind = kSymShift;
     units = N / 2;
   } else {
@@ -197,7 +209,6 @@ std::string build_schedule(int mask, int kind, int Nq, int Nk, int g, int groups
   if (walk == kShift && mask != kMaskFull) return "shift scheduling needs a full mask";
   if (walk == kSymShift && mask != kMaskCausal) return "symmetric shift needs a causal mask";
   if (walk == kSymShift && (Nq % 2)) return "symmetric shift needs an even tile count";
-  if (walk == kSymShift && Nk != Nq) return "symmetric shift needs as many key/value tiles as query tiles";
   Schedule s;
   s.mask = mask;
   s.kind = kind;

@@ -181,7 +181,7 @@ def test_rectangular_shapes_match_oracle(case):
     torch.cuda.synchronize()
     assert rel_err(to_f64(o), ref["o"]) <= TOL
     assert np.abs(to_f64(lse) - ref["lse"]).max() <= TOL * max(1.0, np.abs(ref["lse"]).max())
-    scheds = [SERIAL, DESC_Q] + ([] if causal else [SHIFT]) + [ATOMIC, AUTO]
+    scheds = [SERIAL, DESC_Q] + ([SYM_SHIFT] if causal else [SHIFT]) + [ATOMIC, AUTO]
     for sched in scheds:
         say(f"  schedule {_lib.SCHEDULE_NAMES[sched]}")
         opts = make_opts(tile=tile, sync_check=True)

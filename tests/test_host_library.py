@@ -164,6 +164,8 @@ RECT_CASES = [  # mask, sched, Nq, Nk, g, groups, P, cap
     (Sch.FULL, Sch.SHIFT, 4, 6, 1, 2, 12, 0), (Sch.FULL, Sch.SHIFT, 6, 4, 2, 3, 8, 0),
     (Sch.CAUSAL, Sch.SERIAL, 3, 7, 1, 2, 6, 0), (Sch.CAUSAL, Sch.DESC_Q, 4, 9, 2, 2, 5, 0),
     (Sch.FULL, Sch.SHIFT, 8, 32, 1, 16, 256, 0), (Sch.FULL, Sch.SHIFT, 16, 40, 1, 3, 64, 16),
+    (Sch.CAUSAL, Sch.SYM_SHIFT, 4, 10, 2, 3, 8, 0), (Sch.CAUSAL, Sch.SYM_SHIFT, 8, 32, 1, 16, 256, 0),
+    (Sch.CAUSAL, Sch.SYM_SHIFT, 6, 11, 1, 2, 5, 2), (Sch.FULL, Sch.SHIFT, 5, 13, 2, 2, 9, 0),
 ]
 
 
@@ -178,7 +180,8 @@ def test_rectangular_schedules_match_oracle_exactly(mask, sched, Nq, Nk, g, grou
 
 
 def test_rectangular_rejections():
-    for args in [(Sch.CAUSAL, Sch.SERIAL, 5, 4), (Sch.CAUSAL, Sch.SYM_SHIFT, 4, 6), (Sch.CAUSAL, Sch.SHIFT, 4, 6)]:
+    for args in [(Sch.CAUSAL, Sch.SERIAL, 5, 4), (Sch.CAUSAL, Sch.SYM_SHIFT, 5, 6), (Sch.CAUSAL, Sch.SHIFT, 4, 6),
+                 (Sch.CAUSAL, Sch.SYM_SHIFT, 6, 4)]:
         mask, sched, nq, nk = args
         with pytest.raises(_lib.DashError):
             Schedule(mask, sched, nq, 1, 1, 16, Nk=nk)
@@ -187,8 +190,10 @@ def test_rectangular_rejections():
 def test_adaptive_choice_on_rectangles():
     from scheduling_persistent_fa_amd.schedule import choose
     assert choose(Sch.FULL, 16, 128, 1, 256, Nk=64) == (_lib.SHIFT, 0)
-    assert choose(Sch.FULL, 16, 128, 1, 256, Nk=300) == (_lib.SHIFT, 256)   # gang of Nk capped to the grid
-    assert choose(Sch.CAUSAL, 16, 128, 1, 256, Nk=64) == (_lib.DESC_Q, 0)   # no symmetric shift on rectangles
+    assert choose(Sch.FULL, 16, 128, 1, 256, Nk=300) == (_lib.SHIFT, 0)     # gang of min(Nq, Nk) = 16
+    assert choose(Sch.FULL, 400, 128, 1, 256, Nk=300) == (_lib.SHIFT, 256)  # gang of 300 capped to the grid
+    assert choose(Sch.CAUSAL, 16, 128, 1, 256, Nk=64) == (_lib.SYM_SHIFT, 0)
+    assert choose(Sch.CAUSAL, 15, 128, 1, 256, Nk=64) == (_lib.DESC_Q, 0)   # odd Nq: no tile pairs
     assert choose(Sch.CAUSAL, 16, 128, 1, 256, Nk=16) == (_lib.SYM_SHIFT, 0)
     with pytest.raises(_lib.DashError):
         choose(Sch.CAUSAL, 16, 128, 1, 256, Nk=8)

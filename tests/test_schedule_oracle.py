@@ -207,16 +207,42 @@ def test_shift_placement_keeps_runs_of_16_members_on_one_chiplet():
 
 
 @pytest.mark.parametrize("mask,sched", [(FULL, SERIAL), (FULL, DESC_Q), (FULL, SHIFT), (CAUSAL, SERIAL),
-                                        (CAUSAL, DESC_Q)])
+                                        (CAUSAL, DESC_Q), (CAUSAL, SYM_SHIFT)])
 def test_rectangular_schedules_valid_exhaustively(mask, sched):
-    # Every Nq x Nk grid up to 6 x 6 (causal: Nk >= Nq), two groups, several grid sizes.
+    # Every Nq x Nk grid up to 6 x 8 (causal: Nk >= Nq; symmetric shift: Nq
+    # even), two groups, several grid sizes and gang caps.
     for nq in range(1, 7):
-        for nk in range(1, 7):
+        if sched == SYM_SHIFT and nq % 2:
+            continue
+        for nk in range(1, 9):
             if mask == CAUSAL and nk < nq:
                 continue
-            for P in {max(1, nk if sched == SHIFT else 1), nk + 3, 2 * nk}:
-                lists = Sch.build(mask, sched, nq, 2, 2, P, Nk=nk)
-                Sch.validate(lists, mask, nq, 2, 2, Nk=nk)
+            gang = min(nq, nk) if sched == SHIFT else (nq // 2 if sched == SYM_SHIFT else 1)
+            for P in {gang, nk + 3, 2 * nk}:
+                for cap in (0, 1, 2):
+                    lists = Sch.build(mask, sched, nq, 2, 2, P, Nk=nk, max_gang=cap)
+                    Sch.validate(lists, mask, nq, 2, 2, Nk=nk)
+
+
+@pytest.mark.parametrize("mask,sched,nq,nk", [(FULL, SHIFT, 5, 13), (FULL, SHIFT, 8, 24), (FULL, SHIFT, 7, 3),
+                                              (CAUSAL, SYM_SHIFT, 6, 15), (CAUSAL, SYM_SHIFT, 8, 24),
+                                              (CAUSAL, SYM_SHIFT, 8, 8)])
+def test_rectangular_gangs_never_meet_on_a_query_tile(mask, sched, nq, nk):
+    # Latin property of the uncapped gangs: at every lock-step position the
+    # members of a gang sit on distinct query tiles, so in the unit-cost DAG
+    # model no step waits for another member (zero total wait).
+    P = min(nq, nk) if sched == SHIFT else nq // 2
+    lists = Sch.build(mask, sched, nq, 1, 1, P, Nk=nk)
+    Sch.validate(lists, mask, nq, 1, 1, Nk=nk)
+    longest = max(len(l) for l in lists)
+    for t in range(longest):
+        at_t = [l[t].qi for l in lists if t < len(l)]
+        assert len(at_t) == len(set(at_t)), (t, at_t)
+    _, wait = Sch.simulate(lists, 1.0, 0.0)
+    assert wait == 0.0
+    # every visible (qi, kj) pair once
+    pairs = {(s.qi, s.kj) for l in lists for s in l}
+    assert len(pairs) == sum(len(l) for l in lists)
 
 
 def test_rectangular_shift_contributions_are_one_per_step_when_nk_le_nq():
