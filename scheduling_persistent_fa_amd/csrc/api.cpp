@@ -85,16 +85,19 @@ struct WsLayout {
   size_t ws_dq, delta, sem, err, dummy, total;
 };
 
-WsLayout ws_layout(int B, int Hq, int S, int D) {
+// Sq query rows per head; Sw (a multiple of 64) workspace rows per head, the
+// query tiles' virtual rows (see TileGrid).
+WsLayout ws_layout(int B, int Hq, int Sq, int Sw, int D) {
   WsLayout L;
-  const size_t rows = (size_t)B * Hq * S;
+  const size_t rows = (size_t)B * Hq * Sq;
+  const size_t wrows = (size_t)B * Hq * Sw;
   size_t off = 0;
   L.ws_dq = off;
-  off = align256(off + rows * D * sizeof(float));
+  off = align256(off + wrows * D * sizeof(float));
   L.delta = off;
   off = align256(off + rows * sizeof(float));
   L.sem = off;
-  off = align256(off + (size_t)B * Hq * (S / 64) * kSemWordsPerBlock * sizeof(int));
+  off = align256(off + (size_t)B * Hq * (Sw / 64) * kSemWordsPerBlock * sizeof(int));
   L.err = off;
   off = align256(off + 16);
   L.dummy = off;  // 8 dQ tiles' worth of scratch for writes with no destination
@@ -103,20 +106,58 @@ WsLayout ws_layout(int B, int Hq, int S, int D) {
   return L;
 }
 
-int check_common(const void* const* ptrs, int nptr, int B, int Hq, int Hkv, int Sq, int Sk, int D, int mask) {
-  for (int i = 0; i < nptr; ++i) {
-    if (!ptrs[i]) return fail(DASH_ERR_INVALID_ARG, "null tensor pointer (argument " + std::to_string(i) + ")");
-    if (reinterpret_cast<uintptr_t>(ptrs[i]) % 16) return fail(DASH_ERR_INVALID_ARG, "tensor pointer not 16-byte aligned");
-  }
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Sk <= 0 || D <= 0) return fail(DASH_ERR_INVALID_ARG, "sizes must be positive");
+// Returned by check_sizes when there are no query rows (B = 0 or Sq = 0).
+constexpr int kEmpty = 1;
+
+int check_sizes(int B, int Hq, int Hkv, int Sq, int Sk, int D, int mask) {
+  if (B < 0 || Sq < 0 || Sk < 0) return fail(DASH_ERR_INVALID_ARG, "sizes must not be negative");
+  if (Hq <= 0 || Hkv <= 0 || D <= 0) return fail(DASH_ERR_INVALID_ARG, "head counts and head dimension must be positive");
   if (Hq % Hkv) return fail(DASH_ERR_INVALID_ARG, "Hq must be a multiple of Hkv");
   if (mask != DASH_MASK_FULL && mask != DASH_MASK_CAUSAL) return fail(DASH_ERR_INVALID_ARG, "unknown mask");
   if (mask == DASH_MASK_CAUSAL && Sk < Sq)
     return fail(DASH_ERR_INVALID_ARG, "a causal mask needs Sk >= Sq (it is aligned at the bottom right)");
   if (D != 64 && D != 128) return fail(DASH_ERR_UNSUPPORTED, "head dimension must be 64 or 128");
-  if (Sq % 64 || Sk % 64) return fail(DASH_ERR_UNSUPPORTED, "sequence lengths must be multiples of 64");
-  if ((long long)B * Hq * std::max(Sq, Sk) * D >= (1LL << 40)) return fail(DASH_ERR_UNSUPPORTED, "problem too large");
+  if ((long long)B * Hq * (std::max(Sq, Sk) + 256LL) * D >= (1LL << 40))
+    return fail(DASH_ERR_UNSUPPORTED, "problem too large");
+  if (B == 0 || Sq == 0) return kEmpty;
+  if (Sk == 0) return fail(DASH_ERR_INVALID_ARG, "no keys: the softmax of an empty row is undefined");
   return DASH_OK;
+}
+
+int check_ptrs(const void* const* ptrs, int nptr) {
+  for (int i = 0; i < nptr; ++i) {
+    if (!ptrs[i]) return fail(DASH_ERR_INVALID_ARG, "null tensor pointer (argument " + std::to_string(i) + ")");
+    if (reinterpret_cast<uintptr_t>(ptrs[i]) % 16) return fail(DASH_ERR_INVALID_ARG, "tensor pointer not 16-byte aligned");
+  }
+  return DASH_OK;
+}
+
+// Tile grid of one backward call.  Key/value tiles: Nk = ceil(Sk / T), the
+// last one possibly partial.  Query tiles cover virtual rows, virtual row =
+// query row + qshift.  Full mask: qshift = 0, Nq = ceil(Sq / T).  Causal
+// (bottom right, offset Sk - Sq = diag_off * T + qshift): the query tiles
+// are aligned with the key/value tiles, so query tile qi meets the diagonal
+// in key/value tile qi + diag_off exactly as in the square case, and
+// Nq = Nk - diag_off (the first tile starts qshift rows before row 0).
+struct TileGrid {
+  int T, Nq, Nk, qshift, diag_off, Sw;
+};
+
+TileGrid tile_grid(int Sq, int Sk, int T, int mask) {
+  TileGrid t;
+  t.T = T;
+  t.Nk = (Sk + T - 1) / T;
+  if (mask == DASH_MASK_CAUSAL) {
+    t.diag_off = (Sk - Sq) / T;
+    t.qshift = (Sk - Sq) % T;
+    t.Nq = t.Nk - t.diag_off;
+  } else {
+    t.diag_off = 0;
+    t.qshift = 0;
+    t.Nq = (Sq + T - 1) / T;
+  }
+  t.Sw = t.Nq * T;
+  return t;
 }
 
 float default_scale(float s, int D) { return s > 0.f ? s : 1.0f / std::sqrt((float)D); }
@@ -208,7 +249,10 @@ int dash_schedule_choose(int mask, int N, int D, int g, int P, int* schedule, in
 int dash_attn_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
                      int Sq, int Sk, int D, float softmax_scale, int mask, void* stream) {
   const void* ptrs[] = {q, k, v, o, lse};
-  int st = check_common(ptrs, 5, B, Hq, Hkv, Sq, Sk, D, mask);
+  int st = check_sizes(B, Hq, Hkv, Sq, Sk, D, mask);
+  if (st == kEmpty) return DASH_OK;  // no query rows: nothing to write
+  if (st) return st;
+  st = check_ptrs(ptrs, 5);
   if (st) return st;
   if ((long long)B * Hq > 65535) return fail(DASH_ERR_UNSUPPORTED, "B*Hq exceeds the grid limit");
   hipError_t e = dash::launch_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, default_scale(softmax_scale, D), mask,
@@ -223,14 +267,18 @@ int dash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
 
 int dash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D, size_t* bytes) {
   if (!bytes) return fail(DASH_ERR_INVALID_ARG, "null output");
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || D <= 0) return fail(DASH_ERR_INVALID_ARG, "sizes must be positive");
-  *bytes = ws_layout(B, Hq, S, D).total;
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || S < 0 || D <= 0) return fail(DASH_ERR_INVALID_ARG, "sizes must not be negative");
+  // Any key length and tile: at most round_up(S, T) + T virtual rows per head.
+  *bytes = ws_layout(B, Hq, S, ((S + 127) / 128) * 128 + 128, D).total;
   return DASH_OK;
 }
 
 int dash_attn_bwd_delta(const void* o, const void* dO, float* delta, int B, int H, int S, int D, void* stream) {
   const void* ptrs[] = {o, dO, delta};
-  int st = check_common(ptrs, 3, B, H, H, S, S, D, DASH_MASK_FULL);
+  int st = check_sizes(B, H, H, S, S, D, DASH_MASK_FULL);
+  if (st == kEmpty) return DASH_OK;
+  if (st) return st;
+  st = check_ptrs(ptrs, 3);
   if (st) return st;
   hipError_t e = dash::launch_delta(o, dO, delta, (long long)B * H * S, D, nullptr, 0, nullptr, 0, (hipStream_t)stream);
   return e == hipSuccess ? DASH_OK : hip_fail(e, "delta launch");
@@ -247,9 +295,23 @@ int dash_attn_bwd_qk(const void* q, const void* k, const void* v, const void* o,
                      void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk, int D, float softmax_scale,
                      int mask, int schedule, const dash_bwd_opts* opts, void* stream) {
   const void* ptrs[] = {q, k, v, o, dO, lse, dq, dk, dv};
-  int st = check_common(ptrs, 9, B, Hq, Hkv, Sq, Sk, D, mask);
-  if (st) return st;
+  int st = check_sizes(B, Hq, Hkv, Sq, Sk, D, mask);
+  if (st != DASH_OK && st != kEmpty) return st;
   if (schedule < DASH_SCHED_SERIAL || schedule > DASH_SCHED_AUTO) return fail(DASH_ERR_INVALID_ARG, "unknown schedule");
+  if (st == kEmpty) {
+    // No query rows: dQ is empty and dK = dV = 0 (no key receives any gradient).
+    const long long kv_words = (long long)B * Hkv * Sk * D / 2;  // bf16 pairs
+    if (kv_words == 0) return DASH_OK;
+    const void* kv_ptrs[] = {dk, dv};
+    st = check_ptrs(kv_ptrs, 2);
+    if (st) return st;
+    hipError_t e = dash::launch_delta(nullptr, nullptr, nullptr, 0, D, (int*)dk, kv_words, nullptr, 0, (hipStream_t)stream);
+    if (e == hipSuccess)
+      e = dash::launch_delta(nullptr, nullptr, nullptr, 0, D, (int*)dv, kv_words, nullptr, 0, (hipStream_t)stream);
+    return e == hipSuccess ? DASH_OK : hip_fail(e, "zero-fill launch");
+  }
+  st = check_ptrs(ptrs, 9);
+  if (st) return st;
   dash_bwd_opts op;
   std::memset(&op, 0, sizeof(op));
   if (opts) {
@@ -267,8 +329,8 @@ int dash_attn_bwd_qk(const void* q, const void* k, const void* v, const void* o,
 
   const int T = op.tile ? op.tile : (std::min(Sq, Sk) < 512 ? 64 : 128);
   if (T != 64 && T != 128) return fail(DASH_ERR_UNSUPPORTED, "tile must be 64 or 128");
-  if (Sq % T || Sk % T) return fail(DASH_ERR_UNSUPPORTED, "sequence lengths must be multiples of the tile");
-  const int Nq = Sq / T, Nk = Sk / T;
+  const TileGrid tg = tile_grid(Sq, Sk, T, mask);
+  const int Nq = tg.Nq, Nk = tg.Nk;
   const int P = op.num_workgroups > 0 ? op.num_workgroups : di.num_cu;
   if (op.num_workgroups < 0) return fail(DASH_ERR_INVALID_ARG, "negative workgroup count");
   if (op.max_gang < 0) return fail(DASH_ERR_INVALID_ARG, "negative gang cap");
@@ -321,7 +383,7 @@ int dash_attn_bwd_qk(const void* q, const void* k, const void* v, const void* o,
   }
 
   // Workspace.
-  const WsLayout L = ws_layout(B, Hq, Sq, D);
+  const WsLayout L = ws_layout(B, Hq, Sq, tg.Sw, D);
   char* ws = nullptr;
   if (op.workspace) {
     if (reinterpret_cast<uintptr_t>(op.workspace) % 256) return fail(DASH_ERR_WORKSPACE, "workspace not 256-byte aligned");
@@ -352,7 +414,8 @@ int dash_attn_bwd_qk(const void* q, const void* k, const void* v, const void* o,
   const long long rows = (long long)B * Hq * Sq;
   const long long n_sem = (long long)((L.err - L.sem) / 4) + 4;  // semaphores, padding and the error word
 
-  e = dash::launch_delta(o, dO, delta, rows, D, sem, n_sem, atomic ? ws_dq : nullptr, atomic ? rows * D : 0, strm);
+  const long long ws_elems = (long long)B * Hq * tg.Sw * D;
+  e = dash::launch_delta(o, dO, delta, rows, D, sem, n_sem, atomic ? ws_dq : nullptr, atomic ? ws_elems : 0, strm);
   if (e != hipSuccess) return hip_fail(e, "preprocess launch");
 
   dash::BwdLaunch bl;
@@ -382,6 +445,9 @@ int dash_attn_bwd_qk(const void* q, const void* k, const void* v, const void* o,
   bl.T = T;
   bl.g = g;
   bl.causal = mask;
+  bl.qshift = tg.qshift;
+  bl.nblk = tg.Sw / 64;
+  bl.diag_off = tg.diag_off;
   bl.P = P;
   bl.atomic = atomic;
   if (op.event_start) {
@@ -394,7 +460,7 @@ int dash_attn_bwd_qk(const void* q, const void* k, const void* v, const void* o,
     e = hipEventRecord((hipEvent_t)op.event_stop, strm);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord(stop)");
   }
-  e = dash::launch_dq_finalize(ws_dq, dq, rows * D, D, scale, atomic, strm);
+  e = dash::launch_dq_finalize(ws_dq, dq, ws_elems, D, scale, atomic, tg.Sw / 64, tg.qshift, Sq, strm);
   if (e != hipSuccess) return hip_fail(e, "finalize launch");
 
   if (op.sync_check) {

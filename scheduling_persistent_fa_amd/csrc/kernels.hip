@@ -135,7 +135,8 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const __bf16* __restric
   const int head = blockIdx.y;  // b * Hq + hq
   const int kvh = head / g;
   const int q_base = blockIdx.x * 32 * NW;
-  const int q_row = q_base + 32 * w + c32;  // this lane's query row
+  const int q_row = q_base + 32 * w + c32;  // this lane's query row (past Sq on a ragged last block)
+  const int q_ld = min(q_row, Sq - 1);      // rows past Sq read a valid row and are not stored
   const __bf16* qh = q + (size_t)head * Sq * D;
   const __bf16* kh = k + (size_t)kvh * Sk * D;
   const __bf16* vh = v + (size_t)kvh * Sk * D;
@@ -143,17 +144,20 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const __bf16* __restric
 
   bf16x8 qb[DC];
 #pragma unroll
-  for (int c = 0; c < DC; ++c) qb[c] = *(const bf16x8*)(qh + (size_t)q_row * D + 16 * c + 8 * h2);
+  for (int c = 0; c < DC; ++c) qb[c] = *(const bf16x8*)(qh + (size_t)q_ld * D + 16 * c + 8 * h2);
 
-  const int n_tiles = causal ? (q_base + 32 * NW - 1 + off) / KVT + 1 : Sk / KVT;
+  // Key/value tiles of 64 rows; the last one may be partial (rows past Sk
+  // read row Sk - 1 and are masked out of the softmax).
+  const int kv_tiles = (Sk + KVT - 1) / KVT;
+  const int n_tiles = causal ? min(kv_tiles, (q_base + 32 * NW - 1 + off) / KVT + 1) : kv_tiles;
 
   bf16x8 pk[CPT], pv[CPT];
   auto load_tile = [&](int t) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int ch = threadIdx.x + i * NT, row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-      pk[i] = *(const bf16x8*)(kh + (size_t)(t * KVT + row) * D + col);
-      pv[i] = *(const bf16x8*)(vh + (size_t)(t * KVT + row) * D + col);
+      const int ch = threadIdx.x + i * NT, row = min(t * KVT + ch / (D / 8), Sk - 1), col = (ch % (D / 8)) * 8;
+      pk[i] = *(const bf16x8*)(kh + (size_t)row * D + col);
+      pv[i] = *(const bf16x8*)(vh + (size_t)row * D + col);
     }
   };
   auto store_tile = [&](int buf) {
@@ -186,14 +190,15 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const __bf16* __restric
       for (int c = 0; c < DC; ++c) s[kb] = mfma32(lds_row8(sk + (kb * 32 + c32) * PITCH + (16 * c + 8 * h2) * 2), qb[c], s[kb]);
     }
     float mt = -INFINITY;
+    const bool tail = (t + 1) * KVT > Sk;  // the ragged last tile
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float x = s[kb][r] * scale_log2;
-        if (causal) {
+        if (causal || tail) {
           const int kv = t * KVT + kb * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-          if (kv > q_row + off) x = -INFINITY;
+          if ((causal && kv > q_row + off) || kv >= Sk) x = -INFINITY;
         }
         s[kb][r] = x;
         mt = fmaxf(mt, x);
@@ -232,6 +237,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const __bf16* __restric
   }
   const float l_tot = l_part + __shfl_xor(l_part, 32);
   const float inv = 1.f / l_tot;
+  if (q_row >= Sq) return;
   __bf16* oh = o + (size_t)head * Sq * D + (size_t)q_row * D;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -299,7 +305,18 @@ __global__ __launch_bounds__(256) void delta_kernel(const __bf16* __restrict__ o
 // over all 64 query rows.  The 2*D/32 C tiles of the block's dQ partial are
 // spread over the waves.
 //
-// Workspace dQ layout: per (query head, 64-row block) a 64 x D fp32 block
+// Ragged lengths.  Query tile qi covers the virtual rows qi*T .. qi*T+T-1,
+// virtual row = query row + qshift; qshift > 0 only for a causal mask whose
+// offset Sk - Sq is not a multiple of T, and it aligns the query tiles with
+// the key/value tiles so that the diagonal crosses tile pair
+// (qi, qi + diag_off) at the same local positions as in the square case.
+// Virtual rows outside 0 .. Sq-1 read a valid row and get LSE = +inf, so
+// their P, dS and every contribution they make are exactly zero.  Key/value
+// rows past Sk in the last tile read row Sk - 1 and are masked out of P like
+// the upper triangle of a diagonal tile; their dK/dV rows go to the dummy
+// tiles.
+//
+// Workspace dQ layout: per (query head, 64-row block of virtual rows) a 64 x D fp32 block
 // stored as 32 x 32 MFMA C tiles (tile = qb * D/32 + db).  The deterministic
 // schedules keep a tile as [register / 4][lane][register % 4], so one wave
 // access is a 16-byte-per-lane, 1 KiB contiguous transfer; the atomic variant
@@ -341,6 +358,9 @@ struct BwdArgs {
   float scale;       // softmax scale
   float scale_log2;  // softmax scale * log2(e)
   int Sq, Sk, g, causal;
+  int qshift;        // virtual query row = query row + qshift
+  int nblk;          // 64-row workspace blocks per query head (virtual rows / 64)
+  int diag_off;      // causal: tile pair (qi, qi + diag_off) straddles the diagonal
 };
 
 // Semaphore words per 64-row dQ block: one per wave that holds dQ tiles.
@@ -400,8 +420,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
   const int wg = blockIdx.x;
   const int beg = offsets[wg], end = offsets[wg + 1];
   const int Sq = a.Sq, Sk = a.Sk, g = a.g;
-  const int nblk = Sq / M;  // 64-row blocks per head
-  const int diag_off = (Sk - Sq) / T;  // causal: tile pair (qi, qi + diag_off) straddles the diagonal
+  const int nblk = a.nblk, diag_off = a.diag_off, qshift = a.qshift;
   unsigned long long stall = 0;
   const unsigned long long t_start = __builtin_amdgcn_s_memtime();
   if (threadIdx.x == 0) *s_flag = 0;
@@ -422,17 +441,23 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
   float pstat = 0.f;
   const int st_tid = threadIdx.x < 2 * M ? threadIdx.x : 0;
   const float st_mul = st_tid < M ? kLog2e : 1.f;
-  auto load_block = [&](int head, int row0) {
-    const __bf16* qh = a.q + ((size_t)head * Sq + row0) * D;
-    const __bf16* doh = a.dO + ((size_t)head * Sq + row0) * D;
+  auto load_block = [&](int head, int vrow0) {  // vrow0: first virtual row of the block
+    const __bf16* qh = a.q + (size_t)head * Sq * D;
+    const __bf16* doh = a.dO + (size_t)head * Sq * D;
+    const int row0 = vrow0 - qshift;
 #pragma unroll
     for (int i = 0; i < QCH; ++i) {
       const int ch = threadIdx.x + i * NT;
-      pq[i] = *(const bf16x8*)(qh + (size_t)ch * 8);
-      pdo[i] = *(const bf16x8*)(doh + (size_t)ch * 8);
+      const int row = min(max(row0 + ch / (D / 8), 0), Sq - 1);
+      const size_t e = (size_t)row * D + (ch % (D / 8)) * 8;
+      pq[i] = *(const bf16x8*)(qh + e);
+      pdo[i] = *(const bf16x8*)(doh + e);
     }
+    const int srow = row0 + (st_tid & (M - 1));
+    const bool valid = srow >= 0 && srow < Sq;
     const float* src = st_tid < M ? a.lse : a.delta;
-    pstat = src[(size_t)head * Sq + row0 + (st_tid & (M - 1))];
+    const float x = src[(size_t)head * Sq + min(max(srow, 0), Sq - 1)];
+    pstat = valid ? x : (st_tid < M ? INFINITY : 0.f);  // LSE = +inf: P = 0 on rows outside the sequence
   };
   auto store_block = [&](int buf) {
 #pragma unroll
@@ -453,14 +478,20 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
     const size_t o_lane = (size_t)opaque((kv0 + 4 * h2) * D + hf * DH * 32 + c32);
     __bf16* dkh = a.dk + ((size_t)kvh_ * Sk + (size_t)kj_ * T) * D + o_lane;
     __bf16* dvh = a.dv + ((size_t)kvh_ * Sk + (size_t)kj_ * T) * D + o_lane;
+    __bf16* sink = (__bf16*)a.dummy + o_lane;  // rows past Sk (same offsets, 32 KiB)
+    const int kv_valid = Sk - kj_ * T;
 #pragma unroll
-    for (int j = 0; j < DH; ++j)
+    for (int r = 0; r < 16; ++r) {
+      const bool ok = kv0 + 4 * h2 + 8 * (r >> 2) + (r & 3) < kv_valid;
+      __bf16* pk = ok ? dkh : sink;
+      __bf16* pv = ok ? dvh : sink;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
+      for (int j = 0; j < DH; ++j) {
         const int off = (8 * (r >> 2) + (r & 3)) * D + j * 32;
-        dkh[off] = (__bf16)(dk_acc[j][r] * a.scale);
-        dvh[off] = (__bf16)dv_acc[j][r];
+        pk[off] = (__bf16)(dk_acc[j][r] * a.scale);
+        pv[off] = (__bf16)dv_acc[j][r];
       }
+    }
   };
   int buf = 0;
   // dQ read-modify-write pipelined by one sub-step (deterministic schedules):
@@ -495,16 +526,17 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
     const int kvh = head / g;
     const __bf16* kh = a.k + ((size_t)kvh * Sk + (size_t)kj * T) * D;
     const __bf16* vh = a.v + ((size_t)kvh * Sk + (size_t)kj * T) * D;
+    const int kv_valid = Sk - kj * T;  // key/value rows of this tile inside the sequence (>= T but on the last)
     if (first) {
       // New chain: its V rows to registers and its K tile to LDS.  The previous
       // chain's dK/dV are written only after that, so that waiting for these
       // loads never waits for those writes to drain.
 #pragma unroll
-      for (int c = 0; c < DC; ++c) vb[c] = *(const bf16x8*)(vh + (size_t)kv_local * D + 16 * c + 8 * h2);
+      for (int c = 0; c < DC; ++c) vb[c] = *(const bf16x8*)(vh + (size_t)min(kv_local, kv_valid - 1) * D + 16 * c + 8 * h2);
       bf16x8 kt[KCH];
 #pragma unroll
       for (int u = 0; u < KCH; ++u) {
-        const int ch = threadIdx.x + u * NT, row = ch / (D / 8), col = (ch % (D / 8)) * 8;
+        const int ch = threadIdx.x + u * NT, row = min(ch / (D / 8), kv_valid - 1), col = (ch % (D / 8)) * 8;
         kt[u] = *(const bf16x8*)(kh + (size_t)row * D + col);
       }
       __syncthreads();  // previous chain's dQ contraction is done with sK
@@ -522,6 +554,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
       }
     }
     const bool diag = a.causal && (kj == qi + diag_off);
+    const bool mask_on = diag || kv_valid < T;  // a diagonal tile, or the ragged last key/value tile
 
     for (int sub = 0; sub < SUBS; ++sub) {
       __syncthreads();  // B1: Q/dO/LSE/Delta of this block (and sK) visible; P^T, dS^T free
@@ -566,9 +599,12 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
           }
         }
         // P = exp2(S*scale*log2e - LSE*log2e); dS = P * (dP - Delta); both to LDS transposed.
-        // On a diagonal tile P is zero where key/value row > query row; the bound is made
-        // opaque so that the comparisons are formed here rather than kept live across the loop.
-        int kv_minus_q = kv_local - (sub * M + 32 * hf + 4 * h2);
+        // Under mask_on, P is zero where thr > 8j + e: on a diagonal tile where key/value
+        // row > query row, and in every row of a key/value column past Sk.  The bound is
+        // made opaque so that the comparisons are formed here rather than kept live
+        // across the loop.
+        int kv_minus_q = diag ? kv_local - (sub * M + 32 * hf + 4 * h2) : -(1 << 20);
+        if (kv_local >= kv_valid) kv_minus_q = 1 << 20;
         asm volatile("" : "+v"(kv_minus_q));
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -579,7 +615,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * j + e;
             float p = __builtin_amdgcn_exp2f(s[r] * a.scale_log2 - l4[e]);
-            if (diag && kv_minus_q > 8 * j + e) p = 0.f;
+            if (mask_on && kv_minus_q > 8 * j + e) p = 0.f;
             tp[e] = (__bf16)p;
             ts[e] = (__bf16)(p * (dp[r] - d4[e]));
           }
@@ -771,20 +807,24 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
 // dQ = bf16(scale * workspace), undoing the fragment order.  One thread per
 // (block, tile, register group of four, lane): four rows of one column.
 // Deterministic layout (X4): tile as [register / 4][lane][register % 4]; the
-// atomic layout: tile as [register][lane].
+// atomic layout: tile as [register][lane].  Workspace blocks hold virtual
+// rows (query row + qshift, nblk blocks per head); rows outside 0 .. Sq-1
+// are not written.
 template <int D, bool X4>
 __global__ __launch_bounds__(256) void dq_finalize_kernel(const float* __restrict__ ws, __bf16* __restrict__ dq,
-                                                          long long n_groups, float scale) {
+                                                          long long n_groups, float scale, int nblk, int qshift,
+                                                          int Sq) {
   const long long f = (long long)blockIdx.x * 256 + threadIdx.x;
   if (f >= n_groups) return;
   constexpr int GROUPS_PER_BLOCK = 64 * D / 4;
   const long long blk = f / GROUPS_PER_BLOCK;  // (head, 64-row block)
+  const long long head = blk / nblk;
   const int rem = (int)(f % GROUPS_PER_BLOCK);
   const int tile = rem / 256, j = (rem % 256) / 64, l = rem % 64;
   const int qb = tile / (D / 32), db = tile % (D / 32);
   const int col = db * 32 + (l & 31);
-  const int row0 = qb * 32 + 8 * j + 4 * (l >> 5);
-  __bf16* out = dq + (size_t)blk * 64 * D;
+  const int row0 = (int)(blk % nblk) * 64 + qb * 32 + 8 * j + 4 * (l >> 5) - qshift;
+  __bf16* out = dq + (size_t)head * Sq * D;
   f32x4 v;
   if constexpr (X4) {
     v = *(const f32x4*)(ws + (size_t)blk * 64 * D + tile * 1024 + j * 256 + l * 4);
@@ -794,7 +834,8 @@ __global__ __launch_bounds__(256) void dq_finalize_kernel(const float* __restric
     for (int e = 0; e < 4; ++e) v[e] = src[e * 64];
   }
 #pragma unroll
-  for (int e = 0; e < 4; ++e) out[(size_t)(row0 + e) * D + col] = (__bf16)(v[e] * scale);
+  for (int e = 0; e < 4; ++e)
+    if (row0 + e >= 0 && row0 + e < Sq) out[(size_t)(row0 + e) * D + col] = (__bf16)(v[e] * scale);
 }
 
 }  // namespace
@@ -806,8 +847,8 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, floa
                       int Sq, int Sk, int D, float scale, int causal, hipStream_t st) {
   const int g = Hq / Hkv;
   const float sl2 = scale * kLog2e;
-  const bool big = (Sq % 128) == 0;
-  dim3 grid(Sq / (big ? 128 : 64), B * Hq);
+  const bool big = Sq >= 1024;  // 128 query rows per workgroup, else 64
+  dim3 grid((Sq + (big ? 127 : 63)) / (big ? 128 : 64), B * Hq);
   auto qp = (const __bf16*)q;
   auto kp = (const __bf16*)k;
   auto vp = (const __bf16*)v;
@@ -862,6 +903,9 @@ hipError_t launch_bwd(const BwdLaunch& L, hipStream_t st) {
   a.Sk = L.Sk;
   a.g = L.g;
   a.causal = L.causal;
+  a.qshift = L.qshift;
+  a.nblk = L.nblk;
+  a.diag_off = L.diag_off;
   dim3 grid(L.P);
 #define DASH_BWD_CASE(D_, T_)                                                                     \
   if (L.D == D_ && L.T == T_) {                                                                   \
@@ -895,11 +939,13 @@ hipError_t bwd_kernel_fits(int D, int T, bool atomic, int num_cu, int P, bool* f
   return hipSuccess;
 }
 
-hipError_t launch_dq_finalize(const float* ws, void* dq, long long elems, int D, float scale, bool atomic_layout,
-                              hipStream_t st) {
-  const long long n_f4 = elems / 4;
+hipError_t launch_dq_finalize(const float* ws, void* dq, long long ws_elems, int D, float scale, bool atomic_layout,
+                              int nblk, int qshift, int Sq, hipStream_t st) {
+  const long long n_f4 = ws_elems / 4;
   const unsigned blocks = (unsigned)((n_f4 + 255) / 256);
-#define DASH_FIN(D_, X4_) hipLaunchKernelGGL((dq_finalize_kernel<D_, X4_>), dim3(blocks), dim3(256), 0, st, ws, (__bf16*)dq, n_f4, scale)
+#define DASH_FIN(D_, X4_)                                                                                    \
+  hipLaunchKernelGGL((dq_finalize_kernel<D_, X4_>), dim3(blocks), dim3(256), 0, st, ws, (__bf16*)dq, n_f4, scale, \
+                     nblk, qshift, Sq)
   if (D == 128) {
     if (atomic_layout) DASH_FIN(128, false);
     else DASH_FIN(128, true);

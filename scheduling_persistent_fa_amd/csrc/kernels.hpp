@@ -26,6 +26,9 @@ struct BwdLaunch {
   long long spin_ticks;    // wait budget in 100 MHz real-time ticks
   float scale;
   int Sq, Sk, D, T, g, causal, P;
+  int qshift;    // virtual query row = query row + qshift (aligns query tiles with key/value tiles)
+  int nblk;      // 64-row dQ workspace blocks per query head
+  int diag_off;  // causal: tile pair (qi, qi + diag_off) straddles the diagonal
   bool atomic;
 };
 
@@ -35,7 +38,7 @@ hipError_t launch_delta(const void* o, const void* dO, float* delta, long long r
                         long long n_zero_i32, float* zero_f32, long long n_zero_f32, hipStream_t st);
 hipError_t launch_bwd(const BwdLaunch& L, hipStream_t st);
 hipError_t bwd_kernel_fits(int D, int T, bool atomic, int num_cu, int P, bool* fits);
-hipError_t launch_dq_finalize(const float* ws, void* dq, long long elems, int D, float scale, bool atomic_layout,
-                              hipStream_t st);
+hipError_t launch_dq_finalize(const float* ws, void* dq, long long ws_elems, int D, float scale, bool atomic_layout,
+                              int nblk, int qshift, int Sq, hipStream_t st);
 
 }  // namespace dash

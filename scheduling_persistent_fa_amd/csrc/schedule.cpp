@@ -201,6 +201,13 @@ std::string build_schedule(int mask, int kind, int Nq, int Nk, int g, int groups
   if (kind < kSerial || kind > kAtomic) return "unknown schedule";
   if (Nq > 32767 || Nk > 32767) return "too many tiles";
   if (mask == kMaskCausal && Nk < Nq) return "a causal mask needs at least as many key/value tiles as query tiles";
+  {
+    // Step indices are int32 on the device.
+    const long long per_head = (mask == kMaskCausal)
+                                   ? (long long)Nq * (Nk - Nq) + (long long)Nq * (Nq + 1) / 2
+                                   : (long long)Nq * Nk;
+    if (per_head * g * groups > 0x7fffffffLL) return "too many steps for 32-bit step indices";
+  }
   int walk = kind;
   if (kind == kAtomic) {
     walk = (atomic_walk < 0) ? (mask == kMaskCausal ? kDescQ : kSerial) : atomic_walk;

@@ -31,12 +31,13 @@ def to_f64(t) -> np.ndarray:
 class DeviceProblem:
     """Seeded inputs uploaded to the GPU plus their exact float64 values."""
 
-    def __init__(self, B, Hq, Hkv, S, D, causal, std=1.0, seed=0):
+    def __init__(self, B, Hq, Hkv, S, D, causal, std=1.0, seed=0, Sk=None):
         import torch
         from scheduling_persistent_fa_amd.attention import bf16_from_bits
         self.B, self.Hq, self.Hkv, self.S, self.D, self.causal = B, Hq, Hkv, S, D, causal
+        self.Sk = S if Sk is None else Sk
         self.scale = 1.0 / math.sqrt(D)
-        self.inp = make_inputs(B, Hq, Hkv, S, D, seed=seed, std=std)
+        self.inp = make_inputs(B, Hq, Hkv, S, D, seed=seed, std=std, Sk=Sk)
         self.q = bf16_from_bits(self.inp.q)
         self.k = bf16_from_bits(self.inp.k)
         self.v = bf16_from_bits(self.inp.v)

@@ -109,8 +109,11 @@ def test_workload_shapes_on_sampled_rows(case):
 def test_unsupported_shapes_are_rejected_before_launch():
     pb = DeviceProblem(1, 1, 1, 320, 64, True)
     o, lse = attn_fwd(pb.q, pb.k, pb.v, True)
-    with pytest.raises(_lib.DashError) as ei:  # 320 is not a multiple of the 128 tile
-        attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, True, SERIAL, opts=make_opts(tile=128))
+    with pytest.raises(_lib.DashError) as ei:  # tiles are 64 or 128 rows
+        attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, True, SERIAL, opts=make_opts(tile=96))
+    assert ei.value.status == _lib.ERR_UNSUPPORTED
+    with pytest.raises(_lib.DashError) as ei:  # symmetric shift needs an even tile count (ceil(320/128) = 3)
+        attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, True, SYM_SHIFT, opts=make_opts(tile=128))
     assert ei.value.status == _lib.ERR_UNSUPPORTED
     with pytest.raises(_lib.DashError) as ei:  # shift needs a full mask
         attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, True, SHIFT, opts=make_opts(tile=64))
@@ -194,3 +197,78 @@ def test_rectangular_shapes_match_oracle(case):
             again = attn_bwd(q, k, v, o, do, lse, causal, sched, opts=opts)
             for a_, b_ in zip((dq, dk, dv), again):
                 assert torch.equal(a_.view(torch.int16), b_.view(torch.int16))
+
+
+# ---- ragged lengths (not multiples of the tile) and degenerate sizes ----
+
+RAGGED = [  # name, B, Hq, Hkv, Sq, Sk, D, causal, tile (0 = the library's choice)
+    ("full_q200_k333_d64", 1, 2, 1, 200, 333, 64, False, 0),
+    ("full_q777_k129_d128_t128", 1, 2, 1, 777, 129, 128, False, 128),
+    ("causal_s300_d128_odd_tiles", 1, 2, 2, 300, 300, 128, True, 0),
+    ("causal_s333_d64", 2, 2, 1, 333, 333, 64, True, 0),
+    ("causal_q250_k700_d64_shift2", 2, 2, 1, 250, 700, 64, True, 0),
+    ("causal_q700_k1000_d128_t128_shift44", 1, 4, 2, 700, 1000, 128, True, 128),
+    ("full_q1_k1_d128", 1, 1, 1, 1, 1, 128, False, 0),
+    ("causal_q1_k1000_d64", 1, 2, 1, 1, 1000, 64, True, 0),
+    ("causal_s1_d64", 1, 1, 1, 1, 1, 64, True, 0),
+]
+
+
+def _query_tiles(Sq, Sk, causal, tile):
+    """Query tiles of the library's tile grid (causal: aligned with the key tiles)."""
+    T = tile or (64 if min(Sq, Sk) < 512 else 128)
+    nk = -(-Sk // T)
+    return nk - (Sk - Sq) // T if causal else -(-Sq // T)
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=[c[0] for c in RAGGED])
+def test_ragged_lengths_match_oracle(case):
+    from scheduling_persistent_fa_amd.attention import AUTO
+    name, B, Hq, Hkv, Sq, Sk, D, causal, tile = case
+    say(f"[parity-ragged] {name}")
+    pb = DeviceProblem(B, Hq, Hkv, Sq, D, causal, seed=3, Sk=Sk)
+    ref = A.backward(pb.f64("q"), pb.f64("k"), pb.f64("v"), pb.f64("do"), pb.scale, causal)
+    o, lse = attn_fwd(pb.q, pb.k, pb.v, causal)
+    torch.cuda.synchronize()
+    assert rel_err(to_f64(o), ref["o"]) <= TOL
+    assert np.abs(to_f64(lse) - ref["lse"]).max() <= TOL * max(1.0, np.abs(ref["lse"]).max())
+    nq = _query_tiles(Sq, Sk, causal, tile)
+    fast = ([SYM_SHIFT] if nq % 2 == 0 else []) if causal else [SHIFT]
+    for sched in [SERIAL, DESC_Q] + fast + [ATOMIC, AUTO]:
+        say(f"  schedule {_lib.SCHEDULE_NAMES[sched]}")
+        opts = make_opts(tile=tile, sync_check=True)
+        # outputs start as NaN so that an element the kernels never write shows
+        dq, dk, dv = (torch.full_like(t, float("nan")) for t in (pb.q, pb.k, pb.v))
+        attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, causal, sched, dq=dq, dk=dk, dv=dv, opts=opts)
+        torch.cuda.synchronize()
+        for nm, got in (("dq", dq), ("dk", dk), ("dv", dv)):
+            g64 = to_f64(got)
+            if np.abs(ref[nm]).max() == 0.0:
+                # One visible key per query (Sk = 1) makes dS exactly zero: dP and
+                # Delta are the same dot product, formed twice in fp32 over D terms,
+                # so dQ and dK are rounding noise far below 1e-3.
+                assert np.isfinite(g64).all() and np.abs(g64).max() <= 1e-3, (name, nm)
+                continue
+            e = rel_err(g64, ref[nm])
+            assert e <= TOL, (name, _lib.SCHEDULE_NAMES[sched], nm, e)
+        if sched != ATOMIC:
+            again = attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, causal, sched, opts=opts)
+            for a_, b_ in zip((dq, dk, dv), again):
+                assert torch.equal(a_.view(torch.int16), b_.view(torch.int16))
+
+
+def test_no_queries_gives_zero_key_gradients():
+    # Sq = 0: dQ is empty, and no key or value receives any gradient.
+    say("[parity-ragged] no queries")
+    k = torch.randn(2, 2, 300, 64, device="cuda").to(torch.bfloat16)
+    v = torch.randn(2, 2, 300, 64, device="cuda").to(torch.bfloat16)
+    q = torch.empty(2, 4, 0, 64, device="cuda", dtype=torch.bfloat16)
+    o, lse = attn_fwd(q, k, v, False)
+    assert o.shape == (2, 4, 0, 64) and lse.shape == (2, 4, 0)
+    dk = torch.full_like(k, float("nan"))
+    dv = torch.full_like(v, float("nan"))
+    for causal in (False, True):
+        dq, dk, dv = attn_bwd(q, k, v, o, torch.empty_like(q), lse, causal, SERIAL, dk=dk, dv=dv)
+        torch.cuda.synchronize()
+        assert dq.numel() == 0
+        assert torch.count_nonzero(dk.float()).item() == 0 and torch.count_nonzero(dv.float()).item() == 0

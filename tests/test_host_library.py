@@ -102,9 +102,13 @@ def test_bwd_argument_errors_need_no_gpu():
     assert st == _lib.ERR_INVALID_ARG
     # Hq not a multiple of Hkv
     assert L.dash_attn_bwd(*good, 1, 3, 2, 128, 64, 0.0, 0, 0, None, None) == _lib.ERR_INVALID_ARG
-    # unsupported head dimension / sequence length
+    # unsupported head dimension
     assert L.dash_attn_bwd(*good, 1, 1, 1, 128, 96, 0.0, 0, 0, None, None) == _lib.ERR_UNSUPPORTED
-    assert L.dash_attn_bwd(*good, 1, 1, 1, 100, 64, 0.0, 0, 0, None, None) == _lib.ERR_UNSUPPORTED
+    # negative sizes; keys missing; causal with fewer keys than queries
+    assert L.dash_attn_bwd(*good, 1, 1, 1, -1, 64, 0.0, 0, 0, None, None) == _lib.ERR_INVALID_ARG
+    assert L.dash_attn_bwd_qk(*good, 1, 1, 1, 100, 0, 64, 0.0, 0, 0, None, None) == _lib.ERR_INVALID_ARG
+    assert L.dash_attn_bwd_qk(*good, 1, 1, 1, 100, 99, 64, 0.0, 1, 0, None, None) == _lib.ERR_INVALID_ARG
+    assert L.dash_attn_fwd_qk(*good[:5], 1, 1, 1, 7, 0, 64, 0.0, 0, None) == _lib.ERR_INVALID_ARG
     # misaligned pointer
     bad = list(good)
     bad[3] = vp(4096 + 8)
@@ -113,6 +117,24 @@ def test_bwd_argument_errors_need_no_gpu():
     n = ctypes.c_size_t()
     assert L.dash_attn_bwd_workspace_bytes(2, 24, 24, 4096, 64, ctypes.byref(n)) == 0
     assert n.value >= 2 * 24 * 4096 * 64 * 4
+    # ragged lengths: room for up to one extra tile of virtual query rows per head
+    assert L.dash_attn_bwd_workspace_bytes(1, 2, 1, 100, 64, ctypes.byref(n)) == 0
+    assert n.value >= 2 * (128 + 128) * 64 * 4
+
+
+def test_empty_problems_are_no_ops_without_touching_the_device():
+    # No batch entries: every output is empty, nothing is launched, and null
+    # pointers are accepted (an empty tensor may have none).
+    L = _lib.lib()
+    z = [ctypes.c_void_p(0)] * 9
+    for mask in (0, 1):
+        assert L.dash_attn_bwd_qk(*z, 0, 4, 2, 300, 500, 128, 0.0, mask, _lib.AUTO, None, None) == 0
+        assert L.dash_attn_fwd_qk(*z[:5], 0, 4, 2, 300, 500, 128, 0.0, mask, None) == 0
+    # No queries: the forward has nothing to write
+    assert L.dash_attn_fwd_qk(*z[:5], 2, 4, 2, 0, 500, 128, 0.0, 1, None) == 0
+    assert L.dash_attn_bwd_delta(*z[:3], 2, 4, 0, 64, None) == 0
+    # No queries and no keys: nothing at all
+    assert L.dash_attn_bwd_qk(*z, 2, 4, 2, 0, 0, 64, 0.0, 0, _lib.AUTO, None, None) == 0
 
 
 # Fastest deterministic schedule per workload, measured on MI355X (every
