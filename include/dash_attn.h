@@ -25,8 +25,12 @@
  *  - Return value: DASH_OK (0) or a negative status.  Arguments are checked
  *    before anything is enqueued; on error nothing is launched and
  *    dash_last_error() describes the problem.  No exception crosses the ABI.
- *  - Supported: D in {64, 128}; S a positive multiple of the tile (64 or
- *    128); Hq a multiple of Hkv.
+ *  - Supported: D in {64, 128}; Hq a multiple of Hkv; any sequence lengths
+ *    (the last tile may be partial).  Empty problems are valid: with B = 0
+ *    or no query rows nothing is launched (pointers may then be NULL),
+ *    except that the backward pass writes dK = dV = 0 when Sq = 0 and
+ *    Sk > 0.  Query rows with no keys (Sk = 0, Sq > 0) are invalid: their
+ *    softmax is undefined.
  */
 #ifndef DASH_ATTN_H
 #define DASH_ATTN_H
@@ -40,8 +44,8 @@ extern "C" {
 
 enum dash_status {
   DASH_OK = 0,
-  DASH_ERR_INVALID_ARG = -1,      /* null pointer, non-positive size, Hq % Hkv != 0 */
-  DASH_ERR_UNSUPPORTED = -2,      /* valid but not implemented: D, tile, S % tile, mask/schedule pair, gang > workgroups */
+  DASH_ERR_INVALID_ARG = -1,      /* null pointer, negative size, no keys, Hq % Hkv != 0 */
+  DASH_ERR_UNSUPPORTED = -2,      /* valid but not implemented: D, tile, mask/schedule pair, gang > workgroups, size */
   DASH_ERR_HIP = -3,              /* a HIP runtime call failed */
   DASH_ERR_INVALID_SCHEDULE = -4, /* a step list failed validation */
   DASH_ERR_TIMEOUT = -5,          /* a workgroup gave up waiting on a dQ semaphore (reported with sync_check) */
@@ -81,7 +85,7 @@ enum dash_schedule_kind {
 typedef struct dash_bwd_opts {
   uint32_t struct_size;      /* sizeof(dash_bwd_opts) */
   int num_workgroups;        /* persistent workgroups; 0 = one per compute unit */
-  int tile;                  /* tile edge 64 or 128; 0 = 64 when S < 512 else 128 */
+  int tile;                  /* tile edge 64 or 128; 0 = 64 when min(Sq, Sk) < 512 else 128 */
   int atomic_walk;           /* ATOMIC only: walk of SERIAL/DESC_Q/SHIFT/SYM_SHIFT; <0 = SERIAL (full) / DESC_Q (causal) */
   int xcd_local;             /* gang members on one chiplet where possible: 1 (default when 0) / -1 off */
   void* workspace;           /* optional device workspace, 256-byte aligned; NULL = library-managed */
@@ -110,8 +114,8 @@ int dash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
  * Forward pass with Sq query rows and Sk key/value rows: Q, O bfloat16
  * [B,Hq,Sq,D], K, V bfloat16 [B,Hkv,Sk,D], lse float32 [B,Hq,Sq].  The causal
  * mask is aligned at the bottom right (query row i sees keys 0 .. i + Sk - Sq)
- * and needs Sk >= Sq (DASH_ERR_INVALID_ARG otherwise).  Sq and Sk are multiples
- * of 64.  dash_attn_fwd is the case Sq = Sk = S.
+ * and needs Sk >= Sq (DASH_ERR_INVALID_ARG otherwise).  dash_attn_fwd is the
+ * case Sq = Sk = S.
  */
 int dash_attn_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int Hq, int Hkv, int Sq, int Sk, int D, float softmax_scale, int mask,
@@ -135,14 +139,18 @@ int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
 
 /*
  * Backward pass with Sq query rows and Sk key/value rows (shapes and mask as
- * in dash_attn_fwd_qk; dQ like Q, dK/dV like K).  Sq and Sk are multiples of
- * the tile.  Schedules over the Nq x Nk tile grid: SERIAL and DESC_Q walk the
+ * in dash_attn_fwd_qk; dQ like Q, dK/dV like K).  Tile grid: Nk = ceil(Sk/T)
+ * key/value tiles; full mask: Nq = ceil(Sq/T) query tiles; causal: the query
+ * tiles start (Sk - Sq) mod T rows before the first query row, so that they
+ * line up with the key/value tiles, and Nq = Nk - floor((Sk - Sq)/T).
+ * Schedules over the Nq x Nk tile grid: SERIAL and DESC_Q walk the
  * query tiles that see each key/value tile; SHIFT (full mask) runs a gang of
  * min(Nq, Nk) workgroups, the member holding key/value tile i visiting query
  * tiles (i + t) mod Nq (with Nk > Nq member p holds tiles p, p + Nq, ... in
  * turn); SYM_SHIFT (causal, Nq even) runs the square schedule on the last Nq
  * key/value tiles and hands the Nk - Nq fully visible ones to the same N/2
- * members in shifted rounds.  The workspace is sized with S = Sq.
+ * members in shifted rounds.  dash_attn_bwd_workspace_bytes with S = Sq gives
+ * enough workspace.
  */
 int dash_attn_bwd_qk(const void* q, const void* k, const void* v, const void* o, const void* dO,
                      const float* lse, void* dq, void* dk, void* dv,
@@ -150,7 +158,9 @@ int dash_attn_bwd_qk(const void* q, const void* k, const void* v, const void* o,
                      int schedule, const dash_bwd_opts* opts, void* stream);
 
 /* Bytes of device workspace dash_attn_bwd needs for these sizes (fp32 dQ
- * accumulator, Delta, semaphores, error word).  Returns DASH_OK or an error. */
+ * accumulator over the query tiles' rows, Delta, semaphores, error word,
+ * scratch tiles); an upper bound valid for any key length and tile when
+ * S = Sq.  Returns DASH_OK or an error. */
 int dash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D, size_t* bytes);
 
 /* Delta[b,h,i] = sum_d dO[b,h,i,d] * O[b,h,i,d] in fp32 ([B*H*S] float32
