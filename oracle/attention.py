@@ -26,6 +26,13 @@ causal mask is then aligned at the bottom right: query row i sees keys
 for queries that continue a longer key sequence); with Sq = Sk it is the
 ordinary lower triangle.
 
+Banded (sliding-window) masks: with window = (left, right), query row i
+sees keys j with -left <= j - (i + Sk - Sq) <= right; None on a side means
+unbounded, so causal is window (None, 0) and the full mask (None, None).
+A window with causal=True keeps its left side and takes right = 0.  Every
+query row sees at least the key on its diagonal, so no row is empty when
+Sk >= Sq.
+
 Grouped-query attention: query head hq reads key/value head hq // g with
 g = Hq / Hkv (contiguous groups); dK/dV of a key/value head sum over its g
 query heads.  Layout is BHSD.  Rows are processed in blocks only to bound
@@ -38,16 +45,36 @@ from __future__ import annotations
 import numpy as np
 
 
+def band(causal: bool, window=None):
+    """(left, right) extent of the visible keys around the diagonal, None = unbounded."""
+    left, right = (None, None) if window is None else window
+    if causal:
+        right = 0
+    return left, right
+
+
+def visible(i, j, offset: int, causal: bool, window=None):
+    """Boolean mask: query row(s) i see key(s) j (broadcasting)."""
+    left, right = band(causal, window)
+    d = j - (i + offset)  # key position relative to the query's diagonal key
+    ok = np.ones(np.broadcast(i, j).shape, dtype=bool)
+    if right is not None:
+        ok &= d <= right
+    if left is not None:
+        ok &= d >= -left
+    return ok
+
+
 def _scores(qrows: np.ndarray, k: np.ndarray, scale: float, row0: int, causal: bool,
-            bias: np.ndarray | None = None, offset: int = 0) -> np.ndarray:
+            bias: np.ndarray | None = None, offset: int = 0, window=None) -> np.ndarray:
     """Scores of query rows row0.. against all keys; ``offset`` = Sk - Sq."""
     s = scale * (qrows @ k.T)
     if bias is not None:
         s = s + bias
-    if causal:
+    if causal or window is not None:
         i = np.arange(row0, row0 + qrows.shape[0])[:, None]
         j = np.arange(k.shape[0])[None, :]
-        s = np.where(j > i + offset, -np.inf, s)
+        s = np.where(visible(i, j, offset, causal, window), s, -np.inf)
     return s
 
 
@@ -59,7 +86,7 @@ def _softmax_rows(s: np.ndarray):
     return p, lse
 
 
-def forward(q, k, v, scale: float, causal: bool, row_block: int = 1024, bias=None):
+def forward(q, k, v, scale: float, causal: bool, row_block: int = 1024, bias=None, window=None):
     """O [B,Hq,S,D] and LSE [B,Hq,S] (natural log) in float64.
 
     ``bias`` (optional, [S,S]) is an additive score bias used by the tests.
@@ -76,14 +103,14 @@ def forward(q, k, v, scale: float, causal: bool, row_block: int = 1024, bias=Non
             for r0 in range(0, S, row_block):
                 r1 = min(S, r0 + row_block)
                 s = _scores(q[b, hq, r0:r1], k[b, hk], scale, r0, causal,
-                            None if bias is None else bias[r0:r1], off)
+                            None if bias is None else bias[r0:r1], off, window)
                 p, l_ = _softmax_rows(s)
                 o[b, hq, r0:r1] = p @ v[b, hk]
                 lse[b, hq, r0:r1] = l_
     return o, lse
 
 
-def backward(q, k, v, do, scale: float, causal: bool, row_block: int = 1024, bias=None):
+def backward(q, k, v, do, scale: float, causal: bool, row_block: int = 1024, bias=None, window=None):
     """Full gradients.  Returns dict with dq, dk, dv, o, lse, delta (float64)."""
     q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
     B, Hq, S, D = q.shape
@@ -103,7 +130,7 @@ def backward(q, k, v, do, scale: float, causal: bool, row_block: int = 1024, bia
                 r1 = min(S, r0 + row_block)
                 qr, dor = q[b, hq, r0:r1], do[b, hq, r0:r1]
                 s = _scores(qr, k[b, hk], scale, r0, causal,
-                            None if bias is None else bias[r0:r1], off)
+                            None if bias is None else bias[r0:r1], off, window)
                 p, l_ = _softmax_rows(s)
                 orow = p @ v[b, hk]
                 dlt = (dor * orow).sum(axis=1)
@@ -118,7 +145,7 @@ def backward(q, k, v, do, scale: float, causal: bool, row_block: int = 1024, bia
     return {"dq": dq, "dk": dk, "dv": dv, "o": o, "lse": lse, "delta": delta}
 
 
-def head_stats(q, k, v, do, b: int, hq: int, scale: float, causal: bool, row_block: int = 1024):
+def head_stats(q, k, v, do, b: int, hq: int, scale: float, causal: bool, row_block: int = 1024, window=None):
     """LSE and Delta of every query row of one (batch, query head), float64.
 
     Needed to evaluate single rows of dK/dV, which depend on all query rows.
@@ -132,14 +159,14 @@ def head_stats(q, k, v, do, b: int, hq: int, scale: float, causal: bool, row_blo
     delta = np.zeros(S)
     for r0 in range(0, S, row_block):
         r1 = min(S, r0 + row_block)
-        s = _scores(q[b, hq, r0:r1], k[b, hk], scale, r0, causal, None, off)
+        s = _scores(q[b, hq, r0:r1], k[b, hk], scale, r0, causal, None, off, window)
         p, l_ = _softmax_rows(s)
         lse[r0:r1] = l_
         delta[r0:r1] = (do[b, hq, r0:r1] * (p @ v[b, hk])).sum(axis=1)
     return lse, delta
 
 
-def dq_rows(q, k, v, do, b: int, hq: int, rows, scale: float, causal: bool):
+def dq_rows(q, k, v, do, b: int, hq: int, rows, scale: float, causal: bool, window=None):
     """dQ[b, hq, rows, :] from the definition, one query row at a time."""
     q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
     g = q.shape[1] // k.shape[1]
@@ -147,7 +174,7 @@ def dq_rows(q, k, v, do, b: int, hq: int, rows, scale: float, causal: bool):
     off = k.shape[2] - q.shape[2]
     out = []
     for i in rows:
-        s = _scores(q[b, hq, i:i + 1], k[b, hk], scale, i, causal, None, off)
+        s = _scores(q[b, hq, i:i + 1], k[b, hk], scale, i, causal, None, off, window)
         p, _ = _softmax_rows(s)
         o_i = p @ v[b, hk]
         dp = do[b, hq, i:i + 1] @ v[b, hk].T
@@ -156,7 +183,7 @@ def dq_rows(q, k, v, do, b: int, hq: int, rows, scale: float, causal: bool):
     return np.array(out)
 
 
-def dkdv_rows(q, k, v, do, b: int, hk: int, cols, scale: float, causal: bool, stats=None):
+def dkdv_rows(q, k, v, do, b: int, hk: int, cols, scale: float, causal: bool, stats=None, window=None):
     """dK[b, hk, cols, :] and dV[b, hk, cols, :] from the definition.
 
     ``stats`` maps each query head of the group to its (LSE, Delta) from
@@ -169,7 +196,7 @@ def dkdv_rows(q, k, v, do, b: int, hk: int, cols, scale: float, causal: bool, st
     dk_out, dv_out = [], []
     heads = list(range(hk * g, hk * g + g))
     if stats is None:
-        stats = {hq: head_stats(q, k, v, do, b, hq, scale, causal) for hq in heads}
+        stats = {hq: head_stats(q, k, v, do, b, hq, scale, causal, window=window) for hq in heads}
     for j in cols:
         dkj = np.zeros(q.shape[3])
         dvj = np.zeros(q.shape[3])
@@ -178,8 +205,8 @@ def dkdv_rows(q, k, v, do, b: int, hk: int, cols, scale: float, causal: bool, st
             i = np.arange(S)
             s = scale * (q[b, hq] @ k[b, hk, j])
             p = np.exp(s - lse)
-            if causal:
-                p = np.where(i + off >= j, p, 0.0)
+            if causal or window is not None:
+                p = np.where(visible(i, j, off, causal, window), p, 0.0)
             dp = do[b, hq] @ v[b, hk, j]
             ds = p * (dp - delta)
             dvj += p @ do[b, hq]
@@ -189,10 +216,10 @@ def dkdv_rows(q, k, v, do, b: int, hk: int, cols, scale: float, causal: bool, st
     return np.array(dk_out), np.array(dv_out)
 
 
-def head_matrices(q_head, k_head, v_head, do_head, scale: float, causal: bool):
+def head_matrices(q_head, k_head, v_head, do_head, scale: float, causal: bool, window=None):
     """P, dP and dS of one head, float64 ([Sq, Sk] each); used by the row-identity tests."""
     q_head, k_head, v_head, do_head = (np.asarray(x, dtype=np.float64) for x in (q_head, k_head, v_head, do_head))
-    s = _scores(q_head, k_head, scale, 0, causal, None, k_head.shape[0] - q_head.shape[0])
+    s = _scores(q_head, k_head, scale, 0, causal, None, k_head.shape[0] - q_head.shape[0], window)
     p, _ = _softmax_rows(s)
     o = p @ v_head
     dp = do_head @ v_head.T

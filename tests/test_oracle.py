@@ -284,3 +284,115 @@ def test_rectangular_matches_torch_autograd_float64():
         assert np.allclose(r["o"], o.detach().numpy(), atol=1e-13)
         for got, t in ((r["dq"], tq), (r["dk"], tk), (r["dv"], tv)):
             assert np.allclose(got, t.grad.numpy(), atol=1e-12)
+
+
+# ---- banded (sliding-window) masks: query i sees keys j with
+# ---- -left <= j - (i + Sk - Sq) <= right (None = unbounded) ----
+
+WINDOWS = [((1, 0), False), ((2, 1), False), ((0, 2), False), ((3, None), False), ((None, 1), False), ((2, 5), True)]
+
+
+@pytest.mark.parametrize("window,causal", WINDOWS)
+@pytest.mark.parametrize("Sq,Sk,D,g", [(5, 5, 3, 1), (3, 7, 4, 2)])
+def test_window_gradients_match_central_differences(window, causal, Sq, Sk, D, g):
+    q, do = _rand((1, g, Sq, D), 201), _rand((1, g, Sq, D), 202)
+    k, v = _rand((1, 1, Sk, D), 203), _rand((1, 1, Sk, D), 204)
+    scale = 1.0 / math.sqrt(D)
+    res = A.backward(q, k, v, do, scale, causal, window=window)
+
+    def loss(q_, k_, v_):
+        o, _ = A.forward(q_, k_, v_, scale, causal, window=window)
+        return float((o * do).sum())
+
+    h = 1e-6
+    for name, x in (("dq", q), ("dk", k), ("dv", v)):
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            xp = x.copy(); xp[idx] += h
+            xm = x.copy(); xm[idx] -= h
+            key = {"dq": "q", "dk": "k", "dv": "v"}[name]
+            ap = {"q": q, "k": k, "v": v}; ap[key] = xp
+            am = {"q": q, "k": k, "v": v}; am[key] = xm
+            num[idx] = (loss(ap["q"], ap["k"], ap["v"]) - loss(am["q"], am["k"], am["v"])) / (2 * h)
+        err = np.abs(num - res[name]).max() / max(1e-12, np.abs(num).max())
+        assert err < 1e-6, (name, err)
+
+
+def test_window_row_equals_full_attention_over_its_window():
+    # Query row i sees the contiguous key range [i + off - left, i + off + right]
+    # clipped to the sequence: evaluate that slice with no mask at all.
+    Sq, Sk, D, left, right = 9, 21, 8, 4, 2
+    off = Sk - Sq
+    q, do = _rand((1, 1, Sq, D), 210), _rand((1, 1, Sq, D), 211)
+    k, v = _rand((1, 1, Sk, D), 212), _rand((1, 1, Sk, D), 213)
+    c = A.backward(q, k, v, do, 0.3, False, window=(left, right))
+    for i in range(Sq):
+        lo, hi = max(0, i + off - left), min(Sk, i + off + right + 1)
+        sl = A.backward(q[:, :, i:i + 1], k[:, :, lo:hi], v[:, :, lo:hi], do[:, :, i:i + 1], 0.3, False)
+        assert np.allclose(sl["o"][0, 0, 0], c["o"][0, 0, i], rtol=1e-12, atol=1e-12)
+        assert abs(sl["lse"][0, 0, 0] - c["lse"][0, 0, i]) < 1e-12
+        assert np.allclose(sl["dq"][0, 0, 0], c["dq"][0, 0, i], rtol=1e-12, atol=1e-12)
+
+
+def test_zero_width_window_closed_form():
+    # window (0, 0): every query sees only its diagonal key i + off, so
+    # O_i = V_{i+off}, LSE_i = S_{i,i+off}, dQ = dK = 0 and dV_{i+off} = dO_i.
+    Sq, Sk, D = 6, 10, 5
+    off = Sk - Sq
+    q, do = _rand((1, 1, Sq, D), 220), _rand((1, 1, Sq, D), 221)
+    k, v = _rand((1, 1, Sk, D), 222), _rand((1, 1, Sk, D), 223)
+    r = A.backward(q, k, v, do, 0.5, False, window=(0, 0))
+    assert np.array_equal(r["o"][0, 0], v[0, 0, off:])
+    assert np.allclose(r["lse"][0, 0], 0.5 * (q[0, 0] * k[0, 0, off:]).sum(axis=1), atol=1e-14)
+    assert np.abs(r["dq"]).max() < 1e-14 and np.abs(r["dk"]).max() < 1e-14
+    assert np.array_equal(r["dv"][0, 0, off:], do[0, 0]) and not r["dv"][0, 0, :off].any()
+
+
+def test_wide_windows_reduce_to_full_and_causal_bitwise():
+    Sq, Sk, D = 7, 12, 4
+    q, do = _rand((1, 2, Sq, D), 230), _rand((1, 2, Sq, D), 231)
+    k, v = _rand((1, 1, Sk, D), 232), _rand((1, 1, Sk, D), 233)
+    full = A.backward(q, k, v, do, 0.4, False)
+    causal = A.backward(q, k, v, do, 0.4, True)
+    for name in ("dq", "dk", "dv", "o", "lse"):
+        assert np.array_equal(A.backward(q, k, v, do, 0.4, False, window=(Sk, Sk))[name], full[name])
+        assert np.array_equal(A.backward(q, k, v, do, 0.4, False, window=(Sk, 0))[name], causal[name])
+        assert np.array_equal(A.backward(q, k, v, do, 0.4, True, window=(None, 3))[name], causal[name])
+
+
+def test_keys_outside_every_window_get_zero_gradients():
+    Sq, Sk, D, left = 4, 20, 6, 2
+    q, do = _rand((1, 1, Sq, D), 240), _rand((1, 1, Sq, D), 241)
+    k, v = _rand((1, 1, Sk, D), 242), _rand((1, 1, Sk, D), 243)
+    r = A.backward(q, k, v, do, 0.5, True, window=(left, None))
+    first_seen = Sk - Sq - left  # the first query's window starts here
+    assert not r["dk"][0, 0, :first_seen].any() and not r["dv"][0, 0, :first_seen].any()
+    assert np.abs(r["dv"][0, 0, first_seen:]).min() > 0
+
+
+def test_window_matches_torch_autograd_float64():
+    torch = pytest.importorskip("torch")
+    B, Hq, Hkv, Sq, Sk, D = 1, 2, 1, 11, 23, 8
+    q, do = _rand((B, Hq, Sq, D), 250), _rand((B, Hq, Sq, D), 251)
+    k, v = _rand((B, Hkv, Sk, D), 252), _rand((B, Hkv, Sk, D), 253)
+    scale = 1 / math.sqrt(D)
+    for left, right in ((3, 0), (5, 2), (0, 4)):
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        s = scale * tq @ tk.repeat_interleave(Hq // Hkv, dim=1).transpose(-1, -2)
+        ones = torch.ones(Sq, Sk, dtype=torch.bool)
+        # keep keys j with i + off - left <= j <= i + off + right (off = Sk - Sq)
+        keep = ones.triu(Sk - Sq - left) & ones.tril(Sk - Sq + right)
+        s = s.masked_fill(~keep, float("-inf"))
+        o = torch.softmax(s, dim=-1) @ tv.repeat_interleave(Hq // Hkv, dim=1)
+        o.backward(torch.tensor(do))
+        r = A.backward(q, k, v, do, scale, False, window=(left, right))
+        assert np.allclose(r["o"], o.detach().numpy(), atol=1e-13)
+        for got, t in ((r["dq"], tq), (r["dk"], tk), (r["dv"], tv)):
+            assert np.allclose(got, t.grad.numpy(), atol=1e-12)
+        assert np.allclose(A.dq_rows(q, k, v, do, 0, 1, [0, 5, 10], scale, False, window=(left, right)),
+                           r["dq"][0, 1, [0, 5, 10]], atol=1e-12)
+        dk, dv = A.dkdv_rows(q, k, v, do, 0, 0, [0, 12, 22], scale, False, window=(left, right))
+        assert np.allclose(dk, r["dk"][0, 0, [0, 12, 22]], atol=1e-12)
+        assert np.allclose(dv, r["dv"][0, 0, [0, 12, 22]], atol=1e-12)
