@@ -40,7 +40,7 @@ from __future__ import annotations
 
 from dataclasses import dataclass
 
-FULL, CAUSAL = 0, 1
+FULL, CAUSAL, BAND = 0, 1, 2
 SERIAL, DESC_Q, SHIFT, SYM_SHIFT = 0, 1, 2, 3
 NAMES = {SERIAL: "serial", DESC_Q: "desc_q", SHIFT: "shift", SYM_SHIFT: "sym_shift"}
 
@@ -59,16 +59,50 @@ class ScheduleError(ValueError):
     pass
 
 
-def kv_walk(mask: int, sched: int, N: int, kj: int, Nk: int | None = None) -> list[int]:
+def tile_band(mask: int, band=None):
+    """(dl, dr): key/value tile kj is visible from query tile qi when
+    -dl <= kj - qi - (Nk - N) <= dr; None = unbounded.
+
+    Full mask: everything; causal (aligned at the bottom right): (None, 0);
+    BAND: the given pair (a sliding window of rows, rounded out to tiles).
+    """
+    if mask == FULL:
+        return None, None
+    if mask == CAUSAL:
+        return None, 0
+    if mask == BAND:
+        if band is None:
+            raise ScheduleError("a band mask needs its (left, right) tile extents")
+        return band
+    raise ScheduleError(f"unknown mask {mask}")
+
+
+def q_range(mask: int, N: int, Nk: int, kj: int, band=None) -> range:
+    """Query tiles that see key/value tile kj (possibly empty)."""
+    dl, dr = tile_band(mask, band)
+    off = Nk - N
+    lo = 0 if dr is None else max(0, kj - off - dr)
+    hi = N - 1 if dl is None else min(N - 1, kj - off + dl)
+    return range(lo, hi + 1)
+
+
+def k_range(mask: int, N: int, Nk: int, qi: int, band=None) -> range:
+    """Key/value tiles seen by query tile qi."""
+    dl, dr = tile_band(mask, band)
+    off = Nk - N
+    lo = 0 if dl is None else max(0, qi + off - dl)
+    hi = Nk - 1 if dr is None else min(Nk - 1, qi + off + dr)
+    return range(lo, hi + 1)
+
+
+def kv_walk(mask: int, sched: int, N: int, kj: int, Nk: int | None = None, band=None) -> list[int]:
     """Query tiles visited by key/value tile kj for the serial/descending walks.
 
     N query tiles, Nk key/value tiles (default N).  Under the causal mask,
     aligned at the bottom right, query tile qi sees key/value tiles
-    0 .. qi + Nk - N.
+    0 .. qi + Nk - N; under a band mask those in ``k_range``.
     """
-    off = (N if Nk is None else Nk) - N
-    lo = max(0, kj - off) if mask == CAUSAL else 0
-    tiles = list(range(lo, N))
+    tiles = list(q_range(mask, N, N if Nk is None else Nk, kj, band))
     return tiles[::-1] if sched == DESC_Q else tiles
 
 
@@ -100,7 +134,7 @@ def gang_slot(gang: int, p: int, n_gangs: int, gang_size: int, xcd_local: bool,
 
 
 def build(mask: int, sched: int, N: int, g: int, groups: int, P: int, xcd_local: bool = True,
-          max_gang: int = 0, Nk: int | None = None) -> list[list[Step]]:
+          max_gang: int = 0, Nk: int | None = None, band=None) -> list[list[Step]]:
     """Per-workgroup step lists for ``groups`` kv groups of g query heads, N query
     tiles, Nk key/value tiles (default N), P workgroups.
 
@@ -125,12 +159,23 @@ def build(mask: int, sched: int, N: int, g: int, groups: int, P: int, xcd_local:
     ``max_gang`` > 0 caps a gang schedule's gang below its natural size;
     member p then takes the units (key/value tiles, or tile pairs)
     p, p + gang, p + 2*gang, ... one after another.
+
+    A band mask (``mask`` = BAND, ``band`` = (dl, dr) in tiles) takes the
+    serial and descending walks over the visible tiles only: a key/value
+    tile that no query tile sees has no chain, and a dQ tile's ordinals rank
+    its visible key/value tiles in ascending order.  (Walked descending, the
+    chains of neighbouring key/value tiles then reach each dQ tile one step
+    apart, in ordinal order: the shift structure inside the band.)
     """
     Nk = N if Nk is None else Nk
     if N < 1 or Nk < 1 or g < 1 or groups < 1 or P < 1:
         raise ScheduleError("sizes must be positive")
-    if mask == CAUSAL and Nk < N:
-        raise ScheduleError("a causal mask needs at least as many key/value tiles as query tiles")
+    if mask in (CAUSAL, BAND) and Nk < N:
+        raise ScheduleError("a causal or band mask needs at least as many key/value tiles as query tiles")
+    if mask == BAND:
+        dl, dr = tile_band(mask, band)
+        if (dl is not None and dl < 0) or (dr is not None and dr < 0):
+            raise ScheduleError("band extents must not be negative")
     out: list[list[Step]] = [[] for _ in range(P)]
     if sched in (SERIAL, DESC_Q):
         # Chains in (group, kj) order go to the least-loaded workgroup (unit
@@ -139,10 +184,14 @@ def build(mask: int, sched: int, N: int, g: int, groups: int, P: int, xcd_local:
         load = [0] * P
         for grp in range(groups):
             for kj in range(Nk):
-                walk = kv_walk(mask, sched, N, kj, Nk)
+                walk = kv_walk(mask, sched, N, kj, Nk, band)
+                if not walk:
+                    continue
                 w = min(range(P), key=lambda x: (load[x], x))
-                # ordinal = kj: every dQ tile accumulates key/value tiles in ascending order
-                out[w].extend(_flagged([(h, qi, k, k) for (h, qi, k) in _chain(grp, g, kj, walk)]))
+                # every dQ tile accumulates its key/value tiles in ascending order:
+                # ordinal = kj minus the first key/value tile the query tile sees
+                out[w].extend(_flagged([(h, qi, k, k - k_range(mask, N, Nk, qi, band).start)
+                                        for (h, qi, k) in _chain(grp, g, kj, walk)]))
                 load[w] += g * len(walk)
         return out
     if sched == SHIFT:
@@ -201,14 +250,17 @@ def build(mask: int, sched: int, N: int, g: int, groups: int, P: int, xcd_local:
     return out
 
 
-def contributors(mask: int, N: int, qi: int, Nk: int | None = None) -> int:
+def contributors(mask: int, N: int, qi: int, Nk: int | None = None, band=None) -> int:
     """Number of key/value tiles that add into dQ tile qi (N query tiles, Nk
-    key/value tiles, causal aligned at the bottom right)."""
+    key/value tiles, causal and band masks aligned at the bottom right)."""
     Nk = N if Nk is None else Nk
+    if mask == BAND:
+        return len(k_range(mask, N, Nk, qi, band))
     return qi + Nk - N + 1 if mask == CAUSAL else Nk
 
 
-def validate(lists: list[list[Step]], mask: int, N: int, g: int, groups: int, Nk: int | None = None) -> None:
+def validate(lists: list[list[Step]], mask: int, N: int, g: int, groups: int, Nk: int | None = None,
+             band=None) -> None:
     """Raise ScheduleError unless the lists are a complete, contiguous, well-ordered, deadlock-free schedule."""
     Nk = N if Nk is None else Nk
     heads = g * groups
@@ -217,13 +269,13 @@ def validate(lists: list[list[Step]], mask: int, N: int, g: int, groups: int, Nk
         for s in lst:
             if not (0 <= s.head < heads and 0 <= s.qi < N and 0 <= s.kj < Nk):
                 raise ScheduleError(f"index out of range: {s}")
-            if mask == CAUSAL and s.kj > s.qi + Nk - N:
+            if s.kj not in k_range(mask, N, Nk, s.qi, band):
                 raise ScheduleError(f"masked tile scheduled: {s}")
             key = (s.head, s.qi, s.kj)
             if key in seen:
                 raise ScheduleError(f"tile pair scheduled twice: {key}")
             seen.add(key)
-    expect = sum(contributors(mask, N, qi, Nk) for qi in range(N)) * heads
+    expect = sum(contributors(mask, N, qi, Nk, band) for qi in range(N)) * heads
     if len(seen) != expect:
         raise ScheduleError(f"coverage {len(seen)} != {expect}")
     # chain contiguity: each (group, kj) appears as exactly one run, flagged first..last
@@ -247,7 +299,7 @@ def validate(lists: list[list[Step]], mask: int, N: int, g: int, groups: int, Nk
                 run = None
         if lst and not lst[-1].last:
             raise ScheduleError("list ends inside a chain")
-    if len(chain_owner) != groups * Nk:
+    if len(chain_owner) != groups * sum(1 for kj in range(Nk) if len(q_range(mask, N, Nk, kj, band))):
         raise ScheduleError("chain count mismatch")
     # ordinals: a permutation of 0..count-1 per dQ tile
     ords: dict[tuple[int, int], list[int]] = {}
@@ -255,7 +307,7 @@ def validate(lists: list[list[Step]], mask: int, N: int, g: int, groups: int, Nk
         for s in lst:
             ords.setdefault((s.head, s.qi), []).append(s.ord)
     for (h, qi), o in ords.items():
-        if sorted(o) != list(range(contributors(mask, N, qi, Nk))):
+        if sorted(o) != list(range(contributors(mask, N, qi, Nk, band))):
             raise ScheduleError(f"ordinals of dQ tile {(h, qi)} are {sorted(o)}")
     simulate(lists, 1.0, 1.0)  # raises on deadlock
 

@@ -254,3 +254,60 @@ def test_rectangular_shift_contributions_are_one_per_step_when_nk_le_nq():
         for t, s in enumerate(lst):
             assert s.qi == (s.kj + t) % nq
     assert Sch.monotone_in_lockstep(lists, 1)
+
+
+# ---- band (sliding-window) masks on the tile grid ----
+
+BANDS = [(0, 0), (1, 0), (2, 1), (0, 2), (3, None), (None, 1), (None, 0), (None, None)]
+
+
+@pytest.mark.parametrize("sched", [SERIAL, DESC_Q])
+@pytest.mark.parametrize("band", BANDS)
+def test_band_schedules_valid_exhaustively(sched, band):
+    for nq in range(1, 7):
+        for nk in range(nq, 9):
+            for P in (1, 3, nk + 2):
+                lists = Sch.build(Sch.BAND, sched, nq, 2, 2, P, Nk=nk, band=band)
+                Sch.validate(lists, Sch.BAND, nq, 2, 2, Nk=nk, band=band)
+                # only visible tile pairs, and every one of them
+                pairs = {(s.head, s.qi, s.kj) for l in lists for s in l}
+                for h in range(4):
+                    for qi in range(nq):
+                        for kj in range(nk):
+                            d = kj - qi - (nk - nq)
+                            vis = (band[0] is None or d >= -band[0]) and (band[1] is None or d <= band[1])
+                            assert ((h, qi, kj) in pairs) == vis
+
+
+def test_band_reduces_to_causal_and_full():
+    for sched in (SERIAL, DESC_Q):
+        for nq, nk in ((5, 5), (4, 9)):
+            assert (Sch.build(Sch.BAND, sched, nq, 2, 3, 7, Nk=nk, band=(None, 0))
+                    == Sch.build(CAUSAL, sched, nq, 2, 3, 7, Nk=nk))
+            assert (Sch.build(Sch.BAND, sched, nq, 2, 3, 7, Nk=nk, band=(None, None))
+                    == Sch.build(FULL, sched, nq, 2, 3, 7, Nk=nk))
+
+
+@pytest.mark.parametrize("n,dl", [(12, 3), (16, 5), (9, 0), (20, 19)])
+def test_descending_walk_is_a_shift_inside_a_sliding_window(n, dl):
+    # Sliding-window causal band (dl, 0) with a workgroup per chain: walked in
+    # descending query order, chain kj reaches each dQ tile exactly one step
+    # after chain kj - 1, so in the unit-cost model (reduction free) the whole
+    # head finishes in dl + 1 steps, the length of an unclipped chain; the
+    # ascending walk makes every chain wait for its predecessor's whole walk.
+    desc = Sch.build(Sch.BAND, DESC_Q, n, 1, 1, n, band=(dl, 0))
+    mk, wait = Sch.simulate(desc, 1.0, 0.0)
+    assert mk == dl + 1
+    ser = Sch.build(Sch.BAND, SERIAL, n, 1, 1, n, band=(dl, 0))
+    _, wait_s = Sch.simulate(ser, 1.0, 0.0)
+    assert dl == 0 or wait_s > wait
+
+
+def test_band_rejects_gang_schedules_and_bad_extents():
+    for sched in (SHIFT, SYM_SHIFT):
+        with pytest.raises(Sch.ScheduleError):
+            Sch.build(Sch.BAND, sched, 4, 1, 1, 4, band=(1, 0))
+    with pytest.raises(Sch.ScheduleError):
+        Sch.build(Sch.BAND, SERIAL, 4, 1, 1, 4, band=(-1, 0))
+    with pytest.raises(Sch.ScheduleError):
+        Sch.build(Sch.BAND, SERIAL, 5, 1, 1, 4, Nk=4, band=(1, 0))
