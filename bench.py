@@ -27,12 +27,23 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "bwd_kernel_counters.json")
 
 
-def flops(B, Hq, S, D, causal, Sk=None):
+def flops(B, Hq, S, D, causal, Sk=None, window=None):
     """Nominal backward FLOPs: 10 * B * Hq * D per visible (query, key) pair,
     counting S * Sk pairs, minus S^2 / 2 under the causal mask (which for
-    Sk = S is the usual halving)."""
+    Sk = S is the usual halving).  With a window (left, right) the visible
+    pairs are counted exactly: query i sees keys max(0, i + off - left) ..
+    min(Sk - 1, i + off + right), off = Sk - S."""
     Sk = S if Sk is None else Sk
-    pairs = S * Sk - (S * S / 2 if causal else 0)
+    if window is None:
+        pairs = S * Sk - (S * S / 2 if causal else 0)
+    else:
+        import numpy as np
+        left, right = window
+        right = 0 if causal else right
+        c = np.arange(S, dtype=np.int64) + (Sk - S)
+        lo = np.zeros_like(c) if left is None else np.maximum(0, c - left)
+        hi = np.full_like(c, Sk - 1) if right is None else np.minimum(Sk - 1, c + right)
+        pairs = float(np.maximum(0, hi - lo + 1).sum())
     return 10.0 * B * Hq * D * pairs
 
 
@@ -48,20 +59,21 @@ def cpu_baseline(wl, min_seconds=10.0, max_heads=8):
     except Exception:  # pragma: no cover - threadpoolctl missing
         cores = int(os.environ.get("OMP_NUM_THREADS", "1"))
     S, D, causal = wl["S"], wl["D"], wl["causal"]
-    Sk = wl.get("Sk", S)
+    Sk, window = wl.get("Sk", S), wl.get("window")
     f64 = lambda x: bf16_bits_to_f32(x).astype(np.float64)
     heads, dt = 0, 0.0
     while heads < max_heads and (heads == 0 or dt < min_seconds):
         inp = make_inputs(1, 1, 1, S, D, seed=heads, std=wl["std"], Sk=Sk)
         q, k, v, do = (f64(x) for x in (inp.q, inp.k, inp.v, inp.do))
         t0 = time.perf_counter()
-        A.backward(q, k, v, do, 1.0 / math.sqrt(D), causal)
+        A.backward(q, k, v, do, 1.0 / math.sqrt(D), causal, window=window)
         dt += time.perf_counter() - t0
         heads += 1
-    return {"value": heads * flops(1, 1, S, D, causal, Sk) / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
+    mask = ("causal" if causal else "full") + (f" window={window}" if window else "")
+    return {"value": heads * flops(1, 1, S, D, causal, Sk, window) / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle",
             "sample": f"{heads} (batch, head) slices of the workload (S={S} Sk={Sk} D={D} "
-                      f"{'causal' if causal else 'full'}), float64 forward+backward, {dt:.1f} s"}
+                      f"{mask}), float64 forward+backward, {dt:.1f} s"}
 
 
 def main():
@@ -103,18 +115,20 @@ def main():
 
     wl = dict(WORKLOADS[args.workload])
     B, Hq, Hkv, S, D, causal, tile = wl["B"], wl["Hq"], wl["Hkv"], wl["S"], wl["D"], wl["causal"], wl["tile"]
-    Sk = wl.get("Sk", S)
+    Sk, window = wl.get("Sk", S), wl.get("window")
     torch.cuda.set_device(0)
     info = device_info(0)
     inp = make_inputs(B, Hq, Hkv, S, D, seed=0, std=wl["std"], Sk=Sk)
     q, k, v, do = (bf16_from_bits(getattr(inp, n)) for n in ("q", "k", "v", "do"))
-    o, lse = attn_fwd(q, k, v, causal)
+    o, lse = attn_fwd(q, k, v, causal, window=window)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     torch.cuda.synchronize()
-    fl = flops(B, Hq, S, D, causal, Sk)
+    fl = flops(B, Hq, S, D, causal, Sk, window)
 
     # shift needs a full mask; symmetric shift pairs query tiles p, N-1-p and needs N even
     fast = ["shift"] if not causal else (["sym_shift"] if (S // tile) % 2 == 0 else [])
+    if window is not None:
+        fast = []  # a band takes the list walks (the descending one is its shift)
     det_names = ["serial", "desc_q"] + fast
     if args.schedules:
         det_names = [s for s in args.schedules.split(",") if s]
@@ -130,7 +144,8 @@ def main():
         print(f"[bench] {args.workload} {name}", file=sys.stderr, flush=True)
         base_opts = dict(tile=tile, atomic_walk=walk)
         for _ in range(args.warmup):
-            attn_bwd(q, k, v, o, do, lse, causal, sched, dq=dq, dk=dk, dv=dv, opts=make_opts(**base_opts))
+            attn_bwd(q, k, v, o, do, lse, causal, sched, dq=dq, dk=dk, dv=dv, opts=make_opts(**base_opts),
+                     window=window)
         ref_bits = dq.view(torch.int16).clone(), dk.view(torch.int16).clone(), dv.view(torch.int16).clone()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
         calls = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -143,7 +158,7 @@ def main():
         t_beg.record(stream)
         for i in range(args.steps):
             calls[i][0].record(stream)
-            attn_bwd(q, k, v, o, do, lse, causal, sched, dq=dq, dk=dk, dv=dv, opts=opts[i])
+            attn_bwd(q, k, v, o, do, lse, causal, sched, dq=dq, dk=dk, dv=dv, opts=opts[i], window=window)
             calls[i][1].record(stream)
         t_end.record(stream)
         torch.cuda.synchronize()
@@ -165,7 +180,7 @@ def main():
             ke[0].record(stream)  # materialise the underlying HIP events
             ke[1].record(stream)
             attn_bwd(q, k, v, o, do, lse, causal, sched, dq=dq, dk=dk, dv=dv,
-                     opts=make_opts(stall=stall, sync_check=True, events=ke, **base_opts))
+                     opts=make_opts(stall=stall, sync_check=True, events=ke, **base_opts), window=window)
             x_ = stall.view(-1, 2).double()
             st = x_.sum(0).tolist()
             rec["sem_stall_frac"] = st[0] / max(st[1], 1.0)
@@ -211,7 +226,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": args.workload, "B": B, "Hq": Hq, "Hkv": Hkv, "S": S, "Sk": Sk, "D": D,
-                   "mask": "causal" if causal else "full", "tile": tile, "schedule": best,
+                   "mask": "causal" if causal else "full", "window": window, "tile": tile, "schedule": best,
                    "workgroups": info["num_cu"]},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "tflops_p10_p50_p90": [round(det[best][k], 2) for k in ("tflops_p10", "tflops_p50", "tflops_p90")],

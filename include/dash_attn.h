@@ -8,16 +8,20 @@
  *   [summary] "Resumo Técnico: DASH – Agendamento de Atenção Determinístico
  *             para Treinamento de LLM de Alto Rendimento" (gist.science)
  *   [news]    "DASH如何革新LLM确定性训练" (pwwt.cn)
+ *   [ascend]  the Ascend 910B essay on deterministic FlashAttentionGrad
+ *             (ocdem.com); prior art on other hardware, cited only for the
+ *             mask and shape scenarios it lists
  *
  * Conventions shared by every entry point:
- *  - Tensors are contiguous row-major BHSD: Q, O, dO, dQ are [B, Hq, S, D];
- *    K, V, dK, dV are [B, Hkv, S, D]; all bfloat16 (2-byte) device buffers.
- *    LSE is [B, Hq, S] float32 (natural logarithm).  Every device pointer
- *    must be 16-byte aligned.  The caller owns all buffers.
+ *  - Tensors are contiguous row-major BHSD: Q, O, dO, dQ are [B, Hq, Sq, D];
+ *    K, V, dK, dV are [B, Hkv, Sk, D] (Sq = Sk = S in the entry points that
+ *    take one length); all bfloat16 (2-byte) device buffers.  LSE is
+ *    [B, Hq, Sq] float32 (natural logarithm).  Every device pointer must be
+ *    16-byte aligned.  The caller owns all buffers.
  *  - Query head hq reads key/value head hq / (Hq / Hkv) (grouped-query
  *    attention with contiguous groups).
- *  - The causal mask is top-left aligned: key j is visible to query i iff
- *    j <= i.
+ *  - The causal mask is aligned at the bottom right: key j is visible to
+ *    query i iff j <= i + Sk - Sq (j <= i when Sq = Sk).
  *  - softmax_scale <= 0 selects 1/sqrt(D).
  *  - `stream` is a hipStream_t passed as void* (NULL = default stream).
  *    Device work is enqueued on it and the call returns without waiting;
@@ -122,6 +126,20 @@ int dash_attn_fwd_qk(const void* q, const void* k, const void* v, void* o, float
                      void* stream);
 
 /*
+ * Forward pass with a banded (sliding-window) mask: query row i sees key j
+ * when -window_left <= j - (i + Sk - Sq) <= window_right, i.e. up to
+ * window_left keys before its diagonal key and window_right after it; -1
+ * leaves a side unbounded, so (-1, -1) is the full mask and (-1, 0) the
+ * causal one (banded masks are among the scenarios [ascend]'s abstract
+ * requires a deterministic backward to serve).  A side at least as wide as the sequence
+ * is unbounded.  A bounded side needs Sk >= Sq (DASH_ERR_INVALID_ARG
+ * otherwise).  Shapes as in dash_attn_fwd_qk.
+ */
+int dash_attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int Hq, int Hkv, int Sq, int Sk, int D, float softmax_scale,
+                         int window_left, int window_right, void* stream);
+
+/*
  * Backward pass: dQ, dK, dV (bfloat16) from Q, K, V, O, dO (bfloat16) and
  * lse (float32).  schedule is a dash_schedule_kind; DASH_SCHED_AUTO runs
  * the one dash_schedule_choose picks (with its gang cap unless opts sets
@@ -157,6 +175,23 @@ int dash_attn_bwd_qk(const void* q, const void* k, const void* v, const void* o,
                      int B, int Hq, int Hkv, int Sq, int Sk, int D, float softmax_scale, int mask,
                      int schedule, const dash_bwd_opts* opts, void* stream);
 
+/*
+ * Backward pass with the banded mask of dash_attn_fwd_window.  The tile grid
+ * is the causal one of dash_attn_bwd_qk (query tiles aligned with the
+ * key/value tiles); a window of w rows reaches ceil(w / T) tiles off the
+ * diagonal tile, and only tile pairs inside that band are scheduled.  SERIAL,
+ * DESC_Q and ATOMIC (default walk DESC_Q) serve banded masks; AUTO runs
+ * DESC_Q, whose descending walk reaches each dQ tile in ordinal order, one
+ * step apart between neighbouring key/value tiles.  SHIFT and SYM_SHIFT are
+ * DASH_ERR_UNSUPPORTED unless the window reduces to the full or causal mask.
+ * Keys that no query sees get dK = dV = 0.
+ */
+int dash_attn_bwd_window(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                         const float* lse, void* dq, void* dk, void* dv,
+                         int B, int Hq, int Hkv, int Sq, int Sk, int D, float softmax_scale,
+                         int window_left, int window_right, int schedule,
+                         const dash_bwd_opts* opts, void* stream);
+
 /* Bytes of device workspace dash_attn_bwd needs for these sizes (fp32 dQ
  * accumulator over the query tiles' rows, Delta, semaphores, error word,
  * scratch tiles); an upper bound valid for any key length and tile when
@@ -186,6 +221,14 @@ int dash_schedule_build(int mask, int schedule, int N, int g, int groups, int P,
  * at the bottom right; gang schedules extended as in dash_attn_bwd_qk). */
 int dash_schedule_build_qk(int mask, int schedule, int Nq, int Nk, int g, int groups, int P, int xcd_local,
                            int atomic_walk, int max_gang, dash_schedule** out);
+
+/* Same for a band mask in tile units: key/value tile kj is visible from query
+ * tile qi when -band_left <= kj - qi - (Nk - Nq) <= band_right (-1 leaves a
+ * side unbounded; Nk >= Nq).  Key/value tiles that no query tile sees get
+ * no chain; each dQ tile ranks its visible key/value tiles in ascending
+ * order.  SERIAL, DESC_Q and ATOMIC only (DASH_ERR_UNSUPPORTED otherwise). */
+int dash_schedule_build_band(int schedule, int Nq, int Nk, int band_left, int band_right, int g, int groups,
+                             int P, int xcd_local, int atomic_walk, int max_gang, dash_schedule** out);
 
 int dash_schedule_num_workgroups(const dash_schedule* s);
 long long dash_schedule_num_steps(const dash_schedule* s);

@@ -31,7 +31,8 @@ ORD_MASK = FIRST_FLAG - 1
 
 # Every symbol include/dash_attn.h declares.
 EXPORTS = (
-    "dash_attn_fwd", "dash_attn_fwd_qk", "dash_attn_bwd", "dash_attn_bwd_qk", "dash_attn_bwd_workspace_bytes",
+    "dash_attn_fwd", "dash_attn_fwd_qk", "dash_attn_fwd_window", "dash_attn_bwd", "dash_attn_bwd_qk",
+    "dash_attn_bwd_window", "dash_attn_bwd_workspace_bytes", "dash_schedule_build_band",
     "dash_attn_bwd_delta", "dash_schedule_build", "dash_schedule_build_qk", "dash_schedule_num_workgroups", "dash_schedule_num_steps", "dash_schedule_export",
     "dash_schedule_validate", "dash_schedule_simulate", "dash_schedule_free", "dash_schedule_choose",
     "dash_schedule_choose_qk",
@@ -74,6 +75,9 @@ def _declare(lib):
     lib.dash_attn_fwd_qk.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
     lib.dash_attn_bwd.argtypes = [vp] * 9 + [i, i, i, i, i, f, i, i, ctypes.POINTER(BwdOpts), vp]
     lib.dash_attn_bwd_qk.argtypes = [vp] * 9 + [i, i, i, i, i, i, f, i, i, ctypes.POINTER(BwdOpts), vp]
+    lib.dash_attn_fwd_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
+    lib.dash_attn_bwd_window.argtypes = [vp] * 9 + [i, i, i, i, i, i, f, i, i, i, ctypes.POINTER(BwdOpts), vp]
+    lib.dash_schedule_build_band.argtypes = [i, i, i, i, i, i, i, i, i, i, i, ctypes.POINTER(vp)]
     lib.dash_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, ctypes.POINTER(ctypes.c_size_t)]
     lib.dash_attn_bwd_delta.argtypes = [vp, vp, vp, i, i, i, i, vp]
     lib.dash_schedule_build.argtypes = [i, i, i, i, i, i, i, i, i, ctypes.POINTER(vp)]

@@ -28,11 +28,21 @@ def _check_bhsd(name, t, shape):
                          f"got {t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()} cuda={t.is_cuda}")
 
 
-def attn_fwd(q, k, v, causal: bool, scale: float = 0.0, out=None, lse=None, stream=None):
+def _window(causal: bool, window):
+    """(left, right) for the window entry points, -1 = unbounded; causal forces right = 0."""
+    left, right = (None, None) if window is None else window
+    if causal:
+        right = 0
+    return (-1 if left is None else int(left)), (-1 if right is None else int(right))
+
+
+def attn_fwd(q, k, v, causal: bool, scale: float = 0.0, out=None, lse=None, stream=None, window=None):
     """O [B,Hq,Sq,D] bf16 and LSE [B,Hq,Sq] fp32 from the library's forward kernel.
 
     K and V are [B,Hkv,Sk,D]; with Sq != Sk the causal mask is aligned at the
-    bottom right (query row i sees keys 0 .. i + Sk - Sq)."""
+    bottom right (query row i sees keys 0 .. i + Sk - Sq).  ``window`` =
+    (left, right) restricts row i to keys j with -left <= j - (i + Sk - Sq)
+    <= right (None = unbounded side; with causal=True right is 0)."""
     B, Hq, Sq, D = q.shape
     Hkv, Sk = k.shape[1], k.shape[2]
     _check_bhsd("q", q, (B, Hq, Sq, D))
@@ -42,8 +52,14 @@ def attn_fwd(q, k, v, causal: bool, scale: float = 0.0, out=None, lse=None, stre
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
-    _lib.check(_lib.lib().dash_attn_fwd_qk(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Sk, D,
-                                           float(scale), MASK_CAUSAL if causal else MASK_FULL, _stream(stream)))
+    if window is None:
+        _lib.check(_lib.lib().dash_attn_fwd_qk(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Sk,
+                                               D, float(scale), MASK_CAUSAL if causal else MASK_FULL,
+                                               _stream(stream)))
+    else:
+        wl, wr = _window(causal, window)
+        _lib.check(_lib.lib().dash_attn_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Sq,
+                                                   Sk, D, float(scale), wl, wr, _stream(stream)))
     return out, lse
 
 
@@ -72,9 +88,9 @@ def make_opts(num_workgroups: int = 0, tile: int = 0, atomic_walk: int = -1, xcd
 
 
 def attn_bwd(q, k, v, o, do, lse, causal: bool, schedule: int, scale: float = 0.0, dq=None, dk=None, dv=None,
-             opts: _lib.BwdOpts | None = None, stream=None):
+             opts: _lib.BwdOpts | None = None, stream=None, window=None):
     """dQ, dK, dV (bf16) from the library's persistent backward kernel (Sq query
-    rows from q, Sk key/value rows from k)."""
+    rows from q, Sk key/value rows from k; ``window`` as in attn_fwd)."""
     B, Hq, Sq, D = q.shape
     Hkv, Sk = k.shape[1], k.shape[2]
     for name, t, shp in (("q", q, (B, Hq, Sq, D)), ("k", k, (B, Hkv, Sk, D)), ("v", v, (B, Hkv, Sk, D)),
@@ -86,9 +102,14 @@ def attn_bwd(q, k, v, o, do, lse, causal: bool, schedule: int, scale: float = 0.
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     op = ctypes.byref(opts) if opts is not None else None
-    _lib.check(_lib.lib().dash_attn_bwd_qk(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
-                                           _ptr(dk), _ptr(dv), B, Hq, Hkv, Sq, Sk, D, float(scale),
-                                           MASK_CAUSAL if causal else MASK_FULL, schedule, op, _stream(stream)))
+    ptrs = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv))
+    if window is None:
+        _lib.check(_lib.lib().dash_attn_bwd_qk(*ptrs, B, Hq, Hkv, Sq, Sk, D, float(scale),
+                                               MASK_CAUSAL if causal else MASK_FULL, schedule, op, _stream(stream)))
+    else:
+        wl, wr = _window(causal, window)
+        _lib.check(_lib.lib().dash_attn_bwd_window(*ptrs, B, Hq, Hkv, Sq, Sk, D, float(scale), wl, wr, schedule, op,
+                                                   _stream(stream)))
     return dq, dk, dv
 
 

@@ -67,7 +67,8 @@ struct DevSchedule {
   int32_t* offsets = nullptr;
   long long num_steps = 0;
 };
-using SchedKey = std::tuple<int, int, int, int, int, int, int, int, int, int, int>;  // dev, mask, kind, Nq, Nk, g, groups, P, xcd, walk, cap
+// dev, mask, kind, Nq, Nk, g, groups, P, xcd, walk, cap, band_l, band_r
+using SchedKey = std::tuple<int, int, int, int, int, int, int, int, int, int, int, int, int>;
 std::map<SchedKey, DevSchedule> g_sched;
 
 struct Workspace {
@@ -109,14 +110,55 @@ WsLayout ws_layout(int B, int Hq, int Sq, int Sw, int D) {
 // Returned by check_sizes when there are no query rows (B = 0 or Sq = 0).
 constexpr int kEmpty = 1;
 
-int check_sizes(int B, int Hq, int Hkv, int Sq, int Sk, int D, int mask) {
+// A mask as a window around the bottom-right diagonal: query row i sees key
+// j when -wl <= j - (i + Sk - Sq) <= wr, -1 meaning unbounded.  kind is the
+// schedule-level mask: full (both unbounded), causal (wl unbounded, wr = 0)
+// or band (anything else).
+struct Mask {
+  int kind = dash::kMaskFull;
+  int wl = -1, wr = -1;
+  bool aligned() const { return kind != dash::kMaskFull; }
+};
+
+// From the DASH_MASK_* enum; kind = -1 if unknown.
+Mask mask_from_enum(int mask) {
+  Mask m;
+  if (mask == DASH_MASK_FULL) return m;
+  if (mask == DASH_MASK_CAUSAL) {
+    m.kind = dash::kMaskCausal;
+    m.wr = 0;
+    return m;
+  }
+  m.kind = -1;
+  return m;
+}
+
+// From window extents; a side that reaches past every key is unbounded
+// (left >= Sk - 1, right >= Sq - 1), so a window may reduce to the full or
+// the causal mask.  kind = -1 if an extent is below -1.
+Mask mask_from_window(int wl, int wr, int Sq, int Sk) {
+  Mask m;
+  if (wl < -1 || wr < -1) {
+    m.kind = -1;
+    return m;
+  }
+  m.wl = (wl < 0 || (long long)wl >= (long long)Sk - 1) ? -1 : wl;
+  m.wr = (wr < 0 || (long long)wr >= (long long)Sq - 1) ? -1 : wr;
+  if (m.wl < 0 && m.wr < 0) m.kind = dash::kMaskFull;
+  else if (m.wl < 0 && m.wr == 0) m.kind = dash::kMaskCausal;
+  else m.kind = dash::kMaskBand;
+  return m;
+}
+
+int check_sizes(int B, int Hq, int Hkv, int Sq, int Sk, int D, const Mask& mask) {
   if (B < 0 || Sq < 0 || Sk < 0) return fail(DASH_ERR_INVALID_ARG, "sizes must not be negative");
   if (Hq <= 0 || Hkv <= 0 || D <= 0) return fail(DASH_ERR_INVALID_ARG, "head counts and head dimension must be positive");
   if (Hq % Hkv) return fail(DASH_ERR_INVALID_ARG, "Hq must be a multiple of Hkv");
-  if (mask != DASH_MASK_FULL && mask != DASH_MASK_CAUSAL) return fail(DASH_ERR_INVALID_ARG, "unknown mask");
-  if (mask == DASH_MASK_CAUSAL && Sk < Sq)
-    return fail(DASH_ERR_INVALID_ARG, "a causal mask needs Sk >= Sq (it is aligned at the bottom right)");
+  if (mask.kind < 0) return fail(DASH_ERR_INVALID_ARG, "unknown mask or negative window extent");
+  if (mask.aligned() && Sk < Sq)
+    return fail(DASH_ERR_INVALID_ARG, "a causal or windowed mask needs Sk >= Sq (it is aligned at the bottom right)");
   if (D != 64 && D != 128) return fail(DASH_ERR_UNSUPPORTED, "head dimension must be 64 or 128");
+  if (Sq > (1 << 24) || Sk > (1 << 24)) return fail(DASH_ERR_UNSUPPORTED, "sequence longer than 2^24 rows");
   if ((long long)B * Hq * (std::max(Sq, Sk) + 256LL) * D >= (1LL << 40))
     return fail(DASH_ERR_UNSUPPORTED, "problem too large");
   if (B == 0 || Sq == 0) return kEmpty;
@@ -134,8 +176,8 @@ int check_ptrs(const void* const* ptrs, int nptr) {
 
 // Tile grid of one backward call.  Key/value tiles: Nk = ceil(Sk / T), the
 // last one possibly partial.  Query tiles cover virtual rows, virtual row =
-// query row + qshift.  Full mask: qshift = 0, Nq = ceil(Sq / T).  Causal
-// (bottom right, offset Sk - Sq = diag_off * T + qshift): the query tiles
+// query row + qshift.  Full mask: qshift = 0, Nq = ceil(Sq / T).  Causal and
+// banded masks (bottom right, offset Sk - Sq = diag_off * T + qshift): the query tiles
 // are aligned with the key/value tiles, so query tile qi meets the diagonal
 // in key/value tile qi + diag_off exactly as in the square case, and
 // Nq = Nk - diag_off (the first tile starts qshift rows before row 0).
@@ -143,11 +185,11 @@ struct TileGrid {
   int T, Nq, Nk, qshift, diag_off, Sw;
 };
 
-TileGrid tile_grid(int Sq, int Sk, int T, int mask) {
+TileGrid tile_grid(int Sq, int Sk, int T, bool aligned) {
   TileGrid t;
   t.T = T;
   t.Nk = (Sk + T - 1) / T;
-  if (mask == DASH_MASK_CAUSAL) {
+  if (aligned) {
     t.diag_off = (Sk - Sq) / T;
     t.qshift = (Sk - Sq) % T;
     t.Nq = t.Nk - t.diag_off;
@@ -212,6 +254,23 @@ int dash_schedule_build_qk(int mask, int schedule, int Nq, int Nk, int g, int gr
   return DASH_OK;
 }
 
+int dash_schedule_build_band(int schedule, int Nq, int Nk, int band_left, int band_right, int g, int groups, int P,
+                             int xcd_local, int atomic_walk, int max_gang, dash_schedule** out) {
+  if (!out) return fail(DASH_ERR_INVALID_ARG, "null output");
+  *out = nullptr;
+  if (max_gang < 0) return fail(DASH_ERR_INVALID_ARG, "negative gang cap");
+  if (band_left < -1 || band_right < -1) return fail(DASH_ERR_INVALID_ARG, "band extents must be >= -1");
+  auto s = std::make_unique<dash_schedule>();
+  std::string err = dash::build_schedule(dash::kMaskBand, schedule, Nq, Nk, g, groups, P, xcd_local != 0, atomic_walk,
+                                         max_gang, &s->s, band_left, band_right);
+  if (!err.empty()) {
+    const bool bad = (Nq < 1 || Nk < Nq || g < 1 || groups < 1 || P < 1 || schedule < 0 || schedule > 4);
+    return fail(bad ? DASH_ERR_INVALID_ARG : DASH_ERR_UNSUPPORTED, err);
+  }
+  *out = s.release();
+  return DASH_OK;
+}
+
 int dash_schedule_num_workgroups(const dash_schedule* s) { return s ? s->s.P : 0; }
 long long dash_schedule_num_steps(const dash_schedule* s) { return s ? (long long)s->s.steps.size() : 0; }
 
@@ -246,8 +305,8 @@ int dash_schedule_choose(int mask, int N, int D, int g, int P, int* schedule, in
   return dash_schedule_choose_qk(mask, N, N, D, g, P, schedule, max_gang);
 }
 
-int dash_attn_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
-                     int Sq, int Sk, int D, float softmax_scale, int mask, void* stream) {
+static int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                    int Sq, int Sk, int D, float softmax_scale, const Mask& mask, void* stream) {
   const void* ptrs[] = {q, k, v, o, lse};
   int st = check_sizes(B, Hq, Hkv, Sq, Sk, D, mask);
   if (st == kEmpty) return DASH_OK;  // no query rows: nothing to write
@@ -255,9 +314,21 @@ int dash_attn_fwd_qk(const void* q, const void* k, const void* v, void* o, float
   st = check_ptrs(ptrs, 5);
   if (st) return st;
   if ((long long)B * Hq > 65535) return fail(DASH_ERR_UNSUPPORTED, "B*Hq exceeds the grid limit");
-  hipError_t e = dash::launch_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, default_scale(softmax_scale, D), mask,
-                                  (hipStream_t)stream);
+  hipError_t e = dash::launch_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, default_scale(softmax_scale, D), mask.wl,
+                                  mask.wr, (hipStream_t)stream);
   return e == hipSuccess ? DASH_OK : hip_fail(e, "forward launch");
+}
+
+int dash_attn_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                     int Sq, int Sk, int D, float softmax_scale, int mask, void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, softmax_scale, mask_from_enum(mask), stream);
+}
+
+int dash_attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                         int Sq, int Sk, int D, float softmax_scale, int window_left, int window_right,
+                         void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, softmax_scale,
+                  mask_from_window(window_left, window_right, Sq, Sk), stream);
 }
 
 int dash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int S,
@@ -275,7 +346,7 @@ int dash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D, size_t* 
 
 int dash_attn_bwd_delta(const void* o, const void* dO, float* delta, int B, int H, int S, int D, void* stream) {
   const void* ptrs[] = {o, dO, delta};
-  int st = check_sizes(B, H, H, S, S, D, DASH_MASK_FULL);
+  int st = check_sizes(B, H, H, S, S, D, Mask());
   if (st == kEmpty) return DASH_OK;
   if (st) return st;
   st = check_ptrs(ptrs, 3);
@@ -284,31 +355,28 @@ int dash_attn_bwd_delta(const void* o, const void* dO, float* delta, int B, int 
   return e == hipSuccess ? DASH_OK : hip_fail(e, "delta launch");
 }
 
-int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
-                  void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int S, int D, float softmax_scale, int mask,
-                  int schedule, const dash_bwd_opts* opts, void* stream) {
-  return dash_attn_bwd_qk(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, S, S, D, softmax_scale, mask, schedule, opts,
-                          stream);
+static int zero_bf16(void* p, long long elems, int D, hipStream_t st) {
+  // bf16 zero is all-zero bits: clear elems/2 32-bit words (elems is even, D is)
+  const hipError_t e = dash::launch_delta(nullptr, nullptr, nullptr, 0, D, (int*)p, elems / 2, nullptr, 0, st);
+  return e == hipSuccess ? DASH_OK : hip_fail(e, "zero-fill launch");
 }
 
-int dash_attn_bwd_qk(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
-                     void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk, int D, float softmax_scale,
-                     int mask, int schedule, const dash_bwd_opts* opts, void* stream) {
+static int bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                    void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk, int D, float softmax_scale,
+                    const Mask& mask, int schedule, const dash_bwd_opts* opts, void* stream) {
   const void* ptrs[] = {q, k, v, o, dO, lse, dq, dk, dv};
   int st = check_sizes(B, Hq, Hkv, Sq, Sk, D, mask);
   if (st != DASH_OK && st != kEmpty) return st;
   if (schedule < DASH_SCHED_SERIAL || schedule > DASH_SCHED_AUTO) return fail(DASH_ERR_INVALID_ARG, "unknown schedule");
+  const long long kv_elems = (long long)B * Hkv * Sk * D;
   if (st == kEmpty) {
     // No query rows: dQ is empty and dK = dV = 0 (no key receives any gradient).
-    const long long kv_words = (long long)B * Hkv * Sk * D / 2;  // bf16 pairs
-    if (kv_words == 0) return DASH_OK;
+    if (kv_elems == 0) return DASH_OK;
     const void* kv_ptrs[] = {dk, dv};
     st = check_ptrs(kv_ptrs, 2);
     if (st) return st;
-    hipError_t e = dash::launch_delta(nullptr, nullptr, nullptr, 0, D, (int*)dk, kv_words, nullptr, 0, (hipStream_t)stream);
-    if (e == hipSuccess)
-      e = dash::launch_delta(nullptr, nullptr, nullptr, 0, D, (int*)dv, kv_words, nullptr, 0, (hipStream_t)stream);
-    return e == hipSuccess ? DASH_OK : hip_fail(e, "zero-fill launch");
+    st = zero_bf16(dk, kv_elems, D, (hipStream_t)stream);
+    return st ? st : zero_bf16(dv, kv_elems, D, (hipStream_t)stream);
   }
   st = check_ptrs(ptrs, 9);
   if (st) return st;
@@ -329,15 +397,18 @@ int dash_attn_bwd_qk(const void* q, const void* k, const void* v, const void* o,
 
   const int T = op.tile ? op.tile : (std::min(Sq, Sk) < 512 ? 64 : 128);
   if (T != 64 && T != 128) return fail(DASH_ERR_UNSUPPORTED, "tile must be 64 or 128");
-  const TileGrid tg = tile_grid(Sq, Sk, T, mask);
+  const TileGrid tg = tile_grid(Sq, Sk, T, mask.aligned());
   const int Nq = tg.Nq, Nk = tg.Nk;
+  // band extents in tiles: a window of w rows reaches ceil(w / T) tiles off the diagonal tile
+  const int band_l = mask.kind == dash::kMaskBand && mask.wl >= 0 ? (mask.wl + T - 1) / T : -1;
+  const int band_r = mask.kind == dash::kMaskBand && mask.wr >= 0 ? (mask.wr + T - 1) / T : -1;
   const int P = op.num_workgroups > 0 ? op.num_workgroups : di.num_cu;
   if (op.num_workgroups < 0) return fail(DASH_ERR_INVALID_ARG, "negative workgroup count");
   if (op.max_gang < 0) return fail(DASH_ERR_INVALID_ARG, "negative gang cap");
   const int g = Hq / Hkv;
   if (schedule == DASH_SCHED_AUTO) {
     int cap = 0;
-    std::string err = dash::choose_schedule(mask, Nq, Nk, D, g, P, &schedule, &cap);
+    std::string err = dash::choose_schedule(mask.kind, Nq, Nk, D, g, P, &schedule, &cap);
     if (!err.empty()) return fail(DASH_ERR_INVALID_ARG, err);
     if (op.max_gang == 0) op.max_gang = cap;
   }
@@ -359,11 +430,13 @@ int dash_attn_bwd_qk(const void* q, const void* k, const void* v, const void* o,
   DevSchedule ds;
   {
     std::lock_guard<std::mutex> lk(g_mu);
-    SchedKey key{dev, mask, schedule, Nq, Nk, g, groups, P, xcd, atomic ? (walk < 0 ? -1 : walk) : -1, op.max_gang};
+    SchedKey key{dev, mask.kind, schedule, Nq, Nk, g, groups, P, xcd, atomic ? (walk < 0 ? -1 : walk) : -1, op.max_gang,
+                 band_l, band_r};
     auto it = g_sched.find(key);
     if (it == g_sched.end()) {
       dash::Schedule s;
-      std::string err = dash::build_schedule(mask, schedule, Nq, Nk, g, groups, P, xcd != 0, walk, op.max_gang, &s);
+      std::string err = dash::build_schedule(mask.kind, schedule, Nq, Nk, g, groups, P, xcd != 0, walk, op.max_gang, &s,
+                                             band_l, band_r);
       if (!err.empty()) return fail(DASH_ERR_UNSUPPORTED, err);
       err = dash::validate_schedule(s);
       if (!err.empty()) return fail(DASH_ERR_INVALID_SCHEDULE, err);
@@ -444,12 +517,19 @@ int dash_attn_bwd_qk(const void* q, const void* k, const void* v, const void* o,
   bl.D = D;
   bl.T = T;
   bl.g = g;
-  bl.causal = mask;
+  bl.wl = mask.wl;
+  bl.wr = mask.wr;
   bl.qshift = tg.qshift;
   bl.nblk = tg.Sw / 64;
   bl.diag_off = tg.diag_off;
   bl.P = P;
   bl.atomic = atomic;
+  // Key/value tiles that no query tile sees have no chain: their dK/dV are zero.
+  if (band_l >= 0 && tg.diag_off > band_l) {
+    st = zero_bf16(dk, kv_elems, D, strm);
+    if (!st) st = zero_bf16(dv, kv_elems, D, strm);
+    if (st) return st;
+  }
   if (op.event_start) {
     e = hipEventRecord((hipEvent_t)op.event_start, strm);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord(start)");
@@ -472,6 +552,28 @@ int dash_attn_bwd_qk(const void* q, const void* k, const void* v, const void* o,
     if (h_err) return fail(DASH_ERR_TIMEOUT, "a workgroup timed out waiting on a dQ semaphore");
   }
   return DASH_OK;
+}
+
+int dash_attn_bwd_qk(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                     void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk, int D, float softmax_scale,
+                     int mask, int schedule, const dash_bwd_opts* opts, void* stream) {
+  return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, Sq, Sk, D, softmax_scale, mask_from_enum(mask), schedule,
+                  opts, stream);
+}
+
+int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                  void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int S, int D, float softmax_scale, int mask,
+                  int schedule, const dash_bwd_opts* opts, void* stream) {
+  return dash_attn_bwd_qk(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, S, S, D, softmax_scale, mask, schedule, opts,
+                          stream);
+}
+
+int dash_attn_bwd_window(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                         void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                         float softmax_scale, int window_left, int window_right, int schedule,
+                         const dash_bwd_opts* opts, void* stream) {
+  return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, Sq, Sk, D, softmax_scale,
+                  mask_from_window(window_left, window_right, Sq, Sk), schedule, opts, stream);
 }
 
 }  // extern "C"

@@ -114,12 +114,18 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 // registers and computes S^T = K Q^T so that a lane owns one query row; the
 // online softmax ([summary] §2: the backward consumes the forward's LSE) is
 // then per lane plus one exchange between the two half-waves.
+//
+// Masks are windows around the bottom-right diagonal: query row i sees key j
+// when -wl <= j - (i + Sk - Sq) <= wr, with kUnbounded for an open side (full
+// mask: both open; causal: wr = 0).
 // ---------------------------------------------------------------------------
+constexpr int kUnbounded = 1 << 29;
+
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                                          const __bf16* __restrict__ v, __bf16* __restrict__ o,
                                                          float* __restrict__ lse, int Hq, int g, int Sq, int Sk,
-                                                         float scale_log2, int causal) {
+                                                         float scale_log2, int wl, int wr) {
   constexpr int KVT = 64;               // key/value rows per LDS tile
   constexpr int PITCH = 2 * D + 48;     // bytes per LDS row: 16-byte row reads and transposing reads conflict-free
   constexpr int TILE_BYTES = KVT * PITCH;
@@ -140,7 +146,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const __bf16* __restric
   const __bf16* qh = q + (size_t)head * Sq * D;
   const __bf16* kh = k + (size_t)kvh * Sk * D;
   const __bf16* vh = v + (size_t)kvh * Sk * D;
-  const int off = Sk - Sq;  // causal, aligned at the bottom right: query row i sees keys 0 .. i + off
+  const int off = Sk - Sq;  // the diagonal key of query row i is i + off
 
   bf16x8 qb[DC];
 #pragma unroll
@@ -149,7 +155,10 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const __bf16* __restric
   // Key/value tiles of 64 rows; the last one may be partial (rows past Sk
   // read row Sk - 1 and are masked out of the softmax).
   const int kv_tiles = (Sk + KVT - 1) / KVT;
-  const int n_tiles = causal ? min(kv_tiles, (q_base + 32 * NW - 1 + off) / KVT + 1) : kv_tiles;
+  // tiles holding a key some row of this workgroup sees
+  const int t_beg = wl >= kUnbounded ? 0 : max(0, (q_base + off - wl) / KVT);
+  const int t_end = wr >= kUnbounded ? kv_tiles : min(kv_tiles, (q_base + 32 * NW - 1 + off + wr) / KVT + 1);
+  const bool windowed = wl < kUnbounded || wr < kUnbounded;
 
   bf16x8 pk[CPT], pv[CPT];
   auto load_tile = [&](int t) {
@@ -174,14 +183,14 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const __bf16* __restric
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
   float m_run = -INFINITY, l_part = 0.f;
 
-  load_tile(0);
+  load_tile(t_beg);
   store_tile(0);
   __syncthreads();
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
+  for (int t = t_beg; t < t_end; ++t) {
+    const int buf = (t - t_beg) & 1;
     const LDS char* sk = base + (2 * buf) * TILE_BYTES;
     const LDS char* sv = base + (2 * buf + 1) * TILE_BYTES;
-    if (t + 1 < n_tiles) load_tile(t + 1);
+    if (t + 1 < t_end) load_tile(t + 1);
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -196,23 +205,28 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const __bf16* __restric
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float x = s[kb][r] * scale_log2;
-        if (causal || tail) {
+        if (windowed || tail) {
           const int kv = t * KVT + kb * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-          if ((causal && kv > q_row + off) || kv >= Sk) x = -INFINITY;
+          const int d = kv - (q_row + off);
+          if (d > wr || d < -wl || kv >= Sk) x = -INFINITY;
         }
         s[kb][r] = x;
         mt = fmaxf(mt, x);
       }
     mt = fmaxf(mt, __shfl_xor(mt, 32));
+    // A window can hide whole tiles from a row: while the row has seen no key
+    // its maximum stays -inf, and 0 stands in for it in the exponents so that
+    // no inf - inf occurs (its P and its rescaling factor are then 0).
     const float m_new = fmaxf(m_run, mt);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     m_run = m_new;
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(s[kb][r] - m_new);
+        const float p = __builtin_amdgcn_exp2f(s[kb][r] - m_use);
         s[kb][r] = p;
         rs += p;
       }
@@ -229,7 +243,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_kernel(const __bf16* __restric
         for (int db = 0; db < DB; ++db)
           acc[db] = mfma32(lds_tr8_split(sv, PITCH, kb * 32 + 16 * e + 4 * h2, db * 32, lane), bp, acc[db]);
       }
-    if (t + 1 < n_tiles) {
+    if (t + 1 < t_end) {
       __syncthreads();  // everyone done with the other buffer's previous tile
       store_tile(buf ^ 1);
       __syncthreads();
@@ -305,11 +319,13 @@ __global__ __launch_bounds__(256) void delta_kernel(const __bf16* __restrict__ o
 // over all 64 query rows.  The 2*D/32 C tiles of the block's dQ partial are
 // spread over the waves.
 //
-// Ragged lengths.  Query tile qi covers the virtual rows qi*T .. qi*T+T-1,
-// virtual row = query row + qshift; qshift > 0 only for a causal mask whose
-// offset Sk - Sq is not a multiple of T, and it aligns the query tiles with
-// the key/value tiles so that the diagonal crosses tile pair
-// (qi, qi + diag_off) at the same local positions as in the square case.
+// Ragged lengths and windows.  Query tile qi covers the virtual rows
+// qi*T .. qi*T+T-1, virtual row = query row + qshift; qshift > 0 only for a
+// windowed (causal or banded) mask whose offset Sk - Sq is not a multiple of
+// T, and it aligns the query tiles with the key/value tiles so that the
+// diagonal crosses tile pair (qi, qi + diag_off) at the same local positions
+// as in the square case.  A tile pair is masked element-wise only when some
+// of its pairs fall outside the window, or it is the ragged last tile.
 // Virtual rows outside 0 .. Sq-1 read a valid row and get LSE = +inf, so
 // their P, dS and every contribution they make are exactly zero.  Key/value
 // rows past Sk in the last tile read row Sk - 1 and are masked out of P like
@@ -357,10 +373,11 @@ struct BwdArgs {
   long long spin_ticks;
   float scale;       // softmax scale
   float scale_log2;  // softmax scale * log2(e)
-  int Sq, Sk, g, causal;
+  int Sq, Sk, g;
+  int wl, wr;        // window: query row i sees key j when -wl <= j - (i + Sk - Sq) <= wr (kUnbounded: open)
   int qshift;        // virtual query row = query row + qshift
   int nblk;          // 64-row workspace blocks per query head (virtual rows / 64)
-  int diag_off;      // causal: tile pair (qi, qi + diag_off) straddles the diagonal
+  int diag_off;      // query tile qi's diagonal runs through key/value tile qi + diag_off (windowed masks)
 };
 
 // Semaphore words per 64-row dQ block: one per wave that holds dQ tiles.
@@ -371,7 +388,9 @@ constexpr int bwd_threads() {
   return 64 * 2 * (T / 32);
 }
 
-template <int D, int T, bool ATOMIC>
+// LEFT: the window has a left edge (a band other than causal / full): each
+// element then needs a second comparison, which the other masks skip.
+template <int D, int T, bool ATOMIC, bool LEFT>
 __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
   constexpr int NP = T / 32;          // wave pairs; pair p owns key/value rows 32p .. 32p+31
   constexpr int NW = 2 * NP;          // waves
@@ -553,8 +572,12 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
         dv_acc[j] = f32x16{};
       }
     }
-    const bool diag = a.causal && (kj == qi + diag_off);
-    const bool mask_on = diag || kv_valid < T;  // a diagonal tile, or the ragged last key/value tile
+    // Key offset of this tile from the query tile's diagonal tile, in rows.  The
+    // tile is partly masked when some pair falls outside the window (in the
+    // key-aligned grid of a windowed mask, local key - local row ranges over
+    // -(T-1) .. T-1), or when it is the ragged last key/value tile.
+    const int dd = (kj - qi - diag_off) * T;
+    const bool mask_on = dd > a.wr - (T - 1) || dd < (T - 1) - a.wl || kv_valid < T;
 
     for (int sub = 0; sub < SUBS; ++sub) {
       __syncthreads();  // B1: Q/dO/LSE/Delta of this block (and sK) visible; P^T, dS^T free
@@ -599,13 +622,15 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
           }
         }
         // P = exp2(S*scale*log2e - LSE*log2e); dS = P * (dP - Delta); both to LDS transposed.
-        // Under mask_on, P is zero where thr > 8j + e: on a diagonal tile where key/value
-        // row > query row, and in every row of a key/value column past Sk.  The bound is
+        // Element (8j + e) of this lane has key - diagonal key = rel - (8j + e); under
+        // mask_on P is zero where that exceeds wr (hi > 8j + e) or falls below -wl
+        // (lo < 8j + e), and in every row of a key/value column past Sk.  The bounds are
         // made opaque so that the comparisons are formed here rather than kept live
         // across the loop.
-        int kv_minus_q = diag ? kv_local - (sub * M + 32 * hf + 4 * h2) : -(1 << 20);
-        if (kv_local >= kv_valid) kv_minus_q = 1 << 20;
-        asm volatile("" : "+v"(kv_minus_q));
+        const int rel = kv_local - (sub * M + 32 * hf + 4 * h2) + dd;
+        int hi = kv_local >= kv_valid ? kUnbounded : rel - a.wr;
+        int lo = rel + a.wl;
+        asm volatile("" : "+v"(hi), "+v"(lo));
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const f32x4 l4 = *(const LDS f32x4*)((const LDS char*)slse + o_stat + 32 * j);
@@ -615,7 +640,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * j + e;
             float p = __builtin_amdgcn_exp2f(s[r] * a.scale_log2 - l4[e]);
-            if (mask_on && kv_minus_q > 8 * j + e) p = 0.f;
+            if (mask_on && (hi > 8 * j + e || (LEFT && lo < 8 * j + e))) p = 0.f;
             tp[e] = (__bf16)p;
             ts[e] = (__bf16)(p * (dp[r] - d4[e]));
           }
@@ -844,7 +869,9 @@ __global__ __launch_bounds__(256) void dq_finalize_kernel(const float* __restric
 // Host launchers.
 // ---------------------------------------------------------------------------
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
-                      int Sq, int Sk, int D, float scale, int causal, hipStream_t st) {
+                      int Sq, int Sk, int D, float scale, int wl, int wr, hipStream_t st) {
+  wl = wl < 0 ? kUnbounded : wl;
+  wr = wr < 0 ? kUnbounded : wr;
   const int g = Hq / Hkv;
   const float sl2 = scale * kLog2e;
   const bool big = Sq >= 1024;  // 128 query rows per workgroup, else 64
@@ -854,11 +881,11 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, floa
   auto vp = (const __bf16*)v;
   auto op = (__bf16*)o;
   if (D == 128) {
-    if (big) hipLaunchKernelGGL((fwd_kernel<128, 4>), grid, dim3(256), 0, st, qp, kp, vp, op, lse, Hq, g, Sq, Sk, sl2, causal);
-    else hipLaunchKernelGGL((fwd_kernel<128, 2>), grid, dim3(128), 0, st, qp, kp, vp, op, lse, Hq, g, Sq, Sk, sl2, causal);
+    if (big) hipLaunchKernelGGL((fwd_kernel<128, 4>), grid, dim3(256), 0, st, qp, kp, vp, op, lse, Hq, g, Sq, Sk, sl2, wl, wr);
+    else hipLaunchKernelGGL((fwd_kernel<128, 2>), grid, dim3(128), 0, st, qp, kp, vp, op, lse, Hq, g, Sq, Sk, sl2, wl, wr);
   } else {
-    if (big) hipLaunchKernelGGL((fwd_kernel<64, 4>), grid, dim3(256), 0, st, qp, kp, vp, op, lse, Hq, g, Sq, Sk, sl2, causal);
-    else hipLaunchKernelGGL((fwd_kernel<64, 2>), grid, dim3(128), 0, st, qp, kp, vp, op, lse, Hq, g, Sq, Sk, sl2, causal);
+    if (big) hipLaunchKernelGGL((fwd_kernel<64, 4>), grid, dim3(256), 0, st, qp, kp, vp, op, lse, Hq, g, Sq, Sk, sl2, wl, wr);
+    else hipLaunchKernelGGL((fwd_kernel<64, 2>), grid, dim3(128), 0, st, qp, kp, vp, op, lse, Hq, g, Sq, Sk, sl2, wl, wr);
   }
   return hipGetLastError();
 }
@@ -902,17 +929,24 @@ hipError_t launch_bwd(const BwdLaunch& L, hipStream_t st) {
   a.Sq = L.Sq;
   a.Sk = L.Sk;
   a.g = L.g;
-  a.causal = L.causal;
+  a.wl = L.wl < 0 ? kUnbounded : L.wl;
+  a.wr = L.wr < 0 ? kUnbounded : L.wr;
   a.qshift = L.qshift;
   a.nblk = L.nblk;
   a.diag_off = L.diag_off;
   dim3 grid(L.P);
-#define DASH_BWD_CASE(D_, T_)                                                                     \
-  if (L.D == D_ && L.T == T_) {                                                                   \
-    const dim3 block(bwd_threads<T_>());                                                          \
-    if (L.atomic) hipLaunchKernelGGL((bwd_kernel<D_, T_, true>), grid, block, 0, st, a);          \
-    else hipLaunchKernelGGL((bwd_kernel<D_, T_, false>), grid, block, 0, st, a);                  \
-    return hipGetLastError();                                                                     \
+  const bool left = a.wl < kUnbounded;
+#define DASH_BWD_CASE(D_, T_)                                                                        \
+  if (L.D == D_ && L.T == T_) {                                                                      \
+    const dim3 block(bwd_threads<T_>());                                                             \
+    if (L.atomic) {                                                                                  \
+      if (left) hipLaunchKernelGGL((bwd_kernel<D_, T_, true, true>), grid, block, 0, st, a);         \
+      else hipLaunchKernelGGL((bwd_kernel<D_, T_, true, false>), grid, block, 0, st, a);             \
+    } else {                                                                                         \
+      if (left) hipLaunchKernelGGL((bwd_kernel<D_, T_, false, true>), grid, block, 0, st, a);        \
+      else hipLaunchKernelGGL((bwd_kernel<D_, T_, false, false>), grid, block, 0, st, a);            \
+    }                                                                                                \
+    return hipGetLastError();                                                                        \
   }
   DASH_BWD_CASE(128, 128)
   DASH_BWD_CASE(64, 128)
@@ -923,19 +957,25 @@ hipError_t launch_bwd(const BwdLaunch& L, hipStream_t st) {
 }
 
 hipError_t bwd_kernel_fits(int D, int T, bool atomic, int num_cu, int P, bool* fits) {
-  int per_cu = 0;
-  hipError_t e = hipErrorInvalidValue;
-#define DASH_OCC_CASE(D_, T_)                                                                                  \
-  if (D == D_ && T == T_)                                                                                      \
-    e = atomic ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_kernel<D_, T_, true>, bwd_threads<T_>(), 0) \
-               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_kernel<D_, T_, false>, bwd_threads<T_>(), 0);
+  // Both mask variants of the kernel must fit.
+  int per_cu = 0, per_cu2 = 0;
+  hipError_t e = hipErrorInvalidValue, e2 = hipErrorInvalidValue;
+#define DASH_OCC_CASE(D_, T_)                                                                                   \
+  if (D == D_ && T == T_) {                                                                                     \
+    const int nt = bwd_threads<T_>();                                                                           \
+    e = atomic ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_kernel<D_, T_, true, true>, nt, 0)   \
+               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_kernel<D_, T_, false, true>, nt, 0); \
+    e2 = atomic ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu2, bwd_kernel<D_, T_, true, false>, nt, 0) \
+                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu2, bwd_kernel<D_, T_, false, false>, nt, 0); \
+  }
   DASH_OCC_CASE(128, 128)
   DASH_OCC_CASE(64, 128)
   DASH_OCC_CASE(128, 64)
   DASH_OCC_CASE(64, 64)
 #undef DASH_OCC_CASE
   if (e != hipSuccess) return e;
-  *fits = (long long)per_cu * num_cu >= P;
+  if (e2 != hipSuccess) return e2;
+  *fits = (long long)std::min(per_cu, per_cu2) * num_cu >= P;
   return hipSuccess;
 }
 

@@ -25,15 +25,16 @@ struct BwdLaunch {
   unsigned long long* stall;
   long long spin_ticks;    // wait budget in 100 MHz real-time ticks
   float scale;
-  int Sq, Sk, D, T, g, causal, P;
+  int Sq, Sk, D, T, g, P;
+  int wl, wr;    // window around the bottom-right diagonal in rows (-1: unbounded); causal = (-1, 0)
   int qshift;    // virtual query row = query row + qshift (aligns query tiles with key/value tiles)
   int nblk;      // 64-row dQ workspace blocks per query head
-  int diag_off;  // causal: tile pair (qi, qi + diag_off) straddles the diagonal
+  int diag_off;  // windowed masks: query tile qi's diagonal runs through key/value tile qi + diag_off
   bool atomic;
 };
 
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
-                      int Sq, int Sk, int D, float scale, int causal, hipStream_t st);
+                      int Sq, int Sk, int D, float scale, int wl, int wr, hipStream_t st);
 hipError_t launch_delta(const void* o, const void* dO, float* delta, long long rows, int D, int* zero_i32,
                         long long n_zero_i32, float* zero_f32, long long n_zero_f32, hipStream_t st);
 hipError_t launch_bwd(const BwdLaunch& L, hipStream_t st);

@@ -31,6 +31,39 @@
 #include <utility>
 
 namespace dash {
+
+namespace {
+// Tile-distance extents of a mask: (dl, dr), -1 unbounded.
+void extents(const Schedule& s, int* dl, int* dr) {
+  if (s.mask == kMaskCausal) {
+    *dl = -1;
+    *dr = 0;
+  } else if (s.mask == kMaskBand) {
+    *dl = s.band_l;
+    *dr = s.band_r;
+  } else {
+    *dl = -1;
+    *dr = -1;
+  }
+}
+}  // namespace
+
+void visible_q(const Schedule& s, int kj, int* lo, int* hi) {
+  int dl, dr;
+  extents(s, &dl, &dr);
+  const int off = s.Nk - s.Nq;
+  *lo = dr < 0 ? 0 : std::max(0, kj - off - dr);
+  *hi = dl < 0 ? s.Nq - 1 : std::min(s.Nq - 1, kj - off + dl);
+}
+
+void visible_k(const Schedule& s, int qi, int* lo, int* hi) {
+  int dl, dr;
+  extents(s, &dl, &dr);
+  const int off = s.Nk - s.Nq;
+  *lo = dl < 0 ? 0 : std::max(0, qi + off - dl);
+  *hi = dr < 0 ? s.Nk - 1 : std::min(s.Nk - 1, qi + off + dr);
+}
+
 namespace {
 
 struct Triple {
@@ -59,15 +92,18 @@ std::string build_list_scheduled(const Schedule& s, std::vector<std::vector<Step
   std::vector<int32_t> ords;
   for (int grp = 0; grp < s.groups; ++grp) {
     for (int kj = 0; kj < s.Nk; ++kj) {
-      // causal, bottom-right aligned: the query tiles that see kv tile kj
-      const int lo = (s.mask == kMaskCausal) ? std::max(0, kj - (s.Nk - s.Nq)) : 0;
+      int lo, hi;  // the query tiles that see kv tile kj
+      visible_q(s, kj, &lo, &hi);
+      if (lo > hi) continue;  // seen by no query tile: no chain
       chain.clear();
       ords.clear();
       for (int u = 0; u < s.g; ++u) {
-        for (int t = 0; t < s.Nq - lo; ++t) {
-          const int qi = (s.walk == kDescQ) ? (s.Nq - 1 - t) : (lo + t);
+        for (int t = 0; t <= hi - lo; ++t) {
+          const int qi = (s.walk == kDescQ) ? (hi - t) : (lo + t);
+          int klo, khi;
+          visible_k(s, qi, &klo, &khi);
           chain.push_back({grp * s.g + u, qi, kj});
-          ords.push_back(kj);  // ascending key/value order for every dQ tile
+          ords.push_back(kj - klo);  // ascending key/value order for every dQ tile
         }
       }
       Slot top = heap.top();
@@ -173,6 +209,12 @@ std::string build_gang(const Schedule& s, std::vector<std::vector<StepRec>>& per
 
 std::string choose_schedule(int mask, int Nq, int Nk, int D, int g, int P, int* kind, int* max_gang) {
   if (Nq < 1 || Nk < 1 || D < 1 || g < 1 || P < 1) return "sizes must be positive";
+  if (mask == kMaskBand) {
+    if (Nk < Nq) return "a band mask needs Sk >= Sq";
+    *kind = kDescQ;
+    *max_gang = 0;
+    return "";
+  }
   if (mask != kMaskFull && mask != kMaskCausal) return "unknown mask";
   if (mask == kMaskCausal && Nk < Nq) return "a causal mask needs Sk >= Sq";
   const int N = Nq;
@@ -195,22 +237,20 @@ std::string choose_schedule(int mask, int Nq, int Nk, int D, int g, int P, int* 
 }
 
 std::string build_schedule(int mask, int kind, int Nq, int Nk, int g, int groups, int P, bool xcd_local,
-                           int atomic_walk, int max_gang, Schedule* out) {
+                           int atomic_walk, int max_gang, Schedule* out, int band_l, int band_r) {
   if (Nq < 1 || Nk < 1 || g < 1 || groups < 1 || P < 1) return "sizes must be positive";
-  if (mask != kMaskFull && mask != kMaskCausal) return "unknown mask";
+  if (mask != kMaskFull && mask != kMaskCausal && mask != kMaskBand) return "unknown mask";
+  if (mask == kMaskBand && Nk < Nq) return "a band mask needs at least as many key/value tiles as query tiles";
   if (kind < kSerial || kind > kAtomic) return "unknown schedule";
   if (Nq > 32767 || Nk > 32767) return "too many tiles";
   if (mask == kMaskCausal && Nk < Nq) return "a causal mask needs at least as many key/value tiles as query tiles";
   {
-    // Step indices are int32 on the device.
-    const long long per_head = (mask == kMaskCausal)
-                                   ? (long long)Nq * (Nk - Nq) + (long long)Nq * (Nq + 1) / 2
-                                   : (long long)Nq * Nk;
-    if (per_head * g * groups > 0x7fffffffLL) return "too many steps for 32-bit step indices";
+    // Step indices are int32 on the device (bound: every tile pair visible).
+    if ((long long)Nq * Nk * g * groups > 0x7fffffffLL) return "too many steps for 32-bit step indices";
   }
   int walk = kind;
   if (kind == kAtomic) {
-    walk = (atomic_walk < 0) ? (mask == kMaskCausal ? kDescQ : kSerial) : atomic_walk;
+    walk = (atomic_walk < 0) ? (mask == kMaskFull ? kSerial : kDescQ) : atomic_walk;
     if (walk < kSerial || walk > kSymShift) return "unknown atomic walk";
   }
   if (walk == kShift && mask != kMaskFull) return "shift scheduling needs a full mask";
@@ -227,6 +267,8 @@ std::string build_schedule(int mask, int kind, int Nq, int Nk, int g, int groups
   s.P = P;
   s.xcd_local = xcd_local;
   s.max_gang = max_gang > 0 ? max_gang : 0;
+  s.band_l = mask == kMaskBand ? (band_l < 0 ? -1 : band_l) : -1;
+  s.band_r = mask == kMaskBand ? (band_r < 0 ? -1 : band_r) : -1;
   std::vector<std::vector<StepRec>> per_wg(P);
   std::string err = (walk == kSerial || walk == kDescQ) ? build_list_scheduled(s, per_wg) : build_gang(s, per_wg);
   if (!err.empty()) return err;
@@ -281,7 +323,7 @@ bool simulate_schedule(const Schedule& s, double c, double r, double* makespan, 
 }
 
 std::string validate_schedule(const Schedule& s) {
-  const int Nq = s.Nq, Nk = s.Nk, off = Nk - Nq;  // causal: query tile qi sees kv tiles 0 .. qi + off
+  const int Nq = s.Nq, Nk = s.Nk;
   const long long heads = static_cast<long long>(s.g) * s.groups;
   if (static_cast<int>(s.offsets.size()) != s.P + 1) return "offset table size";
   if (s.offsets[0] != 0 || s.offsets[s.P] != static_cast<int32_t>(s.steps.size())) return "offset table bounds";
@@ -295,7 +337,9 @@ std::string validate_schedule(const Schedule& s) {
       const StepRec& st = s.steps[i];
       if (st.head < 0 || st.head >= heads || st.qi < 0 || st.qi >= Nq || st.kj < 0 || st.kj >= Nk)
         return "step index out of range";
-      if (s.mask == kMaskCausal && st.kj > st.qi + off) return "masked tile pair scheduled";
+      int klo, khi;
+      visible_k(s, st.qi, &klo, &khi);
+      if (st.kj < klo || st.kj > khi) return "masked tile pair scheduled";
       const size_t pair = (static_cast<size_t>(st.head) * Nq + st.qi) * Nk + st.kj;
       if (seen[pair]) return "tile pair scheduled twice";
       seen[pair] = 1;
@@ -313,15 +357,24 @@ std::string validate_schedule(const Schedule& s) {
     if (run >= 0) return "list ends inside a chain";
   }
   long long expect = 0;
-  for (int qi = 0; qi < Nq; ++qi) expect += (s.mask == kMaskCausal) ? qi + off + 1 : Nk;
+  for (int qi = 0; qi < Nq; ++qi) {
+    int klo, khi;
+    visible_k(s, qi, &klo, &khi);
+    expect += std::max(0, khi - klo + 1);
+  }
   if (covered != expect * heads) return "coverage mismatch";
-  for (int32_t o : owner)
-    if (o < 0) return "missing chain";
+  for (size_t c = 0; c < owner.size(); ++c) {
+    int lo, hi;
+    visible_q(s, static_cast<int>(c % Nk), &lo, &hi);
+    if ((owner[c] >= 0) != (lo <= hi)) return "missing or extra chain";
+  }
   // ordinals of each dQ tile: exactly 0..count-1
   std::vector<uint8_t> ordseen(static_cast<size_t>(heads) * Nq * Nk, 0);
   for (const StepRec& st : s.steps) {
     const int32_t ord = st.ordflags & kOrdMask;
-    const int32_t lim = (s.mask == kMaskCausal) ? st.qi + off + 1 : Nk;
+    int klo, khi;
+    visible_k(s, st.qi, &klo, &khi);
+    const int32_t lim = khi - klo + 1;
     if (ord < 0 || ord >= lim) return "ordinal out of range";
     const size_t k = (static_cast<size_t>(st.head) * Nq + st.qi) * Nk + ord;
     if (ordseen[k]) return "ordinal repeated";

@@ -15,7 +15,10 @@
 
 namespace dash {
 
-enum : int { kMaskFull = 0, kMaskCausal = 1 };
+// kMaskBand: key/value tile kj is visible from query tile qi when
+// -band_l <= kj - qi - (Nk - Nq) <= band_r (a negative extent is unbounded);
+// causal is the band (unbounded, 0).
+enum : int { kMaskFull = 0, kMaskCausal = 1, kMaskBand = 2 };
 enum : int { kSerial = 0, kDescQ = 1, kShift = 2, kSymShift = 3, kAtomic = 4 };
 
 constexpr int32_t kFirstFlag = 1 << 28;
@@ -35,6 +38,7 @@ struct Schedule {
   int g = 1, groups = 1, P = 1;
   bool xcd_local = true;
   int max_gang = 0;                  // 0: natural gang size (N for shift, N/2 for symmetric shift)
+  int band_l = -1, band_r = -1;      // kMaskBand extents in tiles (-1: unbounded)
   std::vector<int32_t> offsets;  // P + 1
   std::vector<StepRec> steps;
 };
@@ -43,10 +47,16 @@ struct Schedule {
 // Nq query tiles, Nk key/value tiles.  The causal mask is aligned at the
 // bottom right: query tile qi sees key/value tiles 0 .. qi + Nk - Nq.
 std::string build_schedule(int mask, int kind, int Nq, int Nk, int g, int groups, int P, bool xcd_local,
-                           int atomic_walk, int max_gang, Schedule* out);
+                           int atomic_walk, int max_gang, Schedule* out, int band_l = -1, int band_r = -1);
+// Query tiles [*lo, *hi] that see key/value tile kj, and key/value tiles seen
+// by query tile qi (empty when *lo > *hi).
+void visible_q(const Schedule& s, int kj, int* lo, int* hi);
+void visible_k(const Schedule& s, int qi, int* lo, int* hi);
 // Empty string if valid, else the first violation found.
 std::string validate_schedule(const Schedule& s);
-// The deterministic schedule (and gang cap) chosen for a shape; empty string on success.
+// The deterministic schedule (and gang cap) chosen for a shape; empty string
+// on success.  A band mask takes DESC_Q: walked descending, the chains of a
+// band reach each dQ tile in ordinal order, one step apart.
 std::string choose_schedule(int mask, int Nq, int Nk, int D, int g, int P, int* kind, int* max_gang);
 // Unit-cost DAG simulation; returns false on deadlock.
 bool simulate_schedule(const Schedule& s, double c, double r, double* makespan, double* total_wait);

@@ -73,4 +73,8 @@ WORKLOADS = {
     "x1_cross_q4096_k16384_d128": dict(B=1, Hq=16, Hkv=16, S=4096, Sk=16384, D=128, causal=False, tile=128, std=1.0),
     "x2_causal_q4096_k16384_d128": dict(B=1, Hq=16, Hkv=16, S=4096, Sk=16384, D=128, causal=True, tile=128,
                                         std=1.0),
+    # sliding-window causal attention: each query sees its own key and the
+    # 4095 before it (a 4096-key window)
+    "w1_sliding_s16384_w4096_d128": dict(B=1, Hq=16, Hkv=16, S=16384, D=128, causal=True, window=(4095, 0),
+                                         tile=128, std=1.0),
 }

@@ -25,11 +25,21 @@ class Schedule:
     """
 
     def __init__(self, mask: int, schedule: int, N: int, g: int, groups: int, P: int,
-                 xcd_local: bool = True, atomic_walk: int = -1, max_gang: int = 0, Nk: int | None = None):
+                 xcd_local: bool = True, atomic_walk: int = -1, max_gang: int = 0, Nk: int | None = None,
+                 band=None):
+        """``band`` = (left, right) tile extents (None = unbounded side) builds a
+        band-mask schedule through ``dash_schedule_build_band``; ``mask`` is then
+        ignored."""
         L = _lib.lib()
         h = ctypes.c_void_p()
-        _lib.check(L.dash_schedule_build_qk(mask, schedule, N, N if Nk is None else Nk, g, groups, P,
-                                            int(bool(xcd_local)), atomic_walk, max_gang, ctypes.byref(h)))
+        nk = N if Nk is None else Nk
+        if band is None:
+            _lib.check(L.dash_schedule_build_qk(mask, schedule, N, nk, g, groups, P, int(bool(xcd_local)),
+                                                atomic_walk, max_gang, ctypes.byref(h)))
+        else:
+            bl, br = (-1 if x is None else int(x) for x in band)
+            _lib.check(L.dash_schedule_build_band(schedule, N, nk, bl, br, g, groups, P, int(bool(xcd_local)),
+                                                  atomic_walk, max_gang, ctypes.byref(h)))
         self._h = h
         self.P = L.dash_schedule_num_workgroups(h)
         self.num_steps = L.dash_schedule_num_steps(h)

@@ -272,3 +272,63 @@ def test_no_queries_gives_zero_key_gradients():
         torch.cuda.synchronize()
         assert dq.numel() == 0
         assert torch.count_nonzero(dk.float()).item() == 0 and torch.count_nonzero(dv.float()).item() == 0
+
+
+# ---- banded (sliding-window) masks ----
+
+WINDOWED = [  # name, B, Hq, Hkv, Sq, Sk, D, (left, right), tile (0 = library's choice)
+    ("sliding_causal_s300_w50_d64", 1, 2, 1, 300, 300, 64, (50, 0), 0),
+    ("sliding_causal_s1000_w300_d128_t128", 1, 4, 2, 1000, 1000, 128, (300, 0), 128),
+    ("local_s333_w40_70_d64", 2, 2, 2, 333, 333, 64, (40, 70), 0),
+    ("sliding_q250_k700_w100_d64_unseen_keys", 1, 2, 1, 250, 700, 64, (100, 0), 0),
+    ("right_only_s200_w5_d128", 1, 2, 1, 200, 200, 128, (None, 5), 0),
+    ("zero_width_q64_k200_d64", 1, 1, 1, 64, 200, 64, (0, 0), 0),
+]
+
+
+@pytest.mark.parametrize("case", WINDOWED, ids=[c[0] for c in WINDOWED])
+def test_windowed_masks_match_oracle(case):
+    from scheduling_persistent_fa_amd.attention import AUTO
+    name, B, Hq, Hkv, Sq, Sk, D, window, tile = case
+    say(f"[parity-window] {name}")
+    pb = DeviceProblem(B, Hq, Hkv, Sq, D, False, seed=5, Sk=Sk)
+    ref = A.backward(pb.f64("q"), pb.f64("k"), pb.f64("v"), pb.f64("do"), pb.scale, False, window=window)
+    o, lse = attn_fwd(pb.q, pb.k, pb.v, False, window=window)
+    torch.cuda.synchronize()
+    assert rel_err(to_f64(o), ref["o"]) <= TOL
+    assert np.abs(to_f64(lse) - ref["lse"]).max() <= TOL * max(1.0, np.abs(ref["lse"]).max())
+    for sched in (SERIAL, DESC_Q, ATOMIC, AUTO):
+        say(f"  schedule {_lib.SCHEDULE_NAMES[sched]}")
+        opts = make_opts(tile=tile, sync_check=True)
+        dq, dk, dv = (torch.full_like(t, float("nan")) for t in (pb.q, pb.k, pb.v))
+        attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, False, sched, dq=dq, dk=dk, dv=dv, opts=opts, window=window)
+        torch.cuda.synchronize()
+        for nm, got in (("dq", dq), ("dk", dk), ("dv", dv)):
+            g64 = to_f64(got)
+            if np.abs(ref[nm]).max() == 0.0:
+                # a zero-width window: dS is exactly zero (see the ragged test)
+                assert np.isfinite(g64).all() and np.abs(g64).max() <= 1e-3, (name, nm)
+                continue
+            e = rel_err(g64, ref[nm])
+            assert e <= TOL, (name, _lib.SCHEDULE_NAMES[sched], nm, e)
+            # keys that no query sees: exactly zero
+            unseen = np.abs(ref[nm]).max(axis=-1) == 0.0
+            if nm != "dq" and unseen.any():
+                assert not g64[unseen].any(), (name, nm)
+        if sched != ATOMIC:
+            again = attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, False, sched, opts=opts, window=window)
+            for a_, b_ in zip((dq, dk, dv), again):
+                assert torch.equal(a_.view(torch.int16), b_.view(torch.int16))
+
+
+def test_windows_that_reduce_to_full_or_causal_take_the_gang_schedules():
+    # A window wider than the sequence is the full or causal mask, and the
+    # shift schedules accept it.
+    pb = DeviceProblem(1, 2, 2, 512, 128, True, seed=6)
+    ref = A.backward(pb.f64("q"), pb.f64("k"), pb.f64("v"), pb.f64("do"), pb.scale, True)
+    o, lse = attn_fwd(pb.q, pb.k, pb.v, False, window=(5000, 0))
+    dq, dk, dv = attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, False, SYM_SHIFT, window=(5000, 0),
+                          opts=make_opts(tile=128, sync_check=True))
+    torch.cuda.synchronize()
+    for nm, got in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert rel_err(to_f64(got), ref[nm]) <= TOL

@@ -162,7 +162,8 @@ def test_adaptive_choice_rules():
     assert choose(Sch.FULL, 512, 128, 1, 256) == (_lib.SHIFT, 256)      # gang of 512 capped to the grid
     assert choose(Sch.CAUSAL, 1024, 128, 1, 256) == (_lib.SYM_SHIFT, 256)
     assert choose(Sch.CAUSAL, 512, 128, 1, 256) == (_lib.SYM_SHIFT, 0)  # N/2 = 256 fits exactly
-    for bad in [(Sch.FULL, 0, 128, 1, 256), (2, 8, 128, 1, 256), (Sch.FULL, 8, 128, 1, 0)]:
+    assert choose(Sch.BAND, 8, 128, 1, 256) == (_lib.DESC_Q, 0)         # band masks: descending walk
+    for bad in [(Sch.FULL, 0, 128, 1, 256), (3, 8, 128, 1, 256), (Sch.FULL, 8, 128, 1, 0)]:
         with pytest.raises(_lib.DashError) as ei:
             choose(*bad)
         assert ei.value.status == _lib.ERR_INVALID_ARG
@@ -219,3 +220,47 @@ def test_adaptive_choice_on_rectangles():
     assert choose(Sch.CAUSAL, 16, 128, 1, 256, Nk=16) == (_lib.SYM_SHIFT, 0)
     with pytest.raises(_lib.DashError):
         choose(Sch.CAUSAL, 16, 128, 1, 256, Nk=8)
+
+
+# ---- band (sliding-window) masks ----
+
+BAND_CASES = [  # sched, Nq, Nk, band, g, groups, P
+    (Sch.SERIAL, 6, 6, (2, 0), 1, 2, 5), (Sch.DESC_Q, 6, 6, (2, 0), 2, 2, 7), (Sch.DESC_Q, 5, 9, (1, 1), 1, 3, 4),
+    (Sch.SERIAL, 4, 11, (0, 2), 2, 2, 6), (Sch.DESC_Q, 32, 128, (8, 0), 1, 16, 256),
+    (Sch.DESC_Q, 7, 7, (None, 2), 1, 1, 3), (Sch.SERIAL, 7, 10, (3, None), 1, 2, 4),
+]
+
+
+@pytest.mark.parametrize("sched,Nq,Nk,band,g,groups,P", BAND_CASES)
+def test_band_schedules_match_oracle_exactly(sched, Nq, Nk, band, g, groups, P):
+    lib_s = Schedule(0, sched, Nq, g, groups, P, Nk=Nk, band=band)
+    lib_s.validate()
+    ora = Sch.build(Sch.BAND, sched, Nq, g, groups, P, Nk=Nk, band=band)
+    Sch.validate(ora, Sch.BAND, Nq, g, groups, Nk=Nk, band=band)
+    assert lib_s.lists() == _oracle_tuples(ora)
+    # atomic default walk on a band: descending
+    a = Schedule(0, _lib.ATOMIC, Nq, g, groups, P, Nk=Nk, band=band)
+    assert np.array_equal(a.steps, Schedule(0, Sch.DESC_Q, Nq, g, groups, P, Nk=Nk, band=band).steps)
+
+
+def test_band_schedule_rejections():
+    for sched in (Sch.SHIFT, Sch.SYM_SHIFT):
+        with pytest.raises(_lib.DashError) as ei:
+            Schedule(0, sched, 4, 1, 1, 4, band=(1, 0))
+        assert ei.value.status == _lib.ERR_UNSUPPORTED
+    for args in [dict(N=5, Nk=4, band=(1, 0)), dict(N=4, Nk=4, band=(-2, 0))]:
+        with pytest.raises(_lib.DashError) as ei:
+            Schedule(0, Sch.SERIAL, args["N"], 1, 1, 4, Nk=args["Nk"], band=args["band"])
+        assert ei.value.status == _lib.ERR_INVALID_ARG
+
+
+def test_window_argument_errors_need_no_gpu():
+    L = _lib.lib()
+    vp = ctypes.c_void_p
+    good = [vp(4096 * (i + 1)) for i in range(9)]
+    # a bounded window side needs Sk >= Sq; extents below -1 are invalid
+    assert L.dash_attn_bwd_window(*good, 1, 1, 1, 300, 200, 64, 0.0, 16, 0, _lib.AUTO, None, None) == _lib.ERR_INVALID_ARG
+    assert L.dash_attn_bwd_window(*good, 1, 1, 1, 300, 300, 64, 0.0, -2, 0, _lib.AUTO, None, None) == _lib.ERR_INVALID_ARG
+    assert L.dash_attn_fwd_window(*good[:5], 1, 1, 1, 300, 200, 64, 0.0, 16, -1, None) == _lib.ERR_INVALID_ARG
+    # empty batch: nothing launched
+    assert L.dash_attn_bwd_window(*([vp(0)] * 9), 0, 1, 1, 300, 300, 64, 0.0, 16, 0, _lib.AUTO, None, None) == 0
