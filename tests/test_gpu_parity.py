@@ -106,6 +106,46 @@ def test_workload_shapes_on_sampled_rows(case):
             assert torch.isfinite(t.float()).all()
 
 
+# The rectangular and windowed benchmark workloads at full size (bench.py's
+# launch configuration), on sampled query rows and key rows.
+FULL_SIZE_EXT = [  # name, B, Hq, Hkv, Sq, Sk, D, causal, window, schedules
+    ("x1_cross_q4096_k16384_d128", 1, 16, 16, 4096, 16384, 128, False, None, [DESC_Q, SHIFT, ATOMIC]),
+    ("x2_causal_q4096_k16384_d128", 1, 16, 16, 4096, 16384, 128, True, None, [DESC_Q, SYM_SHIFT, ATOMIC]),
+    ("w1_sliding_s16384_w4096_d128", 1, 16, 16, 16384, 16384, 128, True, (4095, 0), [SERIAL, DESC_Q, ATOMIC]),
+]
+
+
+@pytest.mark.parametrize("case", FULL_SIZE_EXT, ids=[c[0] for c in FULL_SIZE_EXT])
+def test_extended_workloads_on_sampled_rows(case):
+    name, B, Hq, Hkv, Sq, Sk, D, causal, window, scheds = case
+    say(f"[parity-full] {name}")
+    pb = DeviceProblem(B, Hq, Hkv, Sq, D, causal, Sk=Sk)
+    o, lse = attn_fwd(pb.q, pb.k, pb.v, causal, window=window)
+    torch.cuda.synchronize()
+    q64, k64, v64, do64 = pb.f64("q"), pb.f64("k"), pb.f64("v"), pb.f64("do")
+    b, hk, hq = 0, Hkv - 1, Hq - 1
+    qrows = sorted({0, 1, 127, 128, Sq // 2 + 5, Sq - 129, Sq - 1})
+    krows = sorted({0, 1, 127, 128, Sk // 3 + 7, Sk // 2 + 5, Sk - 129, Sk - 1})
+    stats = {hq: A.head_stats(q64, k64, v64, do64, b, hq, pb.scale, causal, window=window)}
+    say("  oracle stats done")
+    ref_dq = A.dq_rows(q64, k64, v64, do64, b, hq, qrows, pb.scale, causal, window=window)
+    ref_dk, ref_dv = A.dkdv_rows(q64, k64, v64, do64, b, hk, krows, pb.scale, causal, stats=stats, window=window)
+    got_lse = to_f64(lse[b, hq])
+    assert np.abs(got_lse - stats[hq][0]).max() <= TOL * max(1.0, np.abs(stats[hq][0]).max())
+    for sched in scheds:
+        say(f"  schedule {_lib.SCHEDULE_NAMES[sched]}")
+        dq, dk, dv = attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, causal, sched, opts=make_opts(sync_check=True),
+                              window=window)
+        torch.cuda.synchronize()
+        e_dq = rel_err(to_f64(dq[b, hq, qrows]), ref_dq)
+        e_dk = rel_err(to_f64(dk[b, hk, krows]), ref_dk)
+        e_dv = rel_err(to_f64(dv[b, hk, krows]), ref_dv)
+        say(f"    rel err dq {e_dq:.2e} dk {e_dk:.2e} dv {e_dv:.2e}")
+        assert max(e_dq, e_dk, e_dv) <= TOL
+        for t in (dq, dk, dv):
+            assert torch.isfinite(t.float()).all()
+
+
 def test_unsupported_shapes_are_rejected_before_launch():
     pb = DeviceProblem(1, 1, 1, 320, 64, True)
     o, lse = attn_fwd(pb.q, pb.k, pb.v, True)
