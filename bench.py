@@ -128,7 +128,8 @@ def main():
     # shift needs a full mask; symmetric shift pairs query tiles p, N-1-p and needs N even
     fast = ["shift"] if not causal else (["sym_shift"] if (S // tile) % 2 == 0 else [])
     if window is not None:
-        fast = []  # a band takes the list walks (the descending one is its shift)
+        # a sliding band (left, 0) also takes the band shift schedule
+        fast = ["shift"] if window[1] == 0 or causal else []
     det_names = ["serial", "desc_q"] + fast
     if args.schedules:
         det_names = [s for s in args.schedules.split(",") if s]

@@ -180,11 +180,18 @@ int dash_attn_bwd_qk(const void* q, const void* k, const void* v, const void* o,
  * is the causal one of dash_attn_bwd_qk (query tiles aligned with the
  * key/value tiles); a window of w rows reaches ceil(w / T) tiles off the
  * diagonal tile, and only tile pairs inside that band are scheduled.  SERIAL,
- * DESC_Q and ATOMIC (default walk DESC_Q) serve banded masks; AUTO runs
- * DESC_Q, whose descending walk reaches each dQ tile in ordinal order, one
- * step apart between neighbouring key/value tiles.  SHIFT and SYM_SHIFT are
- * DASH_ERR_UNSUPPORTED unless the window reduces to the full or causal mask.
- * Keys that no query sees get dK = dV = 0.
+ * DESC_Q and ATOMIC (default walk DESC_Q) serve every band; walked
+ * descending, the chains of neighbouring key/value tiles reach each dQ tile
+ * in ordinal order, one step apart.  SHIFT serves sliding bands (window
+ * right edge 0, left edge of 1 .. Nq-1 tiles) when Nk = Nq and the left
+ * extent is even, or Nk - Nq >= the left extent: units of left + 1 steps
+ * (an unclipped key/value tile; the pair of tiles clipped at the first and
+ * the last query tile; the symmetric shift of the corner triangle) are
+ * dealt round-robin over the workgroups, and each dQ tile ranks its
+ * contributors by lock-step position.  AUTO picks SHIFT where it applies,
+ * else DESC_Q (dash_schedule_choose_band).  SYM_SHIFT, and SHIFT elsewhere,
+ * are DASH_ERR_UNSUPPORTED unless the window reduces to the full or causal
+ * mask.  Keys that no query sees get dK = dV = 0.
  */
 int dash_attn_bwd_window(const void* q, const void* k, const void* v, const void* o, const void* dO,
                          const float* lse, void* dq, void* dk, void* dv,
@@ -226,7 +233,8 @@ int dash_schedule_build_qk(int mask, int schedule, int Nq, int Nk, int g, int gr
  * tile qi when -band_left <= kj - qi - (Nk - Nq) <= band_right (-1 leaves a
  * side unbounded; Nk >= Nq).  Key/value tiles that no query tile sees get
  * no chain; each dQ tile ranks its visible key/value tiles in ascending
- * order.  SERIAL, DESC_Q and ATOMIC only (DASH_ERR_UNSUPPORTED otherwise). */
+ * order.  SERIAL, DESC_Q and ATOMIC for every band; SHIFT for the sliding
+ * bands of dash_attn_bwd_window (DASH_ERR_UNSUPPORTED otherwise). */
 int dash_schedule_build_band(int schedule, int Nq, int Nk, int band_left, int band_right, int g, int groups,
                              int P, int xcd_local, int atomic_walk, int max_gang, dash_schedule** out);
 
@@ -270,6 +278,12 @@ int dash_schedule_choose(int mask, int N, int D, int g, int P, int* schedule, in
 /* Same for Nq query tiles and Nk key/value tiles: full mask -> SHIFT (gang of
  * min(Nq, Nk), capped at P); causal -> SYM_SHIFT when Nq is even, else DESC_Q. */
 int dash_schedule_choose_qk(int mask, int Nq, int Nk, int D, int g, int P, int* schedule, int* max_gang);
+
+/* Same for a band mask in tile units (as in dash_schedule_build_band): SHIFT
+ * where the band shift applies (measured faster than DESC_Q on MI355X for a
+ * 4096-key sliding window over 16384 tokens), else DESC_Q; *max_gang = 0. */
+int dash_schedule_choose_band(int Nq, int Nk, int band_left, int band_right, int D, int g, int P, int* schedule,
+                              int* max_gang);
 
 /* ---- misc -------------------------------------------------------------- */
 

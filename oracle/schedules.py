@@ -194,6 +194,8 @@ def build(mask: int, sched: int, N: int, g: int, groups: int, P: int, xcd_local:
                                         for (h, qi, k) in _chain(grp, g, kj, walk)]))
                 load[w] += g * len(walk)
         return out
+    if sched == SHIFT and mask == BAND:
+        return _band_shift(N, Nk, band, g, groups, P, xcd_local)
     if sched == SHIFT:
         if mask != FULL:
             raise ScheduleError("shift scheduling needs a full mask")
@@ -247,6 +249,79 @@ def build(mask: int, sched: int, N: int, g: int, groups: int, P: int, xcd_local:
             w = gang_slot(gang, p, n_gangs, gang_size, xcd_local, P, sched == SHIFT)
             for ch in chains:
                 out[w].extend(_flagged([(h, qi, kj, rank[(h, qi, kj)]) for (h, qi, kj) in ch]))
+    return out
+
+
+def band_shift_units(N: int, Nk: int, dl: int) -> list[list[tuple[int, list[int]]]]:
+    """Units of the shift schedule on a sliding-window band (dl, 0), one group.
+
+    Every unit is a list of chains (kj, walk of one head) of dl + 1 steps in
+    all, walked in descending query order: the chains of neighbouring
+    key/value tiles then visit each query tile one step apart.
+    * unclipped key/value tiles (their whole band inside the grid): one chain;
+    * with Nk - N >= dl, the tiles clipped at the first query tile (band
+      start before query tile 0, l steps) pair with those clipped at the last
+      one (dl + 1 - l steps); walked in that order each keeps its lock-step
+      slots, so the pair fills one unit;
+    * with Nk = N, the tiles clipped at the last query tile form a causal
+      triangle of side dl, which the symmetric shift covers with dl/2 units
+      of dl + 1 steps.
+    Other shapes raise ScheduleError (this implementation's reading: the
+    pages give no schedule for bands).
+    """
+    off = Nk - N
+    L = dl + 1
+    if dl < 1 or N < L:
+        raise ScheduleError("band shift needs 1 <= dl < Nq")
+    units = [[(kj, [kj - off + dl - t for t in range(L)])] for kj in range(off, off + N - dl)]
+    if off >= dl:
+        for ell in range(1, dl + 1):
+            kb, kt = off - dl - 1 + ell, off + N - dl - 1 + ell
+            units.append([(kb, [ell - 1 - t for t in range(ell)]), (kt, [N - 1 - t for t in range(L - ell)])])
+    elif off == 0 and dl % 2 == 0:
+        M, base = dl // 2, N - dl
+        for p in range(M):
+            a = [M + (p + t) % M for t in range(M)] + [p + s for s in range(M - p)]
+            b = [dl - 1 - s for s in range(p + 1)]
+            units.append([(base + p, [base + q for q in a]), (base + dl - 1 - p, [base + q for q in b])])
+    else:
+        raise ScheduleError("band shift needs Nk = Nq with an even band, or Nk - Nq >= the band")
+    return units
+
+
+def _band_shift(N: int, Nk: int, band, g: int, groups: int, P: int, xcd_local: bool) -> list[list[Step]]:
+    """Shift schedule on a sliding-window band: the units of every group are
+    dealt round-robin over the P workgroups ("pooled rounds"), unit i going
+    to workgroup i mod P in round i // P, so that the rounds stay full even
+    when P is not a multiple of the units per group.  A step's lock-step key
+    is its round times the unit length plus its position in the unit; each dQ
+    tile ranks its contributors by (key, kj)."""
+    dl, dr = band
+    if dr != 0 or dl is None:
+        raise ScheduleError("band shift needs a sliding-window band (dl, 0)")
+    units = band_shift_units(N, Nk, dl)
+    U, L = len(units), (dl + 1) * g
+    placed = []  # (workgroup, key0, group, unit)
+    for i in range(groups * U):
+        grp, u = divmod(i, U)
+        m = i % P
+        w = gang_slot(0, m, 1, P, xcd_local, P, True)
+        placed.append((w, (i // P) * L, grp, units[u]))
+    keys: dict[tuple[int, int], list[tuple[int, int]]] = {}
+    for w, key0, grp, chains in placed:
+        pos = key0
+        for kj, walk in chains:
+            for (h, qi, k) in _chain(grp, g, kj, walk):
+                keys.setdefault((h, qi), []).append((pos, k))
+                pos += 1
+    rank = {}
+    for (h, qi), lst in keys.items():
+        for o, (_, kj) in enumerate(sorted(lst)):
+            rank[(h, qi, kj)] = o
+    out: list[list[Step]] = [[] for _ in range(P)]
+    for w, key0, grp, chains in sorted(placed, key=lambda x: (x[0], x[1])):
+        for kj, walk in chains:
+            out[w].extend(_flagged([(h, qi, k, rank[(h, qi, k)]) for (h, qi, k) in _chain(grp, g, kj, walk)]))
     return out
 
 

@@ -35,7 +35,7 @@ EXPORTS = (
     "dash_attn_bwd_window", "dash_attn_bwd_workspace_bytes", "dash_schedule_build_band",
     "dash_attn_bwd_delta", "dash_schedule_build", "dash_schedule_build_qk", "dash_schedule_num_workgroups", "dash_schedule_num_steps", "dash_schedule_export",
     "dash_schedule_validate", "dash_schedule_simulate", "dash_schedule_free", "dash_schedule_choose",
-    "dash_schedule_choose_qk",
+    "dash_schedule_choose_qk", "dash_schedule_choose_band",
     "dash_status_string",
     "dash_last_error", "dash_device_info",
 )
@@ -78,6 +78,7 @@ def _declare(lib):
     lib.dash_attn_fwd_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
     lib.dash_attn_bwd_window.argtypes = [vp] * 9 + [i, i, i, i, i, i, f, i, i, i, ctypes.POINTER(BwdOpts), vp]
     lib.dash_schedule_build_band.argtypes = [i, i, i, i, i, i, i, i, i, i, i, ctypes.POINTER(vp)]
+    lib.dash_schedule_choose_band.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
     lib.dash_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, ctypes.POINTER(ctypes.c_size_t)]
     lib.dash_attn_bwd_delta.argtypes = [vp, vp, vp, i, i, i, i, vp]
     lib.dash_schedule_build.argtypes = [i, i, i, i, i, i, i, i, i, ctypes.POINTER(vp)]

@@ -301,6 +301,14 @@ int dash_schedule_choose_qk(int mask, int Nq, int Nk, int D, int g, int P, int* 
   return err.empty() ? DASH_OK : fail(DASH_ERR_INVALID_ARG, err);
 }
 
+int dash_schedule_choose_band(int Nq, int Nk, int band_left, int band_right, int D, int g, int P, int* schedule,
+                              int* max_gang) {
+  if (!schedule || !max_gang) return fail(DASH_ERR_INVALID_ARG, "null output");
+  if (band_left < -1 || band_right < -1) return fail(DASH_ERR_INVALID_ARG, "band extents must be >= -1");
+  std::string err = dash::choose_schedule(dash::kMaskBand, Nq, Nk, D, g, P, schedule, max_gang, band_left, band_right);
+  return err.empty() ? DASH_OK : fail(DASH_ERR_INVALID_ARG, err);
+}
+
 int dash_schedule_choose(int mask, int N, int D, int g, int P, int* schedule, int* max_gang) {
   return dash_schedule_choose_qk(mask, N, N, D, g, P, schedule, max_gang);
 }
@@ -408,7 +416,7 @@ static int bwd_impl(const void* q, const void* k, const void* v, const void* o, 
   const int g = Hq / Hkv;
   if (schedule == DASH_SCHED_AUTO) {
     int cap = 0;
-    std::string err = dash::choose_schedule(mask.kind, Nq, Nk, D, g, P, &schedule, &cap);
+    std::string err = dash::choose_schedule(mask.kind, Nq, Nk, D, g, P, &schedule, &cap, band_l, band_r);
     if (!err.empty()) return fail(DASH_ERR_INVALID_ARG, err);
     if (op.max_gang == 0) op.max_gang = cap;
   }

@@ -205,13 +205,97 @@ std::string build_gang(const Schedule& s, std::vector<std::vector<StepRec>>& per
   return {};
 }
 
+// Shift on a sliding-window band (dl, 0): units of dl + 1 steps per head
+// (an unclipped key/value tile; a pair of tiles clipped at the first and the
+// last query tile when Nk - Nq >= dl; the symmetric shift of the corner
+// triangle when Nk = Nq and dl is even), every chain walked in descending
+// query order.  The units of all groups are dealt round-robin over the
+// workgroups (unit i: workgroup i mod P, round i / P); a step's lock-step key
+// is round * unit length + its position in the unit, and each dQ tile ranks
+// its contributors by (key, kj).
+std::string build_band_shift(const Schedule& s, std::vector<std::vector<StepRec>>& per_wg) {
+  const int N = s.Nq, off = s.Nk - s.Nq, dl = s.band_l;
+  if (!band_shift_applies(s.Nq, s.Nk, s.band_l, s.band_r))
+    return "band shift needs a sliding band (right = 0, 1 <= left < Nq tiles) on a square grid with an even left "
+           "extent, or Nk - Nq >= left";
+  using Chain = std::pair<int, std::vector<int>>;
+  std::vector<std::vector<Chain>> units;
+  for (int kj = off; kj < off + N - dl; ++kj) {
+    std::vector<int> w;
+    for (int t = 0; t <= dl; ++t) w.push_back(kj - off + dl - t);
+    units.push_back({{kj, std::move(w)}});
+  }
+  if (off >= dl) {
+    for (int ell = 1; ell <= dl; ++ell) {
+      std::vector<int> wb, wt;
+      for (int t = 0; t < ell; ++t) wb.push_back(ell - 1 - t);
+      for (int t = 0; t < dl + 1 - ell; ++t) wt.push_back(N - 1 - t);
+      units.push_back({{off - dl - 1 + ell, std::move(wb)}, {off + N - dl - 1 + ell, std::move(wt)}});
+    }
+  } else {  // off == 0, dl even
+    const int M = dl / 2, base = N - dl;
+    for (int p = 0; p < M; ++p) {
+      std::vector<int> a, b;
+      for (int t = 0; t < M; ++t) a.push_back(base + M + (p + t) % M);
+      for (int q = p; q < M; ++q) a.push_back(base + q);
+      for (int q = dl - 1; q >= dl - 1 - p; --q) b.push_back(base + q);
+      units.push_back({{base + p, std::move(a)}, {base + dl - 1 - p, std::move(b)}});
+    }
+  }
+  const long long U = static_cast<long long>(units.size());
+  const long long L = static_cast<long long>(dl + 1) * s.g;
+  const long long total = U * s.groups;
+  // (head, qi) -> contributors (key, kj)
+  std::vector<std::vector<std::pair<long long, int>>> bucket(static_cast<size_t>(s.g) * s.groups * N);
+  for (long long i = 0; i < total; ++i) {
+    const int grp = static_cast<int>(i / U);
+    long long pos = (i / s.P) * L;
+    for (const Chain& ch : units[i % U])
+      for (int u = 0; u < s.g; ++u)
+        for (int qi : ch.second)
+          bucket[(static_cast<size_t>(grp) * s.g + u) * N + qi].push_back({pos++, ch.first});
+  }
+  std::vector<int32_t> rank(static_cast<size_t>(s.g) * s.groups * N * s.Nk, -1);
+  for (size_t hq = 0; hq < bucket.size(); ++hq) {
+    auto& v = bucket[hq];
+    std::sort(v.begin(), v.end());
+    for (size_t r = 0; r < v.size(); ++r) rank[hq * s.Nk + v[r].second] = static_cast<int32_t>(r);
+  }
+  std::vector<Triple> chain;
+  std::vector<int32_t> ords;
+  for (long long i = 0; i < total; ++i) {  // rounds in order, so every list is in key order
+    const int grp = static_cast<int>(i / U);
+    const int w = gang_slot(0, static_cast<int>(i % s.P), 1, s.P, s);
+    for (const Chain& ch : units[i % U]) {
+      chain.clear();
+      ords.clear();
+      for (int u = 0; u < s.g; ++u)
+        for (int qi : ch.second) {
+          const int head = grp * s.g + u;
+          chain.push_back({head, qi, ch.first});
+          ords.push_back(rank[(static_cast<size_t>(head) * N + qi) * s.Nk + ch.first]);
+        }
+      push_chain(per_wg[w], chain, ords);
+    }
+  }
+  return {};
+}
+
 }  // namespace
 
-std::string choose_schedule(int mask, int Nq, int Nk, int D, int g, int P, int* kind, int* max_gang) {
+bool band_shift_applies(int Nq, int Nk, int band_l, int band_r) {
+  const int off = Nk - Nq;
+  if (band_r != 0 || band_l < 1 || Nq < band_l + 1 || off < 0) return false;
+  return off >= band_l || (off == 0 && band_l % 2 == 0);
+}
+
+std::string choose_schedule(int mask, int Nq, int Nk, int D, int g, int P, int* kind, int* max_gang, int band_l,
+                            int band_r) {
   if (Nq < 1 || Nk < 1 || D < 1 || g < 1 || P < 1) return "sizes must be positive";
   if (mask == kMaskBand) {
     if (Nk < Nq) return "a band mask needs Sk >= Sq";
-    *kind = kDescQ;
+    // measured on MI355X: the band shift beats the descending walk (sliding window of 4096 over 16384 tokens)
+    *kind = band_shift_applies(Nq, Nk, band_l, band_r) ? kShift : kDescQ;
     *max_gang = 0;
     return "";
   }
@@ -253,7 +337,7 @@ std::string build_schedule(int mask, int kind, int Nq, int Nk, int g, int groups
     walk = (atomic_walk < 0) ? (mask == kMaskFull ? kSerial : kDescQ) : atomic_walk;
     if (walk < kSerial || walk > kSymShift) return "unknown atomic walk";
   }
-  if (walk == kShift && mask != kMaskFull) return "shift scheduling needs a full mask";
+  if (walk == kShift && mask == kMaskCausal) return "shift scheduling needs a full or band mask";
   if (walk == kSymShift && mask != kMaskCausal) return "symmetric shift needs a causal mask";
   if (walk == kSymShift && (Nq % 2)) return "symmetric shift needs an even tile count";
   Schedule s;
@@ -270,7 +354,9 @@ std::string build_schedule(int mask, int kind, int Nq, int Nk, int g, int groups
   s.band_l = mask == kMaskBand ? (band_l < 0 ? -1 : band_l) : -1;
   s.band_r = mask == kMaskBand ? (band_r < 0 ? -1 : band_r) : -1;
   std::vector<std::vector<StepRec>> per_wg(P);
-  std::string err = (walk == kSerial || walk == kDescQ) ? build_list_scheduled(s, per_wg) : build_gang(s, per_wg);
+  std::string err = (walk == kSerial || walk == kDescQ) ? build_list_scheduled(s, per_wg)
+                    : (walk == kShift && mask == kMaskBand) ? build_band_shift(s, per_wg)
+                                                             : build_gang(s, per_wg);
   if (!err.empty()) return err;
   s.offsets.resize(P + 1);
   size_t total = 0;

@@ -55,9 +55,13 @@ void visible_k(const Schedule& s, int qi, int* lo, int* hi);
 // Empty string if valid, else the first violation found.
 std::string validate_schedule(const Schedule& s);
 // The deterministic schedule (and gang cap) chosen for a shape; empty string
-// on success.  A band mask takes DESC_Q: walked descending, the chains of a
-// band reach each dQ tile in ordinal order, one step apart.
-std::string choose_schedule(int mask, int Nq, int Nk, int D, int g, int P, int* kind, int* max_gang);
+// on success.  A band mask (extents band_l, band_r in tiles) takes SHIFT where
+// the band shift applies (a sliding band: band_r = 0, and Nk = Nq with an
+// even band_l or Nk - Nq >= band_l, band_l < Nq), else DESC_Q.
+std::string choose_schedule(int mask, int Nq, int Nk, int D, int g, int P, int* kind, int* max_gang,
+                            int band_l = -1, int band_r = -1);
+// Whether the band shift covers a band (see build_schedule).
+bool band_shift_applies(int Nq, int Nk, int band_l, int band_r);
 // Unit-cost DAG simulation; returns false on deadlock.
 bool simulate_schedule(const Schedule& s, double c, double r, double* makespan, double* total_wait);
 

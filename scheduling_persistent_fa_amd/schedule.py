@@ -17,6 +17,15 @@ def choose(mask: int, N: int, D: int, g: int, P: int, Nk: int | None = None):
     return kind.value, cap.value
 
 
+def choose_band(Nq: int, Nk: int, band, D: int, g: int, P: int):
+    """(schedule, max_gang) the adaptive rule picks for a band mask with
+    (left, right) tile extents (None = unbounded side)."""
+    kind, cap = ctypes.c_int(), ctypes.c_int()
+    bl, br = (-1 if x is None else int(x) for x in band)
+    _lib.check(_lib.lib().dash_schedule_choose_band(Nq, Nk, bl, br, D, g, P, ctypes.byref(kind), ctypes.byref(cap)))
+    return kind.value, cap.value
+
+
 class Schedule:
     """Per-workgroup step lists built by ``dash_schedule_build``.
 

@@ -111,7 +111,7 @@ def test_workload_shapes_on_sampled_rows(case):
 FULL_SIZE_EXT = [  # name, B, Hq, Hkv, Sq, Sk, D, causal, window, schedules
     ("x1_cross_q4096_k16384_d128", 1, 16, 16, 4096, 16384, 128, False, None, [DESC_Q, SHIFT, ATOMIC]),
     ("x2_causal_q4096_k16384_d128", 1, 16, 16, 4096, 16384, 128, True, None, [DESC_Q, SYM_SHIFT, ATOMIC]),
-    ("w1_sliding_s16384_w4096_d128", 1, 16, 16, 16384, 16384, 128, True, (4095, 0), [SERIAL, DESC_Q, ATOMIC]),
+    ("w1_sliding_s16384_w4096_d128", 1, 16, 16, 16384, 16384, 128, True, (4095, 0), [SERIAL, DESC_Q, SHIFT, ATOMIC]),
 ]
 
 
@@ -323,7 +323,24 @@ WINDOWED = [  # name, B, Hq, Hkv, Sq, Sk, D, (left, right), tile (0 = library's 
     ("sliding_q250_k700_w100_d64_unseen_keys", 1, 2, 1, 250, 700, 64, (100, 0), 0),
     ("right_only_s200_w5_d128", 1, 2, 1, 200, 200, 128, (None, 5), 0),
     ("zero_width_q64_k200_d64", 1, 1, 1, 64, 200, 64, (0, 0), 0),
+    ("sliding_gqa_s1000_w200_d128_t64_band_shift", 1, 4, 2, 1000, 1000, 128, (200, 0), 64),
 ]
+
+
+def _band_shift_applies(Sq, Sk, window, tile):
+    """Whether the shift schedule covers this window (sliding band, see oracle.schedules)."""
+    from oracle import schedules as Sch
+    left, right = window
+    if left is None or right != 0:
+        return False
+    T = tile or (64 if min(Sq, Sk) < 512 else 128)
+    nk = -(-Sk // T)
+    nq = nk - (Sk - Sq) // T
+    try:
+        Sch.band_shift_units(nq, nk, -(-left // T))
+        return True
+    except Sch.ScheduleError:
+        return False
 
 
 @pytest.mark.parametrize("case", WINDOWED, ids=[c[0] for c in WINDOWED])
@@ -337,7 +354,8 @@ def test_windowed_masks_match_oracle(case):
     torch.cuda.synchronize()
     assert rel_err(to_f64(o), ref["o"]) <= TOL
     assert np.abs(to_f64(lse) - ref["lse"]).max() <= TOL * max(1.0, np.abs(ref["lse"]).max())
-    for sched in (SERIAL, DESC_Q, ATOMIC, AUTO):
+    scheds = [SERIAL, DESC_Q] + ([SHIFT] if _band_shift_applies(Sq, Sk, window, tile) else []) + [ATOMIC, AUTO]
+    for sched in scheds:
         say(f"  schedule {_lib.SCHEDULE_NAMES[sched]}")
         opts = make_opts(tile=tile, sync_check=True)
         dq, dk, dv = (torch.full_like(t, float("nan")) for t in (pb.q, pb.k, pb.v))

@@ -264,3 +264,35 @@ def test_window_argument_errors_need_no_gpu():
     assert L.dash_attn_fwd_window(*good[:5], 1, 1, 1, 300, 200, 64, 0.0, 16, -1, None) == _lib.ERR_INVALID_ARG
     # empty batch: nothing launched
     assert L.dash_attn_bwd_window(*([vp(0)] * 9), 0, 1, 1, 300, 300, 64, 0.0, 16, 0, _lib.AUTO, None, None) == 0
+
+
+@pytest.mark.parametrize("N,Nk,dl,g,groups,P,xcd", [(12, 12, 4, 1, 1, 10, True), (16, 16, 6, 2, 3, 7, False),
+                                                    (8, 20, 4, 1, 2, 5, True), (128, 128, 32, 1, 16, 256, True),
+                                                    (32, 64, 8, 2, 3, 50, True), (64, 64, 16, 4, 8, 256, False)])
+def test_band_shift_matches_oracle_exactly(N, Nk, dl, g, groups, P, xcd):
+    lib_s = Schedule(0, Sch.SHIFT, N, g, groups, P, xcd_local=xcd, Nk=Nk, band=(dl, 0))
+    lib_s.validate()
+    ora = Sch.build(Sch.BAND, Sch.SHIFT, N, g, groups, P, xcd_local=xcd, Nk=Nk, band=(dl, 0))
+    assert lib_s.lists() == _oracle_tuples(ora)
+
+
+def test_band_choice_rule():
+    from scheduling_persistent_fa_amd.schedule import choose_band
+    assert choose_band(128, 128, (32, 0), 128, 1, 256) == (_lib.SHIFT, 0)   # sliding window 4096 / 16384
+    assert choose_band(128, 128, (31, 0), 128, 1, 256) == (_lib.DESC_Q, 0)  # odd corner triangle
+    assert choose_band(8, 20, (4, 0), 128, 1, 256) == (_lib.SHIFT, 0)       # clipped pairs
+    assert choose_band(8, 10, (4, 0), 128, 1, 256) == (_lib.DESC_Q, 0)
+    assert choose_band(8, 8, (2, 1), 128, 1, 256) == (_lib.DESC_Q, 0)       # two-sided band
+    assert choose_band(8, 8, (None, 3), 128, 1, 256) == (_lib.DESC_Q, 0)
+    with pytest.raises(_lib.DashError):
+        choose_band(8, 4, (2, 0), 128, 1, 256)
+    # the rule agrees with where the oracle's band shift applies
+    for nq in range(1, 9):
+        for nk in range(nq, 14):
+            for dl in range(0, 9):
+                try:
+                    Sch.band_shift_units(nq, nk, dl)
+                    ok = dl >= 1
+                except Sch.ScheduleError:
+                    ok = False
+                assert (choose_band(nq, nk, (dl, 0), 64, 1, 16)[0] == _lib.SHIFT) == ok, (nq, nk, dl)

@@ -304,10 +304,35 @@ def test_descending_walk_is_a_shift_inside_a_sliding_window(n, dl):
 
 
 def test_band_rejects_gang_schedules_and_bad_extents():
-    for sched in (SHIFT, SYM_SHIFT):
+    for sched in (SHIFT, SYM_SHIFT):  # (shift needs an even band on a square grid)
         with pytest.raises(Sch.ScheduleError):
             Sch.build(Sch.BAND, sched, 4, 1, 1, 4, band=(1, 0))
     with pytest.raises(Sch.ScheduleError):
         Sch.build(Sch.BAND, SERIAL, 4, 1, 1, 4, band=(-1, 0))
     with pytest.raises(Sch.ScheduleError):
         Sch.build(Sch.BAND, SERIAL, 5, 1, 1, 4, Nk=4, band=(1, 0))
+
+
+@pytest.mark.parametrize("N,Nk,dl,g,groups,P", [(12, 12, 4, 1, 1, 10), (16, 16, 6, 2, 3, 7), (8, 20, 4, 1, 2, 5),
+                                                 (10, 13, 3, 1, 3, 12), (32, 32, 8, 1, 4, 64), (9, 9, 8, 1, 2, 5)])
+def test_band_shift_schedule(N, Nk, dl, g, groups, P):
+    # Shift inside a sliding-window band: valid, every unit dl + 1 steps per
+    # head, and with one round of units per group (P = units) no step waits in
+    # the unit-cost model with free reductions; pooled rounds keep every
+    # workgroup within one unit of the others.
+    lists = Sch.build(Sch.BAND, SHIFT, N, g, groups, P, Nk=Nk, band=(dl, 0))
+    Sch.validate(lists, Sch.BAND, N, g, groups, Nk=Nk, band=(dl, 0))
+    U = len(Sch.band_shift_units(N, Nk, dl))
+    L = (dl + 1) * g
+    lengths = sorted(len(l) for l in lists)
+    assert lengths[-1] - lengths[0] <= L
+    assert sum(lengths) == sum(len(l) for l in Sch.build(Sch.BAND, DESC_Q, N, g, groups, P, Nk=Nk, band=(dl, 0)))
+    one = Sch.build(Sch.BAND, SHIFT, N, g, 1, U, Nk=Nk, band=(dl, 0))
+    mk, wait = Sch.simulate(one, 1.0, 0.0)
+    assert wait == 0.0 and mk == L
+
+
+def test_band_shift_rejects_unsupported_bands():
+    for N, Nk, band in [(8, 8, (3, 0)), (8, 10, (4, 0)), (8, 8, (2, 1)), (4, 4, (4, 0))]:
+        with pytest.raises(Sch.ScheduleError):
+            Sch.build(Sch.BAND, SHIFT, N, 1, 1, 4, Nk=Nk, band=band)
