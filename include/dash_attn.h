@@ -102,7 +102,9 @@ typedef struct dash_bwd_opts {
   void* event_stop;          /* optional hipEvent_t recorded on `stream` just after it */
   int max_gang;              /* SHIFT / SYM_SHIFT (and their ATOMIC walks): cap on the gang size; a capped
                                 gang takes its key/value tiles (or tile pairs) in rounds, so more gangs run
-                                side by side.  0 = natural size (N, or N/2); negative = DASH_ERR_INVALID_ARG */
+                                side by side.  0 = natural size (N, or N/2); negative = DASH_ERR_INVALID_ARG.
+                                The band shift of dash_attn_bwd_window deals its units over all workgroups
+                                and ignores this cap. */
 } dash_bwd_opts;
 
 /*
