@@ -244,38 +244,40 @@ std::string build_band_shift(const Schedule& s, std::vector<std::vector<StepRec>
   }
   const long long U = static_cast<long long>(units.size());
   const long long L = static_cast<long long>(dl + 1) * s.g;
-  const long long total = U * s.groups;
-  // (head, qi) -> contributors (key, kj)
-  std::vector<std::vector<std::pair<long long, int>>> bucket(static_cast<size_t>(s.g) * s.groups * N);
-  for (long long i = 0; i < total; ++i) {
-    const int grp = static_cast<int>(i / U);
-    long long pos = (i / s.P) * L;
-    for (const Chain& ch : units[i % U])
-      for (int u = 0; u < s.g; ++u)
-        for (int qi : ch.second)
-          bucket[(static_cast<size_t>(grp) * s.g + u) * N + qi].push_back({pos++, ch.first});
-  }
-  std::vector<int32_t> rank(static_cast<size_t>(s.g) * s.groups * N * s.Nk, -1);
-  for (size_t hq = 0; hq < bucket.size(); ++hq) {
-    auto& v = bucket[hq];
-    std::sort(v.begin(), v.end());
-    for (size_t r = 0; r < v.size(); ++r) rank[hq * s.Nk + v[r].second] = static_cast<int32_t>(r);
-  }
+  // Groups are independent (their dQ tiles differ), so ranks are formed one
+  // group at a time: unit u of group grp is global unit i = grp * U + u, on
+  // workgroup i mod P in round i / P.
+  std::vector<std::vector<std::pair<long long, int>>> bucket(static_cast<size_t>(s.g) * N);  // (u, qi)
+  std::vector<int32_t> rank(static_cast<size_t>(s.g) * N * s.Nk, -1);                       // [u][qi][kj]
   std::vector<Triple> chain;
   std::vector<int32_t> ords;
-  for (long long i = 0; i < total; ++i) {  // rounds in order, so every list is in key order
-    const int grp = static_cast<int>(i / U);
-    const int w = gang_slot(0, static_cast<int>(i % s.P), 1, s.P, s);
-    for (const Chain& ch : units[i % U]) {
-      chain.clear();
-      ords.clear();
-      for (int u = 0; u < s.g; ++u)
-        for (int qi : ch.second) {
-          const int head = grp * s.g + u;
-          chain.push_back({head, qi, ch.first});
-          ords.push_back(rank[(static_cast<size_t>(head) * N + qi) * s.Nk + ch.first]);
-        }
-      push_chain(per_wg[w], chain, ords);
+  for (int grp = 0; grp < s.groups; ++grp) {
+    for (auto& v : bucket) v.clear();
+    for (long long u = 0; u < U; ++u) {
+      const long long i = grp * U + u;
+      long long pos = (i / s.P) * L;
+      for (const Chain& ch : units[u])
+        for (int h = 0; h < s.g; ++h)
+          for (int qi : ch.second) bucket[static_cast<size_t>(h) * N + qi].push_back({pos++, ch.first});
+    }
+    for (size_t hq = 0; hq < bucket.size(); ++hq) {
+      auto& v = bucket[hq];
+      std::sort(v.begin(), v.end());
+      for (size_t r = 0; r < v.size(); ++r) rank[hq * s.Nk + v[r].second] = static_cast<int32_t>(r);
+    }
+    for (long long u = 0; u < U; ++u) {
+      const long long i = grp * U + u;
+      const int w = gang_slot(0, static_cast<int>(i % s.P), 1, s.P, s);
+      for (const Chain& ch : units[u]) {
+        chain.clear();
+        ords.clear();
+        for (int h = 0; h < s.g; ++h)
+          for (int qi : ch.second) {
+            chain.push_back({grp * s.g + h, qi, ch.first});
+            ords.push_back(rank[(static_cast<size_t>(h) * N + qi) * s.Nk + ch.first]);
+          }
+        push_chain(per_wg[w], chain, ords);
+      }
     }
   }
   return {};
