@@ -149,7 +149,12 @@ int dash_attn_fwd_window(const void* q, const void* k, const void* v, void* o, f
  * backward kernel (one workgroup per compute unit; each key/value tile's
  * chain stays on one workgroup with dK/dV in registers, [summary] §2.1), and
  * the dQ fp32 -> bf16 finalize.  For the deterministic schedules the result
- * is bitwise identical from run to run and independent of num_workgroups.
+ * is bitwise identical from run to run.  It is also independent of
+ * num_workgroups whenever the accumulation order does not depend on it:
+ * always for SERIAL and DESC_Q, for SHIFT / SYM_SHIFT while the gang is not
+ * capped (a gang cap, given or chosen by AUTO, changes the order), and for
+ * the band shift of dash_attn_bwd_window while each group's units fit in one
+ * round.
  * `opts` may be NULL.
  */
 int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,

@@ -133,3 +133,26 @@ def test_auto_schedule_runs_the_chosen_schedule(causal, S, wgs):
     ref = A.backward(pb.f64("q"), pb.f64("k"), pb.f64("v"), pb.f64("do"), pb.scale, causal)
     for t, name in zip(got, ("dq", "dk", "dv")):
         assert rel_err(to_f64(t), ref[name]) <= TOL
+
+
+def test_windowed_schedules_fifty_runs_bit_identical():
+    # Sliding window of 512 keys over 2048 tokens (band of 4 tiles of 128):
+    # the band shift and the descending walk, 50 runs each; the descending
+    # walk is also independent of the workgroup count.
+    B, H, S, D, window = 2, 4, 2048, 128, (511, 0)
+    pb = DeviceProblem(B, H, H, S, D, True, seed=7)
+    o, lse = attn_fwd(pb.q, pb.k, pb.v, True, window=window)
+    for sched in (SHIFT, DESC_Q):
+        say(f"[determinism] sliding window {_lib.SCHEDULE_NAMES[sched]} x{RUNS}")
+        dq, dk, dv = attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, True, sched, opts=make_opts(sync_check=True),
+                              window=window)
+        ref = _digest(dq, dk, dv)
+        for _ in range(RUNS - 1):
+            attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, True, sched, dq=dq, dk=dk, dv=dv, window=window)
+            assert _digest(dq, dk, dv) == ref
+    digests = set()
+    for p in (256, 64, 37):
+        dq, dk, dv = attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, True, DESC_Q,
+                              opts=make_opts(num_workgroups=p, sync_check=True), window=window)
+        digests.add(_digest(dq, dk, dv))
+    assert len(digests) == 1
