@@ -7,6 +7,9 @@
     turns FETCH_SIZE / WRITE_SIZE counter runs of the backward kernel into HBM
     bytes per launch, each scaled by what the same counter reads for a plain
     copy of COPY_BYTES, and records the kernel-source digest they belong to.
+``python -m scheduling_persistent_fa_amd.profiling counters OUT.md "COMMANDS" DIR [DIR ...]``
+    writes the per-dispatch median of every counter of the backward kernel
+    found in the DIRs (one rocprofv3 --pmc pass each), with a few ratios.
 """
 from __future__ import annotations
 
@@ -89,8 +92,58 @@ def traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_bytes, wo
     print(json.dumps(rec))
 
 
+def _all_counters(prof_dir: str, name_filter: str):
+    per = {}
+    for r in csv.DictReader(open(_one(os.path.join(prof_dir, "**", "*counter_collection.csv")))):
+        if name_filter in r["Kernel_Name"]:
+            d = per.setdefault(r["Counter_Name"], {})
+            d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return {k: statistics.median(v.values()) for k, v in per.items()}
+
+
+# Ratios reported when their counters exist.  GRBM_GUI_ACTIVE is summed over
+# the 8 chiplets (XCDs), so kernel cycles = GRBM_GUI_ACTIVE / 8; the SQ busy and
+# LDS counters are summed over the 1024 SIMDs or the 256 CUs, the TCP counter
+# over the 256 CUs.  (label, numerator, units the numerator is summed over)
+_PER_KERNEL_CYCLE = [
+    ("MFMA busy, share of SIMD cycles", "SQ_VALU_MFMA_BUSY_CYCLES", 1024),
+    ("LDS indexed-access active, share of CU cycles", "SQ_LDS_IDX_ACTIVE", 256),
+    ("LDS bank-conflict stall, share of CU cycles", "SQ_LDS_BANK_CONFLICT", 256),
+    ("TCP pending stall, share of CU cycles", "TCP_PENDING_STALL_CYCLES", 256),
+]
+
+
+def counters_table(out_md: str, commands: str, dirs) -> None:
+    vals = {}
+    for d in dirs:
+        vals.update(_all_counters(d, BWD_KERNEL))
+    lines = [f"# Hardware counters of the persistent backward kernel — `{os.path.basename(out_md)}`", "",
+             "Commands (one counter pass per run):", "", "```", commands, "```", "",
+             "Median per dispatch of the backward kernel:", "", "| counter | value |", "|---|---|"]
+    for k in sorted(vals):
+        lines.append(f"| {k} | {vals[k]:.4g} |")
+    lines += ["", "| ratio | value |", "|---|---|"]
+    if vals.get("GRBM_GUI_ACTIVE", 0) > 0:
+        cycles = vals["GRBM_GUI_ACTIVE"] / 8
+        lines.append(f"| kernel cycles (GRBM_GUI_ACTIVE / 8) | {cycles:.4g} |")
+        for label, num, units in _PER_KERNEL_CYCLE:
+            if num in vals:
+                lines.append(f"| {label} | {vals[num] / (cycles * units):.3f} |")
+    if "SQ_LDS_BANK_CONFLICT" in vals and vals.get("SQ_LDS_IDX_ACTIVE", 0) > 0:
+        lines.append(f"| LDS bank-conflict cycles per LDS-active cycle | "
+                     f"{vals['SQ_LDS_BANK_CONFLICT'] / vals['SQ_LDS_IDX_ACTIVE']:.3f} |")
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in vals and vals.get("SQ_INSTS_MFMA", 0) > 0:
+        lines.append(f"| MFMA busy cycles per MFMA instruction | "
+                     f"{vals['SQ_VALU_MFMA_BUSY_CYCLES'] / vals['SQ_INSTS_MFMA']:.1f} |")
+    if "TCC_HIT" in vals and "TCC_MISS" in vals:
+        lines.append(f"| L2 hit rate | {vals['TCC_HIT'] / (vals['TCC_HIT'] + vals['TCC_MISS']):.3f} |")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
-    if sys.argv[1] == "stats":
+    if sys.argv[1] == "counters":
+        counters_table(sys.argv[2], sys.argv[3], sys.argv[4:])
+    elif sys.argv[1] == "stats":
         stats_table(sys.argv[2], sys.argv[3], sys.argv[4])
     elif sys.argv[1] == "traffic":
         traffic(*sys.argv[2:10])
