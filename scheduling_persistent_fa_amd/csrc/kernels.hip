@@ -604,22 +604,22 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
       {
         // S = Q K^T and dP = dO V^T for query rows 32*hf .. +31 x this pair's 32 key/value columns.
         f32x16 s = f32x16{}, dp = f32x16{};
-        constexpr int NPART = DC >= 8 ? 4 : 2;  // operands are read in parts to bound register use
-        constexpr int HC = DC / NPART;
+        // One 16-wide d chunk at a time, double-buffered: chunk c+1's Q, dO and
+        // K operands are read while chunk c's two MFMAs run.
+        bf16x8 aq[2], ado[2], bk[2];
+        auto fetch = [&](int c, int sl) {
+          aq[sl] = lds_row8(sq + o_rowq + 32 * c);
+          ado[sl] = lds_row8(sdo + o_rowq + 32 * c);
+          bk[sl] = lds_row8(base + OFF_K + o_rowk + 32 * c);
+        };
+        fetch(0, 0);
 #pragma unroll
-        for (int half = 0; half < NPART; ++half) {
-          bf16x8 aq[HC], ado[HC], bk[HC];
-#pragma unroll
-          for (int c = 0; c < HC; ++c) {
-            aq[c] = lds_row8(sq + o_rowq + 32 * (half * HC + c));
-            ado[c] = lds_row8(sdo + o_rowq + 32 * (half * HC + c));
-            bk[c] = lds_row8(base + OFF_K + o_rowk + 32 * (half * HC + c));
-          }
-#pragma unroll
-          for (int c = 0; c < HC; ++c) {
-            s = mfma32(aq[c], bk[c], s);
-            dp = mfma32(ado[c], vb[half * HC + c], dp);
-          }
+        for (int c = 0; c < DC; ++c) {
+          if (c + 1 < DC) fetch(c + 1, (c + 1) & 1);
+          __builtin_amdgcn_sched_barrier(0);
+          s = mfma32(aq[c & 1], bk[c & 1], s);
+          dp = mfma32(ado[c & 1], vb[c], dp);
+          __builtin_amdgcn_sched_barrier(0);
         }
         // P = exp2(S*scale*log2e - LSE*log2e); dS = P * (dP - Delta); both to LDS transposed.
         // Element (8j + e) of this lane has key - diagonal key = rel - (8j + e); under
@@ -675,7 +675,48 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
       }
       __syncthreads();  // B2: P^T, dS^T complete
 
-      // dQ partial = dS K over all T key/value rows, for this wave's C tiles.
+      const int blk = qi * SUBS + sub;
+      float* wsb = a.ws + ((size_t)head * nblk + blk) * (size_t)(M * D);
+      int* semp = a.sem + ((size_t)head * nblk + blk) * kSemPerBlock + w;
+      // First look at this block's semaphore now, so that its latency is hidden
+      // behind the dK/dV and dQ contractions (in the lockstep schedules the
+      // predecessor has usually released it by now); the wait below only polls
+      // if not.
+      int sem_seen = 0;
+      if constexpr (!ATOMIC) sem_seen = __hip_atomic_load(semp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // dV += P^T dO, dK += dS^T Q over the block's 64 query rows, d half hf.
+      // Lightly software-pipelined: the next chunk's P^T/dS^T rows and each
+      // B operand are read one MFMA ahead of their use (scheduling barriers
+      // keep that order), which hides part of the LDS latency.
+      {
+        bf16x8 ap[2], ads[2];
+        ap[0] = lds_row8(base + OFF_PT + o_rowt);
+        ads[0] = lds_row8(base + OFF_DS + o_rowt);
+#pragma unroll
+        for (int c = 0; c < QC; ++c) {
+          const int sl = c & 1;
+          bf16x8 bdo[DH], bq[DH];
+          bdo[0] = lds_tr8_at(sdo + o_trq_h + 16 * c * PQ, PQ);
+          bq[0] = lds_tr8_at(sq + o_trq_h + 16 * c * PQ, PQ);
+          if (c + 1 < QC) {
+            ap[sl ^ 1] = lds_row8(base + OFF_PT + o_rowt + 32 * (c + 1));
+            ads[sl ^ 1] = lds_row8(base + OFF_DS + o_rowt + 32 * (c + 1));
+          }
+#pragma unroll
+          for (int j = 0; j < DH; ++j) {
+            if (j + 1 < DH) {
+              bdo[j + 1] = lds_tr8_at(sdo + o_trq_h + 16 * c * PQ + 64 * (j + 1), PQ);
+              bq[j + 1] = lds_tr8_at(sq + o_trq_h + 16 * c * PQ + 64 * (j + 1), PQ);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            dv_acc[j] = mfma32(ap[sl], bdo[j], dv_acc[j]);
+            dk_acc[j] = mfma32(ads[sl], bq[j], dk_acc[j]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+      // dQ partial = dS K over all T key/value rows, for this wave's C tiles
+      // (after the dK/dV contraction, so that the partial is not live there).
       f32x16 dq[TPW];
       {
         bf16x8 bk[KC];
@@ -691,21 +732,21 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
             }
             const LDS char* pds = base + OFF_DS + o_trs + qb * 64;
             f32x16 acc = f32x16{};
+            // the dS^T operand of chunk c+1 is read while chunk c's MFMA runs
+            bf16x8 ads2[2];
+            ads2[0] = lds_tr8_at(pds, PS);
 #pragma unroll
-            for (int c = 0; c < KC; ++c) acc = mfma32(lds_tr8_at(pds + 16 * c * PS, PS), bk[c], acc);
+            for (int c = 0; c < KC; ++c) {
+              if (c + 1 < KC) ads2[(c + 1) & 1] = lds_tr8_at(pds + 16 * (c + 1) * PS, PS);
+              __builtin_amdgcn_sched_barrier(0);
+              acc = mfma32(ads2[c & 1], bk[c], acc);
+              __builtin_amdgcn_sched_barrier(0);
+            }
             dq[ti] = acc;
           }
         }
       }
 
-      const int blk = qi * SUBS + sub;
-      float* wsb = a.ws + ((size_t)head * nblk + blk) * (size_t)(M * D);
-      int* semp = a.sem + ((size_t)head * nblk + blk) * kSemPerBlock + w;
-      // First look at this block's semaphore now, so that its latency is hidden
-      // behind the dK/dV contraction (in the lockstep schedules the predecessor
-      // has usually released it by now); the wait below only polls if not.
-      int sem_seen = 0;
-      if constexpr (!ATOMIC) sem_seen = __hip_atomic_load(semp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if constexpr (ATOMIC) {
 #pragma unroll
         for (int ti = 0; ti < TPW; ++ti) {
@@ -719,23 +760,6 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
         }
       }
 
-      // dV += P^T dO, dK += dS^T Q over the block's 64 query rows, d half hf.
-#pragma unroll
-      for (int c = 0; c < QC; ++c) {
-        const bf16x8 ap = lds_row8(base + OFF_PT + o_rowt + 32 * c);
-        const bf16x8 ads = lds_row8(base + OFF_DS + o_rowt + 32 * c);
-        bf16x8 bdo[DH], bq[DH];
-#pragma unroll
-        for (int j = 0; j < DH; ++j) {
-          bdo[j] = lds_tr8_at(sdo + o_trq_h + 16 * c * PQ + 64 * j, PQ);
-          bq[j] = lds_tr8_at(sq + o_trq_h + 16 * c * PQ + 64 * j, PQ);
-        }
-#pragma unroll
-        for (int j = 0; j < DH; ++j) {
-          dv_acc[j] = mfma32(ap, bdo[j], dv_acc[j]);
-          dk_acc[j] = mfma32(ads, bq[j], dk_acc[j]);
-        }
-      }
       // The other buffer is free (read before B1): stage the prefetched block.
       store_block(buf ^ 1);
       buf ^= 1;
