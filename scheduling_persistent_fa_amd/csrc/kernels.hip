@@ -390,7 +390,11 @@ constexpr int bwd_threads() {
 
 // LEFT: the window has a left edge (a band other than causal / full): each
 // element then needs a second comparison, which the other masks skip.
-template <int D, int T, bool ATOMIC, bool LEFT>
+// LATE: the pending dQ block is finished after the dK/dV contraction instead
+// of right after the S/dP phase, which gives its reads more time to land but
+// issues its writes, and so its release, later (measured faster for the
+// low-wait shift schedule on a full mask, slower for the causal ones).
+template <int D, int T, bool ATOMIC, bool LEFT, bool LATE>
 __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
   constexpr int NP = T / 32;          // wave pairs; pair p owns key/value rows 32p .. 32p+31
   constexpr int NW = 2 * NP;          // waves
@@ -648,7 +652,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
           *(LDS bf16x4*)(base + OFF_DS + o_stt + 16 * j) = ts;
         }
       }
-      if constexpr (!ATOMIC) {
+      if constexpr (!ATOMIC && !LATE) {
         // Finish the pending block: its predecessor's partial has arrived.  The
         // sum is formed on every path so that no path leaves the reads pending.
         // (A select, not a multiply by zero: a value read without a predecessor
@@ -714,6 +718,31 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
             __builtin_amdgcn_sched_barrier(0);
           }
         }
+      }
+      if constexpr (!ATOMIC && LATE) {
+        // Finish the pending block here (LATE: after the dK/dV contraction).  The
+        // sum is formed on every path so that no path leaves the reads pending.
+        // (A select, not a multiply by zero: a value read without a predecessor
+        // is arbitrary bits, possibly NaN.)
+        if (has_tiles) {  // compile-time true when the tiles divide evenly over the waves
+#pragma unroll
+          for (int ti = 0; ti < TPW; ++ti) {
+            const int t_idx = w + NW * ti;
+            const __amdgpu_buffer_rsrc_t rs = ws_rsrc(((EVEN || t_idx < NQT) ? p_ws : a.dummy) + t_idx * 1024);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              f32x4 v4;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int r = 4 * q4 + e;
+                v4[e] = p_add ? pdq[ti][r] + pprev[ti][r] : pdq[ti][r];
+              }
+              __builtin_amdgcn_raw_buffer_store_b128(v4, rs, (q4 * 64 + lane) * 16, 0, kDeviceScope);
+            }
+          }
+        }
+        r_sem = p_sem;
+        r_val = p_val;
       }
       // dQ partial = dS K over all T key/value rows, for this wave's C tiles
       // (after the dK/dV contraction, so that the partial is not live there).
@@ -960,17 +989,20 @@ hipError_t launch_bwd(const BwdLaunch& L, hipStream_t st) {
   a.diag_off = L.diag_off;
   dim3 grid(L.P);
   const bool left = a.wl < kUnbounded;
-#define DASH_BWD_CASE(D_, T_)                                                                        \
-  if (L.D == D_ && L.T == T_) {                                                                      \
-    const dim3 block(bwd_threads<T_>());                                                             \
-    if (L.atomic) {                                                                                  \
-      if (left) hipLaunchKernelGGL((bwd_kernel<D_, T_, true, true>), grid, block, 0, st, a);         \
-      else hipLaunchKernelGGL((bwd_kernel<D_, T_, true, false>), grid, block, 0, st, a);             \
-    } else {                                                                                         \
-      if (left) hipLaunchKernelGGL((bwd_kernel<D_, T_, false, true>), grid, block, 0, st, a);        \
-      else hipLaunchKernelGGL((bwd_kernel<D_, T_, false, false>), grid, block, 0, st, a);            \
-    }                                                                                                \
-    return hipGetLastError();                                                                        \
+#define DASH_BWD_CASE(D_, T_)                                                                             \
+  if (L.D == D_ && L.T == T_) {                                                                           \
+    const dim3 block(bwd_threads<T_>());                                                                  \
+    if (L.atomic) {                                                                                       \
+      if (left) hipLaunchKernelGGL((bwd_kernel<D_, T_, true, true, false>), grid, block, 0, st, a);       \
+      else hipLaunchKernelGGL((bwd_kernel<D_, T_, true, false, false>), grid, block, 0, st, a);           \
+    } else if (L.late_finish) {                                                                           \
+      if (left) hipLaunchKernelGGL((bwd_kernel<D_, T_, false, true, true>), grid, block, 0, st, a);       \
+      else hipLaunchKernelGGL((bwd_kernel<D_, T_, false, false, true>), grid, block, 0, st, a);           \
+    } else {                                                                                              \
+      if (left) hipLaunchKernelGGL((bwd_kernel<D_, T_, false, true, false>), grid, block, 0, st, a);      \
+      else hipLaunchKernelGGL((bwd_kernel<D_, T_, false, false, false>), grid, block, 0, st, a);          \
+    }                                                                                                     \
+    return hipGetLastError();                                                                             \
   }
   DASH_BWD_CASE(128, 128)
   DASH_BWD_CASE(64, 128)
@@ -980,26 +1012,36 @@ hipError_t launch_bwd(const BwdLaunch& L, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
+namespace {
+// Workgroups per CU of every variant of one (D, T, atomic) family (all must fit).
+template <int D, int T, bool ATOMIC>
+hipError_t min_occupancy(int* per_cu) {
+  const int nt = bwd_threads<T>();
+  int v[4] = {0, 0, 0, 0};
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&v[0], bwd_kernel<D, T, ATOMIC, false, false>, nt, 0);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&v[1], bwd_kernel<D, T, ATOMIC, true, false>, nt, 0);
+  if (e == hipSuccess && !ATOMIC)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&v[2], bwd_kernel<D, T, ATOMIC, false, !ATOMIC>, nt, 0);
+  if (e == hipSuccess && !ATOMIC)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&v[3], bwd_kernel<D, T, ATOMIC, true, !ATOMIC>, nt, 0);
+  *per_cu = ATOMIC ? std::min(v[0], v[1]) : std::min(std::min(v[0], v[1]), std::min(v[2], v[3]));
+  return e;
+}
+}  // namespace
+
 hipError_t bwd_kernel_fits(int D, int T, bool atomic, int num_cu, int P, bool* fits) {
-  // Both mask variants of the kernel must fit.
-  int per_cu = 0, per_cu2 = 0;
-  hipError_t e = hipErrorInvalidValue, e2 = hipErrorInvalidValue;
-#define DASH_OCC_CASE(D_, T_)                                                                                   \
-  if (D == D_ && T == T_) {                                                                                     \
-    const int nt = bwd_threads<T_>();                                                                           \
-    e = atomic ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_kernel<D_, T_, true, true>, nt, 0)   \
-               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_kernel<D_, T_, false, true>, nt, 0); \
-    e2 = atomic ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu2, bwd_kernel<D_, T_, true, false>, nt, 0) \
-                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu2, bwd_kernel<D_, T_, false, false>, nt, 0); \
-  }
+  int per_cu = 0;
+  hipError_t e = hipErrorInvalidValue;
+#define DASH_OCC_CASE(D_, T_) \
+  if (D == D_ && T == T_) e = atomic ? min_occupancy<D_, T_, true>(&per_cu) : min_occupancy<D_, T_, false>(&per_cu);
   DASH_OCC_CASE(128, 128)
   DASH_OCC_CASE(64, 128)
   DASH_OCC_CASE(128, 64)
   DASH_OCC_CASE(64, 64)
 #undef DASH_OCC_CASE
   if (e != hipSuccess) return e;
-  if (e2 != hipSuccess) return e2;
-  *fits = (long long)std::min(per_cu, per_cu2) * num_cu >= P;
+  *fits = (long long)per_cu * num_cu >= P;
   return hipSuccess;
 }
 
