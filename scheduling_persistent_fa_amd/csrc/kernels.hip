@@ -719,6 +719,13 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
           }
         }
       }
+      if constexpr (!ATOMIC && !LATE) {
+        // Release the block finished after the S/dP phase as soon as its writes
+        // have had the dK/dV contraction to complete (successors wait on it).
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (r_sem != nullptr && lane == 0) __hip_atomic_store(r_sem, r_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        r_sem = nullptr;
+      }
       if constexpr (!ATOMIC && LATE) {
         // Finish the pending block here (LATE: after the dK/dV contraction).  The
         // sum is formed on every path so that no path leaves the reads pending.
@@ -794,7 +801,8 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
       buf ^= 1;
 
       if constexpr (!ATOMIC) {
-        // Release the block finished in this sub-step once its writes are complete.
+        // Release the block finished in this sub-step once its writes are complete
+        // (LATE; the early variant released it after the dK/dV contraction).
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         if (r_sem != nullptr && lane == 0) __hip_atomic_store(r_sem, r_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         r_sem = nullptr;
