@@ -532,9 +532,6 @@ static int bwd_impl(const void* q, const void* k, const void* v, const void* o, 
   bl.diag_off = tg.diag_off;
   bl.P = P;
   bl.atomic = atomic;
-  // Measured on MI355X: finishing the pending dQ block late pays off for the
-  // shift schedule on a full mask (few semaphore waits), not for the others.
-  bl.late_finish = !atomic && schedule == DASH_SCHED_SHIFT && mask.kind == dash::kMaskFull;
   // Key/value tiles that no query tile sees have no chain: their dK/dV are zero.
   if (band_l >= 0 && tg.diag_off > band_l) {
     st = zero_bf16(dk, kv_elems, D, strm);

@@ -343,16 +343,17 @@ __global__ __launch_bounds__(256) void delta_kernel(const __bf16* __restrict__ o
 // semaphores are only touched with device-scope relaxed atomic loads and
 // stores, which bypass the chiplet-local caches that are not coherent across
 // the device; no cache write-back or invalidate is issued.  Each wave that
-// holds dQ tiles
-//   1. spins until sem == ordinal;
-//   2. issues the loads of its tiles of the block (ordinal > 0), runs its
-//      dK/dV contraction while they are in flight, adds its partial and
-//      writes the tiles back;
-// and at the next sub-step's second barrier -- after every wave has waited
-// for all of its outstanding vector memory operations, so the writes are
-// complete at device scope -- one lane stores sem = ordinal + 1.  Deferring
-// the release overlaps the write latency with the next sub-step's compute;
-// it never waits on another workgroup, so no cycle can form.
+// holds dQ tiles, for the block computed in sub-step s:
+//   1. at the end of s, spins until sem == ordinal (usually already seen by
+//      an early read), then issues the loads of its tiles of the block
+//      (ordinal > 0);
+//   2. after the S/dP phase of s+1, adds its partial and writes the tiles
+//      back;
+//   3. after the dK/dV contraction of s+1 -- once the wave has waited for all
+//      of its outstanding vector memory operations, so the writes are
+//      complete at device scope -- one lane stores sem = ordinal + 1.
+// Deferring the writes and the release overlaps their latency with compute;
+// the release never waits on another workgroup, so no cycle can form.
 // ---------------------------------------------------------------------------
 struct BwdArgs {
   const __bf16* q;
@@ -390,11 +391,7 @@ constexpr int bwd_threads() {
 
 // LEFT: the window has a left edge (a band other than causal / full): each
 // element then needs a second comparison, which the other masks skip.
-// LATE: the pending dQ block is finished after the dK/dV contraction instead
-// of right after the S/dP phase, which gives its reads more time to land but
-// issues its writes, and so its release, later (measured faster for the
-// low-wait shift schedule on a full mask, slower for the causal ones).
-template <int D, int T, bool ATOMIC, bool LEFT, bool LATE>
+template <int D, int T, bool ATOMIC, bool LEFT>
 __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
   constexpr int NP = T / 32;          // wave pairs; pair p owns key/value rows 32p .. 32p+31
   constexpr int NW = 2 * NP;          // waves
@@ -652,7 +649,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
           *(LDS bf16x4*)(base + OFF_DS + o_stt + 16 * j) = ts;
         }
       }
-      if constexpr (!ATOMIC && !LATE) {
+      if constexpr (!ATOMIC) {
         // Finish the pending block: its predecessor's partial has arrived.  The
         // sum is formed on every path so that no path leaves the reads pending.
         // (A select, not a multiply by zero: a value read without a predecessor
@@ -719,37 +716,12 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
           }
         }
       }
-      if constexpr (!ATOMIC && !LATE) {
+      if constexpr (!ATOMIC) {
         // Release the block finished after the S/dP phase as soon as its writes
         // have had the dK/dV contraction to complete (successors wait on it).
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         if (r_sem != nullptr && lane == 0) __hip_atomic_store(r_sem, r_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         r_sem = nullptr;
-      }
-      if constexpr (!ATOMIC && LATE) {
-        // Finish the pending block here (LATE: after the dK/dV contraction).  The
-        // sum is formed on every path so that no path leaves the reads pending.
-        // (A select, not a multiply by zero: a value read without a predecessor
-        // is arbitrary bits, possibly NaN.)
-        if (has_tiles) {  // compile-time true when the tiles divide evenly over the waves
-#pragma unroll
-          for (int ti = 0; ti < TPW; ++ti) {
-            const int t_idx = w + NW * ti;
-            const __amdgpu_buffer_rsrc_t rs = ws_rsrc(((EVEN || t_idx < NQT) ? p_ws : a.dummy) + t_idx * 1024);
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-              f32x4 v4;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int r = 4 * q4 + e;
-                v4[e] = p_add ? pdq[ti][r] + pprev[ti][r] : pdq[ti][r];
-              }
-              __builtin_amdgcn_raw_buffer_store_b128(v4, rs, (q4 * 64 + lane) * 16, 0, kDeviceScope);
-            }
-          }
-        }
-        r_sem = p_sem;
-        r_val = p_val;
       }
       // dQ partial = dS K over all T key/value rows, for this wave's C tiles
       // (after the dK/dV contraction, so that the partial is not live there).
@@ -801,11 +773,6 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
       buf ^= 1;
 
       if constexpr (!ATOMIC) {
-        // Release the block finished in this sub-step once its writes are complete
-        // (LATE; the early variant released it after the dK/dV contraction).
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        if (r_sem != nullptr && lane == 0) __hip_atomic_store(r_sem, r_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        r_sem = nullptr;
         // Wait for this block's predecessor, then start reading its partial.  (The
         // early value is consumed on every path, so it is never left pending.)
         const bool ready = __builtin_amdgcn_readfirstlane(sem_seen) == ord;
@@ -997,20 +964,17 @@ hipError_t launch_bwd(const BwdLaunch& L, hipStream_t st) {
   a.diag_off = L.diag_off;
   dim3 grid(L.P);
   const bool left = a.wl < kUnbounded;
-#define DASH_BWD_CASE(D_, T_)                                                                             \
-  if (L.D == D_ && L.T == T_) {                                                                           \
-    const dim3 block(bwd_threads<T_>());                                                                  \
-    if (L.atomic) {                                                                                       \
-      if (left) hipLaunchKernelGGL((bwd_kernel<D_, T_, true, true, false>), grid, block, 0, st, a);       \
-      else hipLaunchKernelGGL((bwd_kernel<D_, T_, true, false, false>), grid, block, 0, st, a);           \
-    } else if (L.late_finish) {                                                                           \
-      if (left) hipLaunchKernelGGL((bwd_kernel<D_, T_, false, true, true>), grid, block, 0, st, a);       \
-      else hipLaunchKernelGGL((bwd_kernel<D_, T_, false, false, true>), grid, block, 0, st, a);           \
-    } else {                                                                                              \
-      if (left) hipLaunchKernelGGL((bwd_kernel<D_, T_, false, true, false>), grid, block, 0, st, a);      \
-      else hipLaunchKernelGGL((bwd_kernel<D_, T_, false, false, false>), grid, block, 0, st, a);          \
-    }                                                                                                     \
-    return hipGetLastError();                                                                             \
+#define DASH_BWD_CASE(D_, T_)                                                                        \
+  if (L.D == D_ && L.T == T_) {                                                                      \
+    const dim3 block(bwd_threads<T_>());                                                             \
+    if (L.atomic) {                                                                                  \
+      if (left) hipLaunchKernelGGL((bwd_kernel<D_, T_, true, true>), grid, block, 0, st, a);         \
+      else hipLaunchKernelGGL((bwd_kernel<D_, T_, true, false>), grid, block, 0, st, a);             \
+    } else {                                                                                         \
+      if (left) hipLaunchKernelGGL((bwd_kernel<D_, T_, false, true>), grid, block, 0, st, a);        \
+      else hipLaunchKernelGGL((bwd_kernel<D_, T_, false, false>), grid, block, 0, st, a);            \
+    }                                                                                                \
+    return hipGetLastError();                                                                        \
   }
   DASH_BWD_CASE(128, 128)
   DASH_BWD_CASE(64, 128)
@@ -1025,15 +989,10 @@ namespace {
 template <int D, int T, bool ATOMIC>
 hipError_t min_occupancy(int* per_cu) {
   const int nt = bwd_threads<T>();
-  int v[4] = {0, 0, 0, 0};
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&v[0], bwd_kernel<D, T, ATOMIC, false, false>, nt, 0);
-  if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&v[1], bwd_kernel<D, T, ATOMIC, true, false>, nt, 0);
-  if (e == hipSuccess && !ATOMIC)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&v[2], bwd_kernel<D, T, ATOMIC, false, !ATOMIC>, nt, 0);
-  if (e == hipSuccess && !ATOMIC)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&v[3], bwd_kernel<D, T, ATOMIC, true, !ATOMIC>, nt, 0);
-  *per_cu = ATOMIC ? std::min(v[0], v[1]) : std::min(std::min(v[0], v[1]), std::min(v[2], v[3]));
+  int v[2] = {0, 0};
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&v[0], bwd_kernel<D, T, ATOMIC, false>, nt, 0);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&v[1], bwd_kernel<D, T, ATOMIC, true>, nt, 0);
+  *per_cu = std::min(v[0], v[1]);
   return e;
 }
 }  // namespace

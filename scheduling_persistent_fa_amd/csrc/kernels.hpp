@@ -31,7 +31,6 @@ struct BwdLaunch {
   int nblk;      // 64-row dQ workspace blocks per query head
   int diag_off;  // windowed masks: query tile qi's diagonal runs through key/value tile qi + diag_off
   bool atomic;
-  bool late_finish;  // deterministic: finish the pending dQ block after the dK/dV contraction
 };
 
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
