@@ -88,6 +88,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t ws_rsrc(const float* tile) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(tile), (short)0, 4096, 0x00020000);
 }
 
+// A pointer that is the same in every lane, read from the first lane so that
+// the compiler keeps it in scalar registers (a descriptor built from it then
+// needs no per-lane loop).
+template <class X>
+__device__ __forceinline__ X* uniform_ptr(X* p) {
+  const unsigned long long u = (unsigned long long)p;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)u);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(u >> 32));
+  return (X*)(((unsigned long long)hi << 32) | lo);
+}
+
 // Keeps a value opaque to the optimiser, so that addresses formed from it
 // fold their constant parts into instruction offsets instead of being
 // precomputed and held in registers.
@@ -352,6 +363,8 @@ __global__ __launch_bounds__(256) void delta_kernel(const __bf16* __restrict__ o
 //   3. after the dK/dV contraction of s+1 -- once the wave has waited for all
 //      of its outstanding vector memory operations, so the writes are
 //      complete at device scope -- one lane stores sem = ordinal + 1.
+// When s+1 begins a new key/value chain, steps 2 and 3 happen at its start,
+// around the loads of the new K/V tile, instead.
 // Deferring the writes and the release overlaps their latency with compute;
 // the release never waits on another workgroup, so no cycle can form.
 // ---------------------------------------------------------------------------
@@ -517,7 +530,9 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
   // dQ read-modify-write pipelined by one sub-step (deterministic schedules):
   // the block computed in sub-step s is read (after the wait) at the end of
   // s, added and written after the S/dP phase of s+1, and its semaphore is
-  // released at the end of s+1, once the writes are complete.
+  // released after the dK/dV contraction of s+1, once the writes are
+  // complete.  When s+1 starts a new chain, the block is finished and
+  // released before that chain's K/V loads instead (see the chain start).
   f32x16 pdq[TPW], pprev[TPW];
   // The vector-memory sequence of a sub-step is the same on every path (a
   // missing prefetch re-reads the current block, a missing write goes to the
@@ -531,6 +546,25 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
   int r_val = 0;
   constexpr bool EVEN = (NQT % NW) == 0;  // every wave holds NQT / NW dQ tiles
   const bool has_tiles = EVEN || w < NQT;
+  // Pending block's partial plus its predecessor's sum, to its workspace tiles
+  // (tiles of other waves' indices past the last go to the dummy tiles).
+  auto finish_pending = [&]() {
+#pragma unroll
+    for (int ti = 0; ti < TPW; ++ti) {
+      const int t_idx = w + NW * ti;
+      const __amdgpu_buffer_rsrc_t rs = ws_rsrc(uniform_ptr((EVEN || t_idx < NQT) ? p_ws : a.dummy) + t_idx * 1024);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        f32x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * q4 + e;
+          v4[e] = p_add ? pdq[ti][r] + pprev[ti][r] : pdq[ti][r];
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(v4, rs, (q4 * 64 + lane) * 16, 0, kDeviceScope);
+      }
+    }
+  };
   if (beg < end) {
     const int4 r0 = step_at(beg);
     load_block(r0.x, r0.y * T);
@@ -551,6 +585,19 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
       // New chain: its V rows to registers and its K tile to LDS.  The previous
       // chain's dK/dV are written only after that, so that waiting for these
       // loads never waits for those writes to drain.
+      //
+      // The previous chain's last block is finished first and released as soon
+      // as these loads have arrived, rather than a sub-step into the new chain:
+      // where members change chains at different rounds (the causal symmetric
+      // shift), the block's successor is mid-chain and would otherwise wait for
+      // this chain start, and every later block of that successor with it.
+      bool release_now = false;
+      if constexpr (!ATOMIC) {
+        if (__builtin_amdgcn_readfirstlane((int)(p_sem != nullptr))) {
+          release_now = true;
+          finish_pending();
+        }
+      }
 #pragma unroll
       for (int c = 0; c < DC; ++c) vb[c] = *(const bf16x8*)(vh + (size_t)min(kv_local, kv_valid - 1) * D + 16 * c + 8 * h2);
       bf16x8 kt[KCH];
@@ -558,6 +605,16 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
       for (int u = 0; u < KCH; ++u) {
         const int ch = threadIdx.x + u * NT, row = min(ch / (D / 8), kv_valid - 1), col = (ch % (D / 8)) * 8;
         kt[u] = *(const bf16x8*)(kh + (size_t)row * D + col);
+      }
+      if constexpr (!ATOMIC) {
+        if (release_now) {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          if (lane == 0) __hip_atomic_store(p_sem, p_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          // Nothing is pending any more: the finish below writes to the dummy tiles.
+          p_ws = a.dummy;
+          p_sem = nullptr;
+          p_add = false;
+        }
       }
       __syncthreads();  // previous chain's dQ contraction is done with sK
 #pragma unroll
@@ -654,23 +711,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
         // sum is formed on every path so that no path leaves the reads pending.
         // (A select, not a multiply by zero: a value read without a predecessor
         // is arbitrary bits, possibly NaN.)
-        if (has_tiles) {  // compile-time true when the tiles divide evenly over the waves
-#pragma unroll
-          for (int ti = 0; ti < TPW; ++ti) {
-            const int t_idx = w + NW * ti;
-            const __amdgpu_buffer_rsrc_t rs = ws_rsrc(((EVEN || t_idx < NQT) ? p_ws : a.dummy) + t_idx * 1024);
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-              f32x4 v4;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int r = 4 * q4 + e;
-                v4[e] = p_add ? pdq[ti][r] + pprev[ti][r] : pdq[ti][r];
-              }
-              __builtin_amdgcn_raw_buffer_store_b128(v4, rs, (q4 * 64 + lane) * 16, 0, kDeviceScope);
-            }
-          }
-        }
+        if (has_tiles) finish_pending();  // compile-time true when the tiles divide evenly over the waves
         r_sem = p_sem;
         r_val = p_val;
       }
