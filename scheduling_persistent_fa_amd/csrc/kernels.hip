@@ -356,8 +356,8 @@ __global__ __launch_bounds__(256) void delta_kernel(const __bf16* __restrict__ o
 // the device; no cache write-back or invalidate is issued.  Each wave that
 // holds dQ tiles, for the block computed in sub-step s:
 //   1. at the end of s, spins until sem == ordinal (usually already seen by
-//      an early read), then issues the loads of its tiles of the block
-//      (ordinal > 0);
+//      an early read), then issues the loads of its tiles of the block (for
+//      ordinal 0 through an empty buffer range, so that they return zeros);
 //   2. after the S/dP phase of s+1, adds its partial and writes the tiles
 //      back;
 //   3. after the dK/dV contraction of s+1 -- once the wave has waited for all
@@ -541,7 +541,6 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
   float* p_ws = a.dummy;  // block whose partial is pending (the dummy tiles if none)
   int* p_sem = nullptr;   // its semaphore, if it is a real block
   int p_val = 0;
-  bool p_add = false;
   int* r_sem = nullptr;  // semaphore to release once this wave's writes are complete
   int r_val = 0;
   constexpr bool EVEN = (NQT % NW) == 0;  // every wave holds NQT / NW dQ tiles
@@ -557,10 +556,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
       for (int q4 = 0; q4 < 4; ++q4) {
         f32x4 v4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * q4 + e;
-          v4[e] = p_add ? pdq[ti][r] + pprev[ti][r] : pdq[ti][r];
-        }
+        for (int e = 0; e < 4; ++e) v4[e] = pdq[ti][4 * q4 + e] + pprev[ti][4 * q4 + e];
         __builtin_amdgcn_raw_buffer_store_b128(v4, rs, (q4 * 64 + lane) * 16, 0, kDeviceScope);
       }
     }
@@ -613,7 +609,6 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
           // Nothing is pending any more: the finish below writes to the dummy tiles.
           p_ws = a.dummy;
           p_sem = nullptr;
-          p_add = false;
         }
       }
       __syncthreads();  // previous chain's dQ contraction is done with sK
@@ -671,6 +666,10 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
           bk[sl] = lds_row8(base + OFF_K + o_rowk + 32 * c);
         };
         fetch(0, 0);
+        // Each of the three contractions runs at raised wave priority, so that
+        // while one wave of a SIMD issues matrix-core instructions the other
+        // wave's vector and LDS work fills the gaps (about 1% at B1 H16 S16384).
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int c = 0; c < DC; ++c) {
           if (c + 1 < DC) fetch(c + 1, (c + 1) & 1);
@@ -679,6 +678,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
           dp = mfma32(ado[c & 1], vb[c], dp);
           __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_s_setprio(0);
         // P = exp2(S*scale*log2e - LSE*log2e); dS = P * (dP - Delta); both to LDS transposed.
         // Element (8j + e) of this lane has key - diagonal key = rel - (8j + e); under
         // mask_on P is zero where that exceeds wr (hi > 8j + e) or falls below -wl
@@ -707,10 +707,9 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
         }
       }
       if constexpr (!ATOMIC) {
-        // Finish the pending block: its predecessor's partial has arrived.  The
-        // sum is formed on every path so that no path leaves the reads pending.
-        // (A select, not a multiply by zero: a value read without a predecessor
-        // is arbitrary bits, possibly NaN.)
+        // Finish the pending block: its predecessor's partial has arrived (zeros
+        // for a first contribution).  The sum is formed on every path so that no
+        // path leaves the reads pending.
         if (has_tiles) finish_pending();  // compile-time true when the tiles divide evenly over the waves
         r_sem = p_sem;
         r_val = p_val;
@@ -734,6 +733,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
         bf16x8 ap[2], ads[2];
         ap[0] = lds_row8(base + OFF_PT + o_rowt);
         ads[0] = lds_row8(base + OFF_DS + o_rowt);
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int c = 0; c < QC; ++c) {
           const int sl = c & 1;
@@ -756,6 +756,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
             __builtin_amdgcn_sched_barrier(0);
           }
         }
+        __builtin_amdgcn_s_setprio(0);
       }
       if constexpr (!ATOMIC) {
         // Release the block finished after the S/dP phase as soon as its writes
@@ -784,6 +785,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
             // the dS^T operand of chunk c+1 is read while chunk c's MFMA runs
             bf16x8 ads2[2];
             ads2[0] = lds_tr8_at(pds, PS);
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int c = 0; c < KC; ++c) {
               if (c + 1 < KC) ads2[(c + 1) & 1] = lds_tr8_at(pds + 16 * (c + 1) * PS, PS);
@@ -791,6 +793,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
               acc = mfma32(ads2[c & 1], bk[c], acc);
               __builtin_amdgcn_sched_barrier(0);
             }
+            __builtin_amdgcn_s_setprio(0);
             dq[ti] = acc;
           }
         }
@@ -843,7 +846,11 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
           for (int ti = 0; ti < TPW; ++ti) {
             const int t_idx = w + NW * ti;
             asm volatile("" ::: "memory");  // the reads stay after the wait above
-            const __amdgpu_buffer_rsrc_t rs = ws_rsrc(wsb + (t_idx < NQT ? t_idx : t_idx % NQT) * 1024);
+            // A first contribution (ordinal 0) has no predecessor: an empty
+            // buffer range makes these loads return zeros without reading
+            // memory, so the sum below needs no select.
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                wsb + (t_idx < NQT ? t_idx : t_idx % NQT) * 1024, (short)0, ord > 0 ? 4096 : 0, 0x00020000);
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
               const f32x4 v4 = __builtin_amdgcn_raw_buffer_load_b128(rs, (q4 * 64 + lane) * 16, 0, kDeviceScope);
@@ -858,7 +865,6 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
         p_ws = real ? wsb : a.dummy;
         p_sem = real ? semp : nullptr;
         p_val = ord + 1;
-        p_add = ord > 0;
         if (give_up && lane == 0) *s_flag = 1;  // everybody leaves after the next first barrier
       }
     }
@@ -879,7 +885,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
       for (int ti = 0; ti < TPW; ++ti) {
         const int t_idx = w + NW * ti;
         if (EVEN || t_idx < NQT) {
-          if (p_add) pdq[ti] += pprev[ti];
+          pdq[ti] += pprev[ti];
           const __amdgpu_buffer_rsrc_t rs = ws_rsrc(p_ws + t_idx * 1024);
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
