@@ -61,7 +61,10 @@ class Schedule:
     def __del__(self):
         h = getattr(self, "_h", None)
         if h is not None and h.value:
-            _lib.lib().dash_schedule_free(h)
+            try:
+                _lib.lib().dash_schedule_free(h)
+            except (TypeError, AttributeError):
+                pass  # interpreter shutdown: module globals are already gone, and the process frees the memory
             self._h = None
 
     def validate(self) -> None:
