@@ -308,11 +308,14 @@ __global__ __launch_bounds__(256) void delta_kernel(const __bf16* __restrict__ o
 
 // ---------------------------------------------------------------------------
 // LDS row pitches.  gfx950's LDS has 64 four-byte banks.  A 16-byte row read
-// (16 lanes per cycle, 16 consecutive rows) is conflict-free when the pitch in
-// words is 4 x odd modulo 64; a transposing read (16 lanes per cycle: 4 rows x
-// 32 bytes) needs the four rows' 8-bank windows disjoint.  Pitches of 2D + 48
-// bytes (304 for D = 128, 176 for D = 64) satisfy both, as does 144 bytes for
-// the 64-column P^T / dS^T rows (also conflict-free for their 8-byte writes).
+// serves 16 lanes (16 consecutive rows) per cycle and is conflict-free when
+// the pitch in words is 4 x odd modulo 64, as for 2D + 48 bytes (304 for
+// D = 128, 176 for D = 64) and 144 bytes (the 64-column P^T / dS^T rows).  A
+// transposing read serves 32 lanes (4 rows x 64 bytes) per cycle; at these
+// pitches two of the four rows share banks, so it takes 4 cycles instead of 2
+// (only pitches of 64 bytes modulo 256 avoid that, and those make the row
+// reads conflict), and the 8-byte P^T / dS^T stores take 16 cycles instead
+// of 8.  Measured, neither is what bounds the kernel.
 // ---------------------------------------------------------------------------
 // Persistent backward.  One workgroup per compute unit walks its step list
 // (built on the host); each chain (key/value tile x its query heads) runs
