@@ -101,8 +101,8 @@ def main():
         print(json.dumps({"copy_probe_bytes": args.copy_probe << 20, "launches": 3}))
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                                   "(the path shards by (batch, kv head) with no exchange; see DESIGN.md)"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU; --gpus must be 1 (the work would "
+                                   "shard by (batch, kv head), with no exchange between GPUs)"}))
         sys.exit(2)
     if args.block:
         block_bench(args)
