@@ -81,7 +81,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c4_full_s16384_d128")
+    ap.add_argument("--workload", default="full_b1_h16_s16384_d128")
     ap.add_argument("--schedules", default="", help="comma list (serial,desc_q,shift,sym_shift); default: all for the mask")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-atomic", action="store_true")

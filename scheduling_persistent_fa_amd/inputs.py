@@ -60,21 +60,21 @@ def make_inputs(B: int, Hq: int, Hkv: int, S: int, D: int, seed: int = 0, std: f
     return AttnInputs(B=B, Hq=Hq, Hkv=Hkv, S=S, D=D, Sk=Sk, **out)
 
 
-# The five workloads: (name, B, Hq, Hkv, S, D, causal, tile, std).
+# Benchmark workloads, named by mask and sizes: (B, Hq, Hkv, S, D, causal, tile, std).
 WORKLOADS = {
-    "c1_full_s256_d64": dict(B=1, Hq=1, Hkv=1, S=256, D=64, causal=False, tile=64, std=1.0),
-    "c2_causal_s2048_d128": dict(B=4, Hq=16, Hkv=16, S=2048, D=128, causal=True, tile=128, std=1.0),
-    "c3_full_s4096_d64": dict(B=2, Hq=24, Hkv=24, S=4096, D=64, causal=False, tile=128, std=1.0),
-    "c4_full_s16384_d128": dict(B=1, Hq=16, Hkv=16, S=16384, D=128, causal=False, tile=128, std=1.0),
-    "c4_causal_s16384_d128": dict(B=1, Hq=16, Hkv=16, S=16384, D=128, causal=True, tile=128, std=1.0),
-    "c5_gqa_causal_s8192_d128": dict(B=1, Hq=32, Hkv=8, S=8192, D=128, causal=True, tile=128, std=0.5),
+    "full_b1_h1_s256_d64": dict(B=1, Hq=1, Hkv=1, S=256, D=64, causal=False, tile=64, std=1.0),
+    "causal_b4_h16_s2048_d128": dict(B=4, Hq=16, Hkv=16, S=2048, D=128, causal=True, tile=128, std=1.0),
+    "full_b2_h24_s4096_d64": dict(B=2, Hq=24, Hkv=24, S=4096, D=64, causal=False, tile=128, std=1.0),
+    "full_b1_h16_s16384_d128": dict(B=1, Hq=16, Hkv=16, S=16384, D=128, causal=False, tile=128, std=1.0),
+    "causal_b1_h16_s16384_d128": dict(B=1, Hq=16, Hkv=16, S=16384, D=128, causal=True, tile=128, std=1.0),
+    "gqa_causal_b1_hq32_hkv8_s8192_d128": dict(B=1, Hq=32, Hkv=8, S=8192, D=128, causal=True, tile=128, std=0.5),
     # queries and keys of different lengths (S query rows, Sk key rows): cross
     # attention, and a causal continuation aligned at the bottom right
-    "x1_cross_q4096_k16384_d128": dict(B=1, Hq=16, Hkv=16, S=4096, Sk=16384, D=128, causal=False, tile=128, std=1.0),
-    "x2_causal_q4096_k16384_d128": dict(B=1, Hq=16, Hkv=16, S=4096, Sk=16384, D=128, causal=True, tile=128,
-                                        std=1.0),
+    "cross_b1_h16_q4096_k16384_d128": dict(B=1, Hq=16, Hkv=16, S=4096, Sk=16384, D=128, causal=False, tile=128, std=1.0),
+    "causal_b1_h16_q4096_k16384_d128": dict(B=1, Hq=16, Hkv=16, S=4096, Sk=16384, D=128, causal=True, tile=128,
+                                            std=1.0),
     # sliding-window causal attention: each query sees its own key and the
     # 4095 before it (a 4096-key window)
-    "w1_sliding_s16384_w4096_d128": dict(B=1, Hq=16, Hkv=16, S=16384, D=128, causal=True, window=(4095, 0),
-                                         tile=128, std=1.0),
+    "sliding_b1_h16_s16384_w4096_d128": dict(B=1, Hq=16, Hkv=16, S=16384, D=128, causal=True, window=(4095, 0),
+                                             tile=128, std=1.0),
 }

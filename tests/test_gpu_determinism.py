@@ -27,9 +27,9 @@ def _digest(*ts):
 
 
 CASES = [
-    ("c2_causal_s2048_d128", 4, 16, 16, 2048, 128, True, 1.0, [SERIAL, DESC_Q, SYM_SHIFT]),
-    ("c3_full_s4096_d64", 2, 24, 24, 4096, 64, False, 1.0, [SERIAL, DESC_Q, SHIFT]),
-    ("c5_gqa_causal_s8192_d128", 1, 32, 8, 8192, 128, True, 0.5, [DESC_Q, SYM_SHIFT]),
+    ("causal_b4_h16_s2048_d128", 4, 16, 16, 2048, 128, True, 1.0, [SERIAL, DESC_Q, SYM_SHIFT]),
+    ("full_b2_h24_s4096_d64", 2, 24, 24, 4096, 64, False, 1.0, [SERIAL, DESC_Q, SHIFT]),
+    ("gqa_causal_b1_hq32_hkv8_s8192_d128", 1, 32, 8, 8192, 128, True, 0.5, [DESC_Q, SYM_SHIFT]),
 ]
 
 

@@ -27,7 +27,7 @@ def _schedules(causal, N):
 
 SMALL = [
     # (name, B, Hq, Hkv, S, D, causal, tile, std, workgroups)
-    ("c1_full_s256_d64_shift_4wg", 1, 1, 1, 256, 64, False, 64, 1.0, 4),
+    ("full_b1_h1_s256_d64_shift_4wg", 1, 1, 1, 256, 64, False, 64, 1.0, 4),
     ("full_d128_n4", 1, 2, 2, 512, 128, False, 128, 1.0, 0),
     ("causal_d128_n4", 1, 2, 2, 512, 128, True, 128, 1.0, 0),
     ("gqa4_causal_d128_n4", 2, 8, 2, 512, 128, True, 128, 0.5, 0),
@@ -65,11 +65,11 @@ def test_small_shapes_match_oracle(case):
 
 
 FULL_SIZE = [
-    ("c2_causal_s2048_d128", 4, 16, 16, 2048, 128, True, 1.0, [SERIAL, DESC_Q, SYM_SHIFT, ATOMIC]),
-    ("c3_full_s4096_d64", 2, 24, 24, 4096, 64, False, 1.0, [SERIAL, DESC_Q, SHIFT, ATOMIC]),
-    ("c4_full_s16384_d128", 1, 16, 16, 16384, 128, False, 1.0, [SERIAL, DESC_Q, SHIFT, ATOMIC]),
-    ("c4_causal_s16384_d128", 1, 16, 16, 16384, 128, True, 1.0, [SERIAL, DESC_Q, SYM_SHIFT, ATOMIC]),
-    ("c5_gqa_causal_s8192_d128", 1, 32, 8, 8192, 128, True, 0.5, [SERIAL, DESC_Q, SYM_SHIFT, ATOMIC]),
+    ("causal_b4_h16_s2048_d128", 4, 16, 16, 2048, 128, True, 1.0, [SERIAL, DESC_Q, SYM_SHIFT, ATOMIC]),
+    ("full_b2_h24_s4096_d64", 2, 24, 24, 4096, 64, False, 1.0, [SERIAL, DESC_Q, SHIFT, ATOMIC]),
+    ("full_b1_h16_s16384_d128", 1, 16, 16, 16384, 128, False, 1.0, [SERIAL, DESC_Q, SHIFT, ATOMIC]),
+    ("causal_b1_h16_s16384_d128", 1, 16, 16, 16384, 128, True, 1.0, [SERIAL, DESC_Q, SYM_SHIFT, ATOMIC]),
+    ("gqa_causal_b1_hq32_hkv8_s8192_d128", 1, 32, 8, 8192, 128, True, 0.5, [SERIAL, DESC_Q, SYM_SHIFT, ATOMIC]),
 ]
 
 
@@ -109,9 +109,9 @@ def test_workload_shapes_on_sampled_rows(case):
 # The rectangular and windowed benchmark workloads at full size (bench.py's
 # launch configuration), on sampled query rows and key rows.
 FULL_SIZE_EXT = [  # name, B, Hq, Hkv, Sq, Sk, D, causal, window, schedules
-    ("x1_cross_q4096_k16384_d128", 1, 16, 16, 4096, 16384, 128, False, None, [DESC_Q, SHIFT, ATOMIC]),
-    ("x2_causal_q4096_k16384_d128", 1, 16, 16, 4096, 16384, 128, True, None, [DESC_Q, SYM_SHIFT, ATOMIC]),
-    ("w1_sliding_s16384_w4096_d128", 1, 16, 16, 16384, 16384, 128, True, (4095, 0), [SERIAL, DESC_Q, SHIFT, ATOMIC]),
+    ("cross_b1_h16_q4096_k16384_d128", 1, 16, 16, 4096, 16384, 128, False, None, [DESC_Q, SHIFT, ATOMIC]),
+    ("causal_b1_h16_q4096_k16384_d128", 1, 16, 16, 4096, 16384, 128, True, None, [DESC_Q, SYM_SHIFT, ATOMIC]),
+    ("sliding_b1_h16_s16384_w4096_d128", 1, 16, 16, 16384, 16384, 128, True, (4095, 0), [SERIAL, DESC_Q, SHIFT, ATOMIC]),
 ]
 
 
