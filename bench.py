@@ -55,9 +55,11 @@ def cpu_baseline(wl, min_seconds=10.0, max_heads=8):
     from scheduling_persistent_fa_amd.inputs import bf16_bits_to_f32, make_inputs
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+        blas_pools = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        cores = max([p.get("num_threads", 1) for p in blas_pools] or [1])
+        blas = ",".join(sorted({p.get("internal_api", "?") for p in blas_pools})) or "none"
     except Exception:  # pragma: no cover - threadpoolctl missing
-        cores = int(os.environ.get("OMP_NUM_THREADS", "1"))
+        cores, blas = int(os.environ.get("OMP_NUM_THREADS", "1")), "unknown"
     S, D, causal = wl["S"], wl["D"], wl["causal"]
     Sk, window = wl.get("Sk", S), wl.get("window")
     f64 = lambda x: bf16_bits_to_f32(x).astype(np.float64)
@@ -73,7 +75,7 @@ def cpu_baseline(wl, min_seconds=10.0, max_heads=8):
     return {"value": heads * flops(1, 1, S, D, causal, Sk, window) / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle",
             "sample": f"{heads} (batch, head) slices of the workload (S={S} Sk={Sk} D={D} "
-                      f"{mask}), float64 forward+backward, {dt:.1f} s"}
+                      f"{mask}), float64 forward+backward, {blas} BLAS, {dt:.1f} s"}
 
 
 def main():
