@@ -306,16 +306,26 @@ __global__ __launch_bounds__(256) void delta_kernel(const __bf16* __restrict__ o
   for (long long i = gid * 4; i < n_zero_f32; i += stride * 4) *(f32x4*)(zero_f32 + i) = f32x4{};
 }
 
+// Q / dO / K rows of 256 bytes (D = 128) are stored in LDS without padding, with
+// 16-byte chunk c of row r at chunk c ^ lds_swizzle(r).  Sixteen consecutive
+// rows then put one logical chunk into sixteen distinct chunks (the 16-byte
+// row reads are conflict-free), and four consecutive rows from a multiple of
+// four put one 64-byte block into four distinct blocks (the transposing reads
+// take 2 cycles instead of 4).
+__device__ __forceinline__ int lds_swizzle(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
+
 // ---------------------------------------------------------------------------
 // LDS row pitches.  gfx950's LDS has 64 four-byte banks.  A 16-byte row read
 // serves 16 lanes (16 consecutive rows) per cycle and is conflict-free when
-// the pitch in words is 4 x odd modulo 64, as for 2D + 48 bytes (304 for
-// D = 128, 176 for D = 64) and 144 bytes (the 64-column P^T / dS^T rows).  A
-// transposing read serves 32 lanes (4 rows x 64 bytes) per cycle; at these
-// pitches two of the four rows share banks, so it takes 4 cycles instead of 2
-// (only pitches of 64 bytes modulo 256 avoid that, and those make the row
-// reads conflict), and the 8-byte P^T / dS^T stores take 16 cycles instead
-// of 8.  Measured, neither is what bounds the kernel.
+// the pitch in words is 4 x odd modulo 64, as for 2D + 48 bytes (176 for
+// D = 64) and 144 bytes (the 64-column P^T / dS^T rows).  A transposing read
+// serves 32 lanes (4 rows x 64 bytes) per cycle; at these pitches two of the
+// four rows share banks, so it takes 4 cycles instead of 2 (only pitches of 64
+// bytes modulo 256 avoid that, and those make the row reads conflict), and the
+// 8-byte P^T / dS^T stores take 16 cycles instead of 8.  For D = 128 the
+// Q / dO / K rows use the swizzle above instead of padding, which makes both
+// kinds of read conflict-free; measured, that gains about 1%, so the conflicts
+// are not what bounds the kernel.
 // ---------------------------------------------------------------------------
 // Persistent backward.  One workgroup per compute unit walks its step list
 // (built on the host); each chain (key/value tile x its query heads) runs
@@ -422,7 +432,8 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
   constexpr bool SHARE_K = (NW % DB) == 0;  // a wave's dQ tiles share one d block
   constexpr int KC = T / 16;          // 16-row key/value chunks of the dQ contraction
   constexpr int QC = M / 16;          // 16-row query chunks of the dK / dV contraction
-  constexpr int PQ = 2 * D + 48;      // LDS pitch (bytes) of Q / dO / K rows (see the LDS note above)
+  constexpr bool SWZ = D == 128;      // Q / dO / K rows swizzled rather than padded (see lds_swizzle)
+  constexpr int PQ = SWZ ? 2 * D : 2 * D + 48;  // LDS pitch (bytes) of Q / dO / K rows
   constexpr int PS = (M + 8) * 2;     // LDS pitch (bytes) of P^T / dS^T rows
   constexpr int QBUF = M * PQ;
   constexpr int OFF_Q = 0;                       // [2][M][PQ]
@@ -467,6 +478,25 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
   const int o_trq_h = opaque(tr_row * PQ + (tr_col + hf * DH * 32) * 2);  // ... in this wave's d half
   const int o_trs = opaque(tr_row * PS + tr_col * 2);                  // transposing reads, pitch PS
   const int o_rowq = opaque((32 * hf + c32) * PQ + 16 * h2);           // Q / dO rows of this wave's query half
+  // Byte offset of 16-byte chunk `chunk` of Q / dO / K row `row`.
+  auto qk_chunk = [](int row, int chunk) { return row * PQ + 16 * (SWZ ? chunk ^ lds_swizzle(row) : chunk); };
+  // Swizzled layout (D = 128, 256-byte rows), in XOR form: chunk pair c of this
+  // lane's Q / dO (K) row read sits at r_q ^ (c << 5) (r_k ^ ...), and 64-byte
+  // column block blk of the transposing read of rows 8h + 4e + (l%16)/4 at
+  // t_dk[e] ^ ((blk ^ hf*DH) << 6).  Buffer offsets are multiples of 256 bytes,
+  // so they add after the XOR.  The XORs are redone per sub-step, so that no
+  // per-chunk address stays live across the loop.
+  const int swq = lds_swizzle(32 * hf + c32), swk = lds_swizzle(kv0 + c32);
+  const int r_q = opaque((32 * hf + c32) * PQ + 16 * (h2 ^ (swq & 1)) + 32 * (swq >> 1));
+  const int r_k = opaque((kv0 + c32) * PQ + 16 * (h2 ^ (swk & 1)) + 32 * (swk >> 1));
+  int t_dk[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    // row & 3 = tr_a picks the 64-byte block, (row >> 2) & 3 the 16-byte chunk in it
+    const int tr_a = (lane & 15) >> 2, tr_q = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    const int row = 8 * h2 + 4 * e + tr_a;
+    t_dk[e] = opaque((row * PQ + 64 * tr_a + 16 * (tr_q ^ ((2 * h2 + e) & 3)) + 8 * (lane & 1)) ^ ((hf * DH) << 6));
+  }
   const int o_rowt = opaque(kv_local * PS + 16 * h2);                  // P^T / dS^T rows of this lane
   const int o_rowk = opaque(kv_local * PQ + 16 * h2);                  // K rows of this lane
   const int o_stt = opaque(kv_local * PS + (32 * hf + 4 * h2) * 2);    // P^T / dS^T stores
@@ -499,8 +529,8 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < QCH; ++i) {
       const int ch = threadIdx.x + i * NT, row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-      *(LDS bf16x8*)(base + OFF_Q + buf * QBUF + row * PQ + col * 2) = pq[i];
-      *(LDS bf16x8*)(base + OFF_DO + buf * QBUF + row * PQ + col * 2) = pdo[i];
+      *(LDS bf16x8*)(base + OFF_Q + buf * QBUF + qk_chunk(row, col / 8)) = pq[i];
+      *(LDS bf16x8*)(base + OFF_DO + buf * QBUF + qk_chunk(row, col / 8)) = pdo[i];
     }
     if (threadIdx.x < 2 * M) *(LDS float*)(base + OFF_STAT + (buf * 2 * M + threadIdx.x) * 4) = pstat * st_mul;
   };
@@ -618,7 +648,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
 #pragma unroll
       for (int u = 0; u < KCH; ++u) {
         const int ch = threadIdx.x + u * NT, row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-        *(LDS bf16x8*)(base + OFF_K + row * PQ + col * 2) = kt[u];
+        *(LDS bf16x8*)(base + OFF_K + qk_chunk(row, col / 8)) = kt[u];
       }
       if (epi_pending) write_dkdv(epi_kvh, epi_kj);
       epi_pending = false;
@@ -663,10 +693,17 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
         // One 16-wide d chunk at a time, double-buffered: chunk c+1's Q, dO and
         // K operands are read while chunk c's two MFMAs run.
         bf16x8 aq[2], ado[2], bk[2];
+        [[maybe_unused]] const int rq = opaque(buf * QBUF + r_q), rk = opaque(r_k);
         auto fetch = [&](int c, int sl) {
-          aq[sl] = lds_row8(sq + o_rowq + 32 * c);
-          ado[sl] = lds_row8(sdo + o_rowq + 32 * c);
-          bk[sl] = lds_row8(base + OFF_K + o_rowk + 32 * c);
+          if constexpr (SWZ) {
+            aq[sl] = lds_row8(base + OFF_Q + (rq ^ (c << 5)));
+            ado[sl] = lds_row8(base + OFF_DO + (rq ^ (c << 5)));
+            bk[sl] = lds_row8(base + OFF_K + (rk ^ (c << 5)));
+          } else {
+            aq[sl] = lds_row8(sq + o_rowq + 32 * c);
+            ado[sl] = lds_row8(sdo + o_rowq + 32 * c);
+            bk[sl] = lds_row8(base + OFF_K + o_rowk + 32 * c);
+          }
         };
         fetch(0, 0);
         // Each of the three contractions runs at raised wave priority, so that
@@ -734,6 +771,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
       // keep that order), which hides part of the LDS latency.
       {
         bf16x8 ap[2], ads[2];
+        [[maybe_unused]] const int td[2] = {opaque(buf * QBUF + t_dk[0]), opaque(buf * QBUF + t_dk[1])};
         ap[0] = lds_row8(base + OFF_PT + o_rowt);
         ads[0] = lds_row8(base + OFF_DS + o_rowt);
         __builtin_amdgcn_s_setprio(1);
@@ -741,8 +779,17 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
         for (int c = 0; c < QC; ++c) {
           const int sl = c & 1;
           bf16x8 bdo[DH], bq[DH];
-          bdo[0] = lds_tr8_at(sdo + o_trq_h + 16 * c * PQ, PQ);
-          bq[0] = lds_tr8_at(sq + o_trq_h + 16 * c * PQ, PQ);
+          // d block j of this wave's half of dO (is_do) or Q, query chunk c
+          auto tr_dkdv = [&](bool is_do, int j) {
+            if constexpr (SWZ) {
+              const LDS char* b_ = base + (is_do ? OFF_DO : OFF_Q) + 16 * c * PQ;
+              return cat8(lds_tr4(b_ + (td[0] ^ (j << 6))), lds_tr4(b_ + (td[1] ^ (j << 6))));
+            } else {
+              return lds_tr8_at((is_do ? sdo : sq) + o_trq_h + 16 * c * PQ + 64 * j, PQ);
+            }
+          };
+          bdo[0] = tr_dkdv(true, 0);
+          bq[0] = tr_dkdv(false, 0);
           if (c + 1 < QC) {
             ap[sl ^ 1] = lds_row8(base + OFF_PT + o_rowt + 32 * (c + 1));
             ads[sl ^ 1] = lds_row8(base + OFF_DS + o_rowt + 32 * (c + 1));
@@ -750,8 +797,8 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
 #pragma unroll
           for (int j = 0; j < DH; ++j) {
             if (j + 1 < DH) {
-              bdo[j + 1] = lds_tr8_at(sdo + o_trq_h + 16 * c * PQ + 64 * (j + 1), PQ);
-              bq[j + 1] = lds_tr8_at(sq + o_trq_h + 16 * c * PQ + 64 * (j + 1), PQ);
+              bdo[j + 1] = tr_dkdv(true, j + 1);
+              bq[j + 1] = tr_dkdv(false, j + 1);
             }
             __builtin_amdgcn_sched_barrier(0);
             dv_acc[j] = mfma32(ap[sl], bdo[j], dv_acc[j]);
@@ -779,9 +826,16 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
           if (EVEN || t_idx < NQT) {
             const int qb = t_idx / DB, db = t_idx % DB;
             if (ti == 0 || !SHARE_K) {
-              const LDS char* pk = base + OFF_K + o_trq + db * 64;
+              if constexpr (SWZ) {
+                const int o0 = opaque(t_dk[0] ^ ((hf * DH ^ db) << 6)), o1 = opaque(t_dk[1] ^ ((hf * DH ^ db) << 6));
 #pragma unroll
-              for (int c = 0; c < KC; ++c) bk[c] = lds_tr8_at(pk + 16 * c * PQ, PQ);
+                for (int c = 0; c < KC; ++c)
+                  bk[c] = cat8(lds_tr4(base + OFF_K + o0 + 16 * c * PQ), lds_tr4(base + OFF_K + o1 + 16 * c * PQ));
+              } else {
+                const LDS char* pk = base + OFF_K + o_trq + db * 64;
+#pragma unroll
+                for (int c = 0; c < KC; ++c) bk[c] = lds_tr8_at(pk + 16 * c * PQ, PQ);
+              }
             }
             const LDS char* pds = base + OFF_DS + o_trs + qb * 64;
             f32x16 acc = f32x16{};
