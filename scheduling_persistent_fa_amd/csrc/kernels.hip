@@ -53,19 +53,10 @@ __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
 
 __device__ __forceinline__ bf16x8 lds_row8(const LDS char* p) { return *(const LDS bf16x8*)p; }
 
-// Operand from two transposing reads: rows row0 + (l%16)/4 and row0 + 4 + (l%16)/4
-// (pitch in bytes), columns col0 + 16*((l/16)%2) + 4*(l%4) (bf16 elements).
-// Lane l receives rows row0..row0+3 then row0+4..row0+7 of column col0 + l%32.
-__device__ __forceinline__ bf16x8 lds_tr8_consecutive(const LDS char* base, int pitch_bytes, int row0, int col0,
-                                                      int lane) {
-  const int r = row0 + ((lane & 15) >> 2);
-  const int c = col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const LDS char* p = base + r * pitch_bytes + c * 2;
-  return cat8(lds_tr4(p), lds_tr4(p + 4 * pitch_bytes));
-}
-
-// Same, but the second group of four rows starts 8 rows after the first:
-// the k-permutation of a C tile reused as an operand.
+// Operand from two transposing reads: rows row0 + (l%16)/4 and row0 + 8 + (l%16)/4
+// (pitch in bytes), columns col0 + 16*((l/16)%2) + 4*(l%4) (bf16 elements).  Lane
+// l receives rows row0..row0+3 then row0+8..row0+11 of column col0 + l%32: the
+// k-permutation of a C tile reused as an operand.
 __device__ __forceinline__ bf16x8 lds_tr8_split(const LDS char* base, int pitch_bytes, int row0, int col0,
                                                 int lane) {
   const int r = row0 + ((lane & 15) >> 2);
@@ -74,8 +65,9 @@ __device__ __forceinline__ bf16x8 lds_tr8_split(const LDS char* base, int pitch_
   return cat8(lds_tr4(p), lds_tr4(p + 8 * pitch_bytes));
 }
 
-// Same as lds_tr8_consecutive with the lane part of the address already
-// applied: p = block + ((l%16)/4) * pitch + (16*((l/16)%2) + 4*(l%4)) * 2.
+// Operand from two transposing reads with the lane part of the address already
+// applied, p = block + ((l%16)/4) * pitch + (16*((l/16)%2) + 4*(l%4)) * 2: lane l
+// receives rows 0..3 then 4..7 of column l%32 of the block.
 __device__ __forceinline__ bf16x8 lds_tr8_at(const LDS char* p, int pitch_bytes) {
   return cat8(lds_tr4(p), lds_tr4(p + 4 * pitch_bytes));
 }
@@ -113,8 +105,6 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& x, int first) {
   for (int e = 0; e < 8; ++e) r[e] = (__bf16)x[first + e];
   return r;
 }
-
-constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
@@ -306,26 +296,33 @@ __global__ __launch_bounds__(256) void delta_kernel(const __bf16* __restrict__ o
   for (long long i = gid * 4; i < n_zero_f32; i += stride * 4) *(f32x4*)(zero_f32 + i) = f32x4{};
 }
 
-// Q / dO / K rows of 256 bytes (D = 128) are stored in LDS without padding, with
-// 16-byte chunk c of row r at chunk c ^ lds_swizzle(r).  Sixteen consecutive
-// rows then put one logical chunk into sixteen distinct chunks (the 16-byte
-// row reads are conflict-free), and four consecutive rows from a multiple of
-// four put one 64-byte block into four distinct blocks (the transposing reads
-// take 2 cycles instead of 4).
-__device__ __forceinline__ int lds_swizzle(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
+// Q / dO / K rows (2D bytes) are stored in LDS without padding, with 16-byte
+// chunk c of row r at chunk c ^ lds_swizzle<D>(r).  Sixteen consecutive rows
+// then put one logical chunk into sixteen distinct 16-byte bank groups (the
+// 16-byte row reads are conflict-free), and four consecutive rows from a
+// multiple of four put one 64-byte block into four distinct bank groups of
+// four (the transposing reads take 2 cycles instead of 4).  For D = 128 the
+// row's low two bits pick the 64-byte block and the next two the chunk in it;
+// for D = 64 (two rows per 256-byte bank line) bit 1 picks the block and bits
+// 2-3 the chunk.
+template <int D>
+__device__ __forceinline__ int lds_swizzle(int r) {
+  if constexpr (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+  else return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
 
 // ---------------------------------------------------------------------------
 // LDS row pitches.  gfx950's LDS has 64 four-byte banks.  A 16-byte row read
 // serves 16 lanes (16 consecutive rows) per cycle and is conflict-free when
-// the pitch in words is 4 x odd modulo 64, as for 2D + 48 bytes (176 for
-// D = 64) and 144 bytes (the 64-column P^T / dS^T rows).  A transposing read
-// serves 32 lanes (4 rows x 64 bytes) per cycle; at these pitches two of the
-// four rows share banks, so it takes 4 cycles instead of 2 (only pitches of 64
-// bytes modulo 256 avoid that, and those make the row reads conflict), and the
-// 8-byte P^T / dS^T stores take 16 cycles instead of 8.  For D = 128 the
-// Q / dO / K rows use the swizzle above instead of padding, which makes both
-// kinds of read conflict-free; measured, that gains about 1%, so the conflicts
-// are not what bounds the kernel.
+// the pitch in words is 4 x odd modulo 64, as for the 144-byte P^T / dS^T rows
+// (64 columns plus padding).  A transposing read serves 32 lanes (4 rows x 64
+// bytes) per cycle; at such a pitch two of the four rows share banks, so it
+// takes 4 cycles instead of 2 (only pitches of 64 bytes modulo 256 avoid that,
+// and those make the row reads conflict), and the 8-byte P^T / dS^T stores
+// take 16 cycles instead of 8.  The Q / dO / K rows use the swizzle above
+// instead of padding, which makes both kinds of read conflict-free; measured
+// against padded rows, that gains about 1%, so the conflicts are not what
+// bounds the kernel.
 // ---------------------------------------------------------------------------
 // Persistent backward.  One workgroup per compute unit walks its step list
 // (built on the host); each chain (key/value tile x its query heads) runs
@@ -432,8 +429,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
   constexpr bool SHARE_K = (NW % DB) == 0;  // a wave's dQ tiles share one d block
   constexpr int KC = T / 16;          // 16-row key/value chunks of the dQ contraction
   constexpr int QC = M / 16;          // 16-row query chunks of the dK / dV contraction
-  constexpr bool SWZ = D == 128;      // Q / dO / K rows swizzled rather than padded (see lds_swizzle)
-  constexpr int PQ = SWZ ? 2 * D : 2 * D + 48;  // LDS pitch (bytes) of Q / dO / K rows
+  constexpr int PQ = 2 * D;           // LDS pitch (bytes) of Q / dO / K rows, unpadded (see lds_swizzle)
   constexpr int PS = (M + 8) * 2;     // LDS pitch (bytes) of P^T / dS^T rows
   constexpr int QBUF = M * PQ;
   constexpr int OFF_Q = 0;                       // [2][M][PQ]
@@ -472,33 +468,30 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
   const unsigned long long t_start = __builtin_amdgcn_s_memtime();
   if (threadIdx.x == 0) *s_flag = 0;
 
-  // Per-lane LDS byte offsets (each access adds only compile-time constants).
+  // Per-lane LDS byte offsets.
   const int tr_row = 8 * h2 + ((lane & 15) >> 2), tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const int o_trq = opaque(tr_row * PQ + tr_col * 2);                  // transposing reads, pitch PQ
-  const int o_trq_h = opaque(tr_row * PQ + (tr_col + hf * DH * 32) * 2);  // ... in this wave's d half
   const int o_trs = opaque(tr_row * PS + tr_col * 2);                  // transposing reads, pitch PS
-  const int o_rowq = opaque((32 * hf + c32) * PQ + 16 * h2);           // Q / dO rows of this wave's query half
   // Byte offset of 16-byte chunk `chunk` of Q / dO / K row `row`.
-  auto qk_chunk = [](int row, int chunk) { return row * PQ + 16 * (SWZ ? chunk ^ lds_swizzle(row) : chunk); };
-  // Swizzled layout (D = 128, 256-byte rows), in XOR form: chunk pair c of this
-  // lane's Q / dO (K) row read sits at r_q ^ (c << 5) (r_k ^ ...), and 64-byte
-  // column block blk of the transposing read of rows 8h + 4e + (l%16)/4 at
-  // t_dk[e] ^ ((blk ^ hf*DH) << 6).  Buffer offsets are multiples of 256 bytes,
-  // so they add after the XOR.  The XORs are redone per sub-step, so that no
-  // per-chunk address stays live across the loop.
-  const int swq = lds_swizzle(32 * hf + c32), swk = lds_swizzle(kv0 + c32);
+  auto qk_chunk = [](int row, int chunk) { return row * PQ + 16 * (chunk ^ lds_swizzle<D>(row)); };
+  // The swizzled Q / dO / K rows in XOR form: chunk pair c of this lane's Q / dO
+  // (K) row read sits at r_q ^ (c << 5) (r_k ^ ...), and 64-byte column block
+  // blk of the transposing read of rows 8h + 4e + (l%16)/4 at
+  // t_dk[e] ^ ((blk ^ hf*DH) << 6).  The XOR touches only bits 5..7 of a
+  // 2D-byte row, and buffer offsets are multiples of 2D bytes, so they add after
+  // it.  The XORs are redone per sub-step, so that no per-chunk address stays
+  // live across the loop.
+  const int swq = lds_swizzle<D>(32 * hf + c32), swk = lds_swizzle<D>(kv0 + c32);
   const int r_q = opaque((32 * hf + c32) * PQ + 16 * (h2 ^ (swq & 1)) + 32 * (swq >> 1));
   const int r_k = opaque((kv0 + c32) * PQ + 16 * (h2 ^ (swk & 1)) + 32 * (swk >> 1));
   int t_dk[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
-    // row & 3 = tr_a picks the 64-byte block, (row >> 2) & 3 the 16-byte chunk in it
+    // the block bits of the swizzle come from tr_a, its chunk bits, (row >> 2) & 3, from h and e
     const int tr_a = (lane & 15) >> 2, tr_q = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-    const int row = 8 * h2 + 4 * e + tr_a;
-    t_dk[e] = opaque((row * PQ + 64 * tr_a + 16 * (tr_q ^ ((2 * h2 + e) & 3)) + 8 * (lane & 1)) ^ ((hf * DH) << 6));
+    const int row = 8 * h2 + 4 * e + tr_a, blk_bits = D == 128 ? tr_a : (tr_a >> 1);
+    t_dk[e] = opaque((row * PQ + 64 * blk_bits + 16 * (tr_q ^ ((2 * h2 + e) & 3)) + 8 * (lane & 1)) ^ ((hf * DH) << 6));
   }
   const int o_rowt = opaque(kv_local * PS + 16 * h2);                  // P^T / dS^T rows of this lane
-  const int o_rowk = opaque(kv_local * PQ + 16 * h2);                  // K rows of this lane
   const int o_stt = opaque(kv_local * PS + (32 * hf + 4 * h2) * 2);    // P^T / dS^T stores
   const int o_stat = opaque((32 * hf + 4 * h2) * 4);                   // LSE / Delta of this lane's rows
 
@@ -682,8 +675,6 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
         nrow = nr.y * T;
       }
       load_block(nhead, nrow);
-      const LDS char* sq = base + OFF_Q + buf * QBUF;
-      const LDS char* sdo = base + OFF_DO + buf * QBUF;
       const LDS float* slse = (const LDS float*)(base + OFF_STAT + buf * 2 * M * 4);
       const LDS float* sdel = slse + M;
 
@@ -693,17 +684,11 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
         // One 16-wide d chunk at a time, double-buffered: chunk c+1's Q, dO and
         // K operands are read while chunk c's two MFMAs run.
         bf16x8 aq[2], ado[2], bk[2];
-        [[maybe_unused]] const int rq = opaque(buf * QBUF + r_q), rk = opaque(r_k);
+        const int rq = opaque(buf * QBUF + r_q), rk = opaque(r_k);
         auto fetch = [&](int c, int sl) {
-          if constexpr (SWZ) {
-            aq[sl] = lds_row8(base + OFF_Q + (rq ^ (c << 5)));
-            ado[sl] = lds_row8(base + OFF_DO + (rq ^ (c << 5)));
-            bk[sl] = lds_row8(base + OFF_K + (rk ^ (c << 5)));
-          } else {
-            aq[sl] = lds_row8(sq + o_rowq + 32 * c);
-            ado[sl] = lds_row8(sdo + o_rowq + 32 * c);
-            bk[sl] = lds_row8(base + OFF_K + o_rowk + 32 * c);
-          }
+          aq[sl] = lds_row8(base + OFF_Q + (rq ^ (c << 5)));
+          ado[sl] = lds_row8(base + OFF_DO + (rq ^ (c << 5)));
+          bk[sl] = lds_row8(base + OFF_K + (rk ^ (c << 5)));
         };
         fetch(0, 0);
         // Each of the three contractions runs at raised wave priority, so that
@@ -771,7 +756,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
       // keep that order), which hides part of the LDS latency.
       {
         bf16x8 ap[2], ads[2];
-        [[maybe_unused]] const int td[2] = {opaque(buf * QBUF + t_dk[0]), opaque(buf * QBUF + t_dk[1])};
+        const int td[2] = {opaque(buf * QBUF + t_dk[0]), opaque(buf * QBUF + t_dk[1])};
         ap[0] = lds_row8(base + OFF_PT + o_rowt);
         ads[0] = lds_row8(base + OFF_DS + o_rowt);
         __builtin_amdgcn_s_setprio(1);
@@ -781,12 +766,8 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
           bf16x8 bdo[DH], bq[DH];
           // d block j of this wave's half of dO (is_do) or Q, query chunk c
           auto tr_dkdv = [&](bool is_do, int j) {
-            if constexpr (SWZ) {
-              const LDS char* b_ = base + (is_do ? OFF_DO : OFF_Q) + 16 * c * PQ;
-              return cat8(lds_tr4(b_ + (td[0] ^ (j << 6))), lds_tr4(b_ + (td[1] ^ (j << 6))));
-            } else {
-              return lds_tr8_at((is_do ? sdo : sq) + o_trq_h + 16 * c * PQ + 64 * j, PQ);
-            }
+            const LDS char* b_ = base + (is_do ? OFF_DO : OFF_Q) + 16 * c * PQ;
+            return cat8(lds_tr4(b_ + (td[0] ^ (j << 6))), lds_tr4(b_ + (td[1] ^ (j << 6))));
           };
           bdo[0] = tr_dkdv(true, 0);
           bq[0] = tr_dkdv(false, 0);
@@ -826,16 +807,10 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
           if (EVEN || t_idx < NQT) {
             const int qb = t_idx / DB, db = t_idx % DB;
             if (ti == 0 || !SHARE_K) {
-              if constexpr (SWZ) {
-                const int o0 = opaque(t_dk[0] ^ ((hf * DH ^ db) << 6)), o1 = opaque(t_dk[1] ^ ((hf * DH ^ db) << 6));
+              const int o0 = opaque(t_dk[0] ^ ((hf * DH ^ db) << 6)), o1 = opaque(t_dk[1] ^ ((hf * DH ^ db) << 6));
 #pragma unroll
-                for (int c = 0; c < KC; ++c)
-                  bk[c] = cat8(lds_tr4(base + OFF_K + o0 + 16 * c * PQ), lds_tr4(base + OFF_K + o1 + 16 * c * PQ));
-              } else {
-                const LDS char* pk = base + OFF_K + o_trq + db * 64;
-#pragma unroll
-                for (int c = 0; c < KC; ++c) bk[c] = lds_tr8_at(pk + 16 * c * PQ, PQ);
-              }
+              for (int c = 0; c < KC; ++c)
+                bk[c] = cat8(lds_tr4(base + OFF_K + o0 + 16 * c * PQ), lds_tr4(base + OFF_K + o1 + 16 * c * PQ));
             }
             const LDS char* pds = base + OFF_DS + o_trs + qb * 64;
             f32x16 acc = f32x16{};
