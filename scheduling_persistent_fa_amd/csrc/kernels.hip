@@ -99,6 +99,16 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
+// Waits until every vector memory access of this wave has completed.  The
+// inline-asm wait orders the surrounding memory accesses (memory clobber); the
+// builtin repeats it for the compiler's own wait-count tracking, which does not
+// read inline asm.  Without it a later use of a load issued before this point
+// gets a wait for everything issued since, including a semaphore store.
+__device__ __forceinline__ void wait_vmem_all() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt left at their maxima
+}
+
 __device__ __forceinline__ bf16x8 pack8(const f32x16& x, int first) {
   bf16x8 r;
 #pragma unroll
@@ -630,7 +640,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
       }
       if constexpr (!ATOMIC) {
         if (release_now) {
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          wait_vmem_all();
           if (lane == 0) __hip_atomic_store(p_sem, p_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           // Nothing is pending any more: the finish below writes to the dummy tiles.
           p_ws = a.dummy;
@@ -792,7 +802,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
       if constexpr (!ATOMIC) {
         // Release the block finished after the S/dP phase as soon as its writes
         // have had the dK/dV contraction to complete (successors wait on it).
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        wait_vmem_all();
         if (r_sem != nullptr && lane == 0) __hip_atomic_store(r_sem, r_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         r_sem = nullptr;
       }
@@ -926,7 +936,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
           }
         }
       }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      wait_vmem_all();
       if (lane == 0) __hip_atomic_store(p_sem, p_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
