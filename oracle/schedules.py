@@ -115,25 +115,7 @@ def _flagged(chain: list[tuple[int, int, int, int]]) -> list[Step]:
     return [Step(h, qi, kj, o, i == 0, i == n - 1) for i, (h, qi, kj, o) in enumerate(chain)]
 
 
-def gang_slot(gang: int, p: int, n_gangs: int, gang_size: int, xcd_local: bool,
-              P: int = 0, shift: bool = False) -> int:
-    """Workgroup index of member p of a gang (a placement choice: it does not
-    change what any workgroup computes, only which compute unit runs it).
-
-    Workgroup w runs on chiplet w % 8.  With ``xcd_local``, shift gangs on a
-    grid that is a multiple of 128 put runs of 16 consecutive members on one
-    chiplet; otherwise members get indices congruent modulo the gang count.
-    Without it each gang takes a contiguous index range.
-    """
-    if not xcd_local:
-        return gang * gang_size + p
-    if shift and P % 128 == 0:
-        m = gang * gang_size + p
-        return (m // 16) % 8 + 8 * ((m // 128) * 16 + m % 16)
-    return p * n_gangs + gang
-
-
-def build(mask: int, sched: int, N: int, g: int, groups: int, P: int, xcd_local: bool = True,
+def build(mask: int, sched: int, N: int, g: int, groups: int, P: int,
           max_gang: int = 0, Nk: int | None = None, band=None) -> list[list[Step]]:
     """Per-workgroup step lists for ``groups`` kv groups of g query heads, N query
     tiles, Nk key/value tiles (default N), P workgroups.
@@ -159,6 +141,11 @@ def build(mask: int, sched: int, N: int, g: int, groups: int, P: int, xcd_local:
     ``max_gang`` > 0 caps a gang schedule's gang below its natural size;
     member p then takes the units (key/value tiles, or tile pairs)
     p, p + gang, p + 2*gang, ... one after another.
+
+    Gang k (k = group mod the number of gangs) puts member p on workgroup
+    k * gang + p.  Which compute unit runs which member list does not change
+    what any list computes or the order of any dQ tile; the tests compare
+    schedules up to that placement.
 
     A band mask (``mask`` = BAND, ``band`` = (dl, dr) in tiles) takes the
     serial and descending walks over the visible tiles only: a key/value
@@ -195,7 +182,7 @@ def build(mask: int, sched: int, N: int, g: int, groups: int, P: int, xcd_local:
                 load[w] += g * len(walk)
         return out
     if sched == SHIFT and mask == BAND:
-        return _band_shift(N, Nk, band, g, groups, P, xcd_local)
+        return _band_shift(N, Nk, band, g, groups, P)
     if sched == SHIFT:
         if mask != FULL:
             raise ScheduleError("shift scheduling needs a full mask")
@@ -246,7 +233,7 @@ def build(mask: int, sched: int, N: int, g: int, groups: int, P: int, xcd_local:
             for o, (_, kj) in enumerate(sorted(lst)):
                 rank[(h, qi, kj)] = o
         for p, chains in enumerate(members):
-            w = gang_slot(gang, p, n_gangs, gang_size, xcd_local, P, sched == SHIFT)
+            w = gang * gang_size + p
             for ch in chains:
                 out[w].extend(_flagged([(h, qi, kj, rank[(h, qi, kj)]) for (h, qi, kj) in ch]))
     return out
@@ -289,7 +276,7 @@ def band_shift_units(N: int, Nk: int, dl: int) -> list[list[tuple[int, list[int]
     return units
 
 
-def _band_shift(N: int, Nk: int, band, g: int, groups: int, P: int, xcd_local: bool) -> list[list[Step]]:
+def _band_shift(N: int, Nk: int, band, g: int, groups: int, P: int) -> list[list[Step]]:
     """Shift schedule on a sliding-window band: the units of every group are
     dealt round-robin over the P workgroups ("pooled rounds"), unit i going
     to workgroup i mod P in round i // P, so that the rounds stay full even
@@ -304,9 +291,7 @@ def _band_shift(N: int, Nk: int, band, g: int, groups: int, P: int, xcd_local: b
     placed = []  # (workgroup, key0, group, unit)
     for i in range(groups * U):
         grp, u = divmod(i, U)
-        m = i % P
-        w = gang_slot(0, m, 1, P, xcd_local, P, True)
-        placed.append((w, (i // P) * L, grp, units[u]))
+        placed.append((i % P, (i // P) * L, grp, units[u]))
     keys: dict[tuple[int, int], list[tuple[int, int]]] = {}
     for w, key0, grp, chains in placed:
         pos = key0

@@ -27,7 +27,7 @@ def _read_shift_example():
 
 
 def test_shift_four_tiles_matches_the_figure():
-    lists = Sch.build(FULL, SHIFT, 4, 1, 1, 4, xcd_local=False)
+    lists = Sch.build(FULL, SHIFT, 4, 1, 1, 4)
     for cu, order in _read_shift_example():
         assert [s.kj for s in lists[cu]] == [cu] * 4
         assert [s.qi for s in lists[cu]] == order
@@ -88,7 +88,7 @@ def test_sym_shift_causal_has_no_waits(n, m):
 
 
 def test_sym_shift_four_tiles_worked_example():
-    lists = Sch.build(CAUSAL, SYM_SHIFT, 4, 1, 1, 2, xcd_local=False)
+    lists = Sch.build(CAUSAL, SYM_SHIFT, 4, 1, 1, 2)
     assert [(s.kj, s.qi) for s in lists[0]] == [(0, 2), (0, 3), (0, 0), (0, 1), (3, 3)]
     assert [(s.kj, s.qi) for s in lists[1]] == [(1, 3), (1, 2), (1, 1), (2, 3), (2, 2)]
     order = {}
@@ -190,20 +190,6 @@ def test_capped_sym_shift_rounds_have_no_waits(N, cap, m):
     lists = Sch.build(CAUSAL, SYM_SHIFT, N, 1, m, cap, max_gang=cap)
     mk, wait = Sch.simulate(lists, 1.0, 1.0)
     assert wait == 0 and abs(mk - m * (N // 2 // cap) * (N + 1) * 2.0) < 1e-9
-
-
-def test_shift_placement_keeps_runs_of_16_members_on_one_chiplet():
-    # Workgroup w runs on chiplet w % 8: the placement must be a bijection and
-    # keep 16 consecutive gang members (which read each query tile on
-    # consecutive steps) on one chiplet.
-    P, gang, n_gangs = 256, 128, 2
-    slots = [Sch.gang_slot(g, p, n_gangs, gang, True, P, True) for g in range(n_gangs) for p in range(gang)]
-    assert sorted(slots) == list(range(P))
-    for m0 in range(0, P, 16):
-        assert len({slots[m] % 8 for m in range(m0, m0 + 16)}) == 1
-    # other walks and grids keep the congruent mapping
-    assert Sch.gang_slot(1, 3, 4, 64, True, 256, False) == 3 * 4 + 1
-    assert Sch.gang_slot(1, 3, 2, 50, True, 100, True) == 3 * 2 + 1
 
 
 @pytest.mark.parametrize("mask,sched", [(FULL, SERIAL), (FULL, DESC_Q), (FULL, SHIFT), (CAUSAL, SERIAL),
