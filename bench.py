@@ -8,7 +8,11 @@ bf16 inputs already resident in device memory.  FLOPs per step are
 10 * B * Hq * S^2 * D, halved for the causal mask.  Every deterministic
 schedule and every atomic walk of the workload is timed; the reported value is
 the best deterministic schedule.  The persistent kernel is also timed on its
-own with HIP events recorded on the launch stream, for the roofline.
+own with HIP events recorded on the launch stream, for the roofline.  By
+default the causal mask at the same sizes is timed in the same run and
+reported under "also", with its own roofline.  Every timed step writes its
+own output buffers, and all of them are compared bit for bit with the
+warm-up result ("repeat_bitwise").
 
 Prints one JSON line.
 """
@@ -84,6 +88,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="full_b1_h16_s16384_d128")
+    ap.add_argument("--also", default="causal_b1_h16_s16384_d128",
+                    help="comma list of further workloads timed in the same run and reported under 'also' "
+                         "(default: the causal mask at the same sizes); empty for none")
     ap.add_argument("--schedules", default="", help="comma list (serial,desc_q,shift,sym_shift); default: all for the mask")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-atomic", action="store_true")
@@ -110,12 +117,44 @@ def main():
         block_bench(args)
         return
 
+    first = bench_workload(args.workload, args)
+    line = {
+        "metric": METRIC,
+        "value": round(first["value"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(first["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+    }
+    line.update({k: v for k, v in first.items() if k not in ("value", "ms_per_step", "wl")})
+    also = [w for w in args.also.split(",") if w and w != args.workload]
+    if also:
+        line["also"] = {}
+        for name in also:
+            r = bench_workload(name, args)
+            line["also"][name] = {"value": round(r["value"], 2), "ms_per_step": round(r["ms_per_step"], 4),
+                                  **{k: v for k, v in r.items() if k not in ("value", "ms_per_step", "wl")}}
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(first["wl"])
+    print(json.dumps(line), flush=True)
+
+
+def bench_workload(workload, args):
+    """Times every deterministic schedule and atomic walk of one workload;
+    returns the fields of its JSON record (value = best deterministic)."""
     import torch
     from scheduling_persistent_fa_amd import _lib
     from scheduling_persistent_fa_amd.attention import attn_bwd, attn_fwd, bf16_from_bits, device_info, make_opts
     from scheduling_persistent_fa_amd.inputs import WORKLOADS, make_inputs
 
-    wl = dict(WORKLOADS[args.workload])
+    wl = dict(WORKLOADS[workload])
     B, Hq, Hkv, S, D, causal, tile = wl["B"], wl["Hq"], wl["Hkv"], wl["S"], wl["D"], wl["causal"], wl["tile"]
     Sk, window = wl.get("Sk", S), wl.get("window")
     torch.cuda.set_device(0)
@@ -123,9 +162,10 @@ def main():
     inp = make_inputs(B, Hq, Hkv, S, D, seed=0, std=wl["std"], Sk=Sk)
     q, k, v, do = (bf16_from_bits(getattr(inp, n)) for n in ("q", "k", "v", "do"))
     o, lse = attn_fwd(q, k, v, causal, window=window)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     torch.cuda.synchronize()
     fl = flops(B, Hq, S, D, causal, Sk, window)
+    # one output set per timed step, so that every timed step's bits are checked
+    outs = [(torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)) for _ in range(args.steps)]
 
     # shift needs a full mask; symmetric shift pairs query tiles p, N-1-p and needs N even
     fast = ["shift"] if not causal else (["sym_shift"] if (S // tile) % 2 == 0 else [])
@@ -144,8 +184,9 @@ def main():
     stream = torch.cuda.current_stream()
     results = {}
     for name, sched, walk in runs:
-        print(f"[bench] {args.workload} {name}", file=sys.stderr, flush=True)
+        print(f"[bench] {workload} {name}", file=sys.stderr, flush=True)
         base_opts = dict(tile=tile, atomic_walk=walk)
+        dq, dk, dv = outs[0]
         for _ in range(args.warmup):
             attn_bwd(q, k, v, o, do, lse, causal, sched, dq=dq, dk=dk, dv=dv, opts=make_opts(**base_opts),
                      window=window)
@@ -160,6 +201,7 @@ def main():
         torch.cuda.synchronize()
         t_beg.record(stream)
         for i in range(args.steps):
+            dq, dk, dv = outs[i]
             calls[i][0].record(stream)
             attn_bwd(q, k, v, o, do, lse, causal, sched, dq=dq, dk=dk, dv=dv, opts=opts[i], window=window)
             calls[i][1].record(stream)
@@ -169,7 +211,8 @@ def main():
         kms_each = [a_.elapsed_time(b_) for a_, b_ in evs]
         step_each = sorted(a_.elapsed_time(b_) for a_, b_ in calls)
         kms = sum(kms_each) / args.steps
-        same = all(torch.equal(x.view(torch.int16), r) for x, r in zip((dq, dk, dv), ref_bits))
+        # every timed step's dQ, dK, dV against the last warm-up run's bits
+        same = all(torch.equal(x.view(torch.int16), r) for out in outs for x, r in zip(out, ref_bits))
         pct = lambda xs, p: xs[min(len(xs) - 1, max(0, int(round(p * (len(xs) - 1)))))]
         rec = {"ms_per_step": ms, "tflops": fl / (ms * 1e-3) / 1e12, "kernel_ms": kms,
                "kernel_tflops": fl / (kms * 1e-3) / 1e12, "repeat_bitwise": bool(same),
@@ -178,6 +221,7 @@ def main():
                "tflops_p10": fl / (pct(step_each, 0.9) * 1e-3) / 1e12,
                "tflops_p90": fl / (pct(step_each, 0.1) * 1e-3) / 1e12}
         if sched != _lib.ATOMIC:
+            dq, dk, dv = outs[0]
             stall = torch.zeros(2 * info["num_cu"], dtype=torch.int64, device="cuda")
             ke = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             ke[0].record(stream)  # materialise the underlying HIP events
@@ -191,6 +235,8 @@ def main():
             rec["sclk_ghz_est"] = x_[:, 1].max().item() / (ke[0].elapsed_time(ke[1]) * 1e6)
         results[name] = rec
         print(f"[bench]   {ms:.3f} ms/step  {rec['tflops']:.1f} TFLOP/s  kernel {kms:.3f} ms", file=sys.stderr, flush=True)
+    del outs
+    torch.cuda.empty_cache()
 
     det = {n: r for n, r in results.items() if not n.startswith("atomic")}
     atom = {n: r for n, r in results.items() if n.startswith("atomic")}
@@ -208,27 +254,18 @@ def main():
         try:
             from scheduling_persistent_fa_amd.profiling import kernel_source_digest
             c = json.load(open(PROFILE_COUNTERS))
-            if (c.get("workload") == args.workload and c.get("schedule") == best
+            if (c.get("workload") == workload and c.get("schedule") == best
                     and c.get("kernel_source_sha256") == kernel_source_digest()):
                 traffic = c.get("hbm_bytes_per_launch")
         except Exception:
             traffic = None
     kt = det[best]["kernel_tflops"]
     sclk = det[best].get("sclk_ghz_est")
-    line = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(det[best]["ms_per_step"], 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": args.workload, "B": B, "Hq": Hq, "Hkv": Hkv, "S": S, "Sk": Sk, "D": D,
+    return {
+        "wl": wl,
+        "value": value,
+        "ms_per_step": det[best]["ms_per_step"],
+        "config": {"workload": workload, "B": B, "Hq": Hq, "Hkv": Hkv, "S": S, "Sk": Sk, "D": D,
                    "mask": "causal" if causal else "full", "window": window, "tile": tile, "schedule": best,
                    "workgroups": info["num_cu"]},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
@@ -242,10 +279,6 @@ def main():
         "schedules": {n: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in r.items()}
                       for n, r in results.items()},
     }
-    if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(wl)
-    print(json.dumps(line), flush=True)
 
 
 def block_bench(args):

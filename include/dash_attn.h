@@ -52,7 +52,7 @@ enum dash_status {
   DASH_ERR_UNSUPPORTED = -2,      /* valid but not implemented: D, tile, mask/schedule pair, gang > workgroups, size */
   DASH_ERR_HIP = -3,              /* a HIP runtime call failed */
   DASH_ERR_INVALID_SCHEDULE = -4, /* a step list failed validation */
-  DASH_ERR_TIMEOUT = -5,          /* a workgroup gave up waiting on a dQ semaphore (reported with sync_check) */
+  DASH_ERR_TIMEOUT = -5,          /* a workgroup gave up waiting on a dQ semaphore (see dash_check_async_error) */
   DASH_ERR_WORKSPACE = -6         /* caller workspace too small or misaligned */
 };
 
@@ -105,6 +105,12 @@ typedef struct dash_bwd_opts {
                                 side by side.  0 = natural size (N, or N/2); negative = DASH_ERR_INVALID_ARG.
                                 The band shift of dash_attn_bwd_window deals its units over all workgroups
                                 and ignores this cap. */
+  uint32_t debug_delay_seed; /* testing: non-zero runs a separate build of the persistent kernel that sleeps
+                                a seeded 0..63 x 64 clocks before every dQ semaphore wait and release (a hash
+                                of seed, workgroup, step, wave); the result must be bitwise that of seed 0.
+                                Deterministic schedules only (ATOMIC: DASH_ERR_INVALID_ARG). */
+  int* xcc_id_out;           /* optional device buffer [num_workgroups]: the chiplet (XCC) each workgroup ran
+                                on, read from the hardware register */
 } dash_bwd_opts;
 
 /*
@@ -142,6 +148,24 @@ int dash_attn_fwd_window(const void* q, const void* k, const void* v, void* o, f
                          int window_left, int window_right, void* stream);
 
 /*
+ * Failure reporting of the backward calls.  A persistent workgroup that waits
+ * longer than spin_timeout_cycles on a dQ semaphore (which only happens when
+ * the grid is not co-resident, e.g. another kernel holds compute units) gives
+ * up, and every workgroup of the call exits.  The call's dQ, dK and dV are
+ * then written with NaN, and a per-device host-visible word records the
+ * failure: the next dash_attn_bwd* call on the device returns
+ * DASH_ERR_TIMEOUT (and launches nothing), as does dash_check_async_error.
+ * With sync_check the call itself synchronises and returns it.
+ *
+ * Workspace.  With opts->workspace NULL the library keeps one grow-only
+ * workspace per (device, stream): calls on one stream share it in stream
+ * order; calls on different streams never share one.  (A destroyed stream's
+ * workspace is kept until process exit; a new stream with the same handle
+ * value reuses it.)  The first call of a shape allocates its step lists and
+ * copies them with hipMemcpyAsync on `stream`; later calls of the shape
+ * allocate nothing as long as the workspace is large enough.  Up to 64 step
+ * lists are cached per process; evicting one synchronises the device.
+ *
  * Backward pass: dQ, dK, dV (bfloat16) from Q, K, V, O, dO (bfloat16) and
  * lse (float32).  schedule is a dash_schedule_kind; DASH_SCHED_AUTO runs
  * the one dash_schedule_choose picks (with its gang cap unless opts sets
@@ -209,8 +233,15 @@ int dash_attn_bwd_window(const void* q, const void* k, const void* v, const void
 /* Bytes of device workspace dash_attn_bwd needs for these sizes (fp32 dQ
  * accumulator over the query tiles' rows, Delta, semaphores, error word,
  * scratch tiles); an upper bound valid for any key length and tile when
- * S = Sq.  Returns DASH_OK or an error. */
-int dash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D, size_t* bytes);
+ * S = Sq.  mask (DASH_MASK_*) and schedule (dash_schedule_kind) are checked
+ * but do not change the size: every schedule uses the same layout.  Returns
+ * DASH_OK or DASH_ERR_INVALID_ARG. */
+int dash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D, int mask, int schedule, size_t* bytes);
+
+/* Synchronises `stream`, then returns DASH_ERR_TIMEOUT (and clears the
+ * record) if a backward call on the current device gave up on a dQ semaphore
+ * since the last report, else DASH_OK (DASH_ERR_HIP if synchronising fails). */
+int dash_check_async_error(void* stream);
 
 /* Delta[b,h,i] = sum_d dO[b,h,i,d] * O[b,h,i,d] in fp32 ([B*H*S] float32
  * output), the preprocess step of the backward pass, exposed for testing. */
@@ -260,9 +291,14 @@ int dash_schedule_validate(const dash_schedule* s);
 
 /* Unit-cost DAG model ([news] §2.2; [summary] §2.1): each step costs c of
  * compute then r of reduction, a reduction waits for its dQ tile's previous
- * ordinal.  Returns makespan and total waiting time. */
-int dash_schedule_simulate(const dash_schedule* s, double c, double r, double* makespan,
-                           double* total_wait);
+ * ordinal.  jitter_seed != 0 scales the compute cost of step i of workgroup w
+ * by a factor in [0.5, 1.5): 0.5 + (splitmix64(seed ^ (w << 32 | i)) >> 11)
+ * * 2^-53, with SplitMix64's output function (Steele, Lea and Flood, OOPSLA
+ * 2014) applied to its argument plus 0x9e3779b97f4a7c15; 0 = no jitter.
+ * Returns makespan and total waiting time; DASH_ERR_INVALID_SCHEDULE if the
+ * lists deadlock, DASH_ERR_INVALID_ARG for negative costs. */
+int dash_schedule_simulate(const dash_schedule* s, double c, double r, uint64_t jitter_seed,
+                           double* makespan, double* total_wait);
 
 void dash_schedule_free(dash_schedule* s);
 
@@ -297,8 +333,9 @@ int dash_schedule_choose_band(int Nq, int Nk, int band_left, int band_right, int
 const char* dash_status_string(int status);
 /* Message of the last error raised on the calling thread ("" if none). */
 const char* dash_last_error(void);
-/* Compute units, LDS bytes per workgroup and shader clock (kHz) of a device. */
-int dash_device_info(int device, int* num_cu, int* lds_bytes, int* clock_khz);
+/* Compute units, chiplets (XCDs), LDS bytes per workgroup and shader clock
+ * (kHz) of a device; any output may be NULL. */
+int dash_device_info(int device, int* num_cu, int* num_xcd, int* lds_bytes, int* clock_khz);
 
 #ifdef __cplusplus
 }

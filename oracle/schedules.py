@@ -372,12 +372,37 @@ def validate(lists: list[list[Step]], mask: int, N: int, g: int, groups: int, Nk
     simulate(lists, 1.0, 1.0)  # raises on deadlock
 
 
-def simulate(lists: list[list[Step]], c: float, r: float):
+_MASK64 = (1 << 64) - 1
+
+
+def splitmix64(x: int) -> int:
+    """SplitMix64's output function (Steele, Lea and Flood, "Fast splittable
+    pseudorandom number generators", OOPSLA 2014) applied to x advanced by
+    one golden-ratio increment."""
+    z = (x + 0x9E3779B97F4A7C15) & _MASK64
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _MASK64
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _MASK64
+    return z ^ (z >> 31)
+
+
+def jitter(seed: int, w: int, i: int) -> float:
+    """Cost factor in [0.5, 1.5) of step i of workgroup w: a counter-based
+    draw, seed ^ (w << 32 | i) through SplitMix64 (1.0 when seed is 0)."""
+    if seed == 0:
+        return 1.0
+    x = (seed ^ ((w << 32) | i)) & _MASK64
+    return 0.5 + (splitmix64(x) >> 11) * 2.0 ** -53
+
+
+def simulate(lists: list[list[Step]], c: float, r: float, jitter_seed: int = 0):
     """Unit-cost DAG model of [news] §2.2 / [summary] §2.1.
 
     Every step costs c of compute and then r of reduction into its dQ tile;
     the reduction may start only after the tile's previous ordinal finished
     its own.  A workgroup runs its list in order and idles while waiting.
+    With a non-zero ``jitter_seed`` step i of workgroup w costs
+    c * jitter(seed, w, i) of compute instead (timing noise; the order a
+    schedule fixes must not deadlock under any of it).
     Returns (makespan, total wait).  Raises ScheduleError on deadlock.
     """
     P = len(lists)
@@ -395,7 +420,7 @@ def simulate(lists: list[list[Step]], c: float, r: float):
                 key = (s.head, s.qi)
                 if count.get(key, 0) != s.ord:
                     break
-                ready = t[w] + c
+                ready = t[w] + c * jitter(jitter_seed, w, idx[w])
                 start = max(ready, done_at.get(key, 0.0))
                 wait += start - ready
                 t[w] = start + r

@@ -37,7 +37,7 @@ EXPORTS = (
     "dash_schedule_validate", "dash_schedule_simulate", "dash_schedule_free", "dash_schedule_choose",
     "dash_schedule_choose_qk", "dash_schedule_choose_band",
     "dash_status_string",
-    "dash_last_error", "dash_device_info",
+    "dash_last_error", "dash_device_info", "dash_check_async_error",
 )
 
 
@@ -62,6 +62,8 @@ class BwdOpts(ctypes.Structure):
         ("event_start", ctypes.c_void_p),
         ("event_stop", ctypes.c_void_p),
         ("max_gang", ctypes.c_int),
+        ("debug_delay_seed", ctypes.c_uint32),
+        ("xcc_id_out", ctypes.c_void_p),
     ]
 
 
@@ -79,7 +81,7 @@ def _declare(lib):
     lib.dash_attn_bwd_window.argtypes = [vp] * 9 + [i, i, i, i, i, i, f, i, i, i, ctypes.POINTER(BwdOpts), vp]
     lib.dash_schedule_build_band.argtypes = [i, i, i, i, i, i, i, i, i, i, i, ctypes.POINTER(vp)]
     lib.dash_schedule_choose_band.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
-    lib.dash_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, ctypes.POINTER(ctypes.c_size_t)]
+    lib.dash_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(ctypes.c_size_t)]
     lib.dash_attn_bwd_delta.argtypes = [vp, vp, vp, i, i, i, i, vp]
     lib.dash_schedule_build.argtypes = [i, i, i, i, i, i, i, i, i, ctypes.POINTER(vp)]
     lib.dash_schedule_build_qk.argtypes = [i, i, i, i, i, i, i, i, i, i, ctypes.POINTER(vp)]
@@ -88,7 +90,7 @@ def _declare(lib):
     lib.dash_schedule_num_steps.restype = ctypes.c_longlong
     lib.dash_schedule_export.argtypes = [vp, i32p, i32p]
     lib.dash_schedule_validate.argtypes = [vp]
-    lib.dash_schedule_simulate.argtypes = [vp, ctypes.c_double, ctypes.c_double,
+    lib.dash_schedule_simulate.argtypes = [vp, ctypes.c_double, ctypes.c_double, ctypes.c_uint64,
                                            ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
     lib.dash_schedule_free.argtypes = [vp]
     lib.dash_schedule_free.restype = None
@@ -98,7 +100,8 @@ def _declare(lib):
     lib.dash_status_string.restype = ctypes.c_char_p
     lib.dash_last_error.argtypes = []
     lib.dash_last_error.restype = ctypes.c_char_p
-    lib.dash_device_info.argtypes = [i, ctypes.POINTER(i), ctypes.POINTER(i), ctypes.POINTER(i)]
+    lib.dash_device_info.argtypes = [i, ctypes.POINTER(i), ctypes.POINTER(i), ctypes.POINTER(i), ctypes.POINTER(i)]
+    lib.dash_check_async_error.argtypes = [vp]
 
 
 def lib():

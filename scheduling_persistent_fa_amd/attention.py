@@ -66,7 +66,7 @@ def attn_fwd(q, k, v, causal: bool, scale: float = 0.0, out=None, lse=None, stre
 def make_opts(num_workgroups: int = 0, tile: int = 0, atomic_walk: int = -1, xcd_local: bool = True,
               workspace: torch.Tensor | None = None, stall: torch.Tensor | None = None,
               spin_timeout_cycles: int = 0, sync_check: bool = False, events=None,
-              max_gang: int = 0) -> _lib.BwdOpts:
+              max_gang: int = 0, delay_seed: int = 0, xcc: torch.Tensor | None = None) -> _lib.BwdOpts:
     o = _lib.BwdOpts()
     o.struct_size = ctypes.sizeof(_lib.BwdOpts)
     o.num_workgroups = num_workgroups
@@ -84,6 +84,9 @@ def make_opts(num_workgroups: int = 0, tile: int = 0, atomic_walk: int = -1, xcd
         o.event_start = events[0].cuda_event
         o.event_stop = events[1].cuda_event
     o.max_gang = max_gang
+    o.debug_delay_seed = delay_seed
+    if xcc is not None:
+        o.xcc_id_out = xcc.data_ptr()
     return o
 
 
@@ -101,6 +104,8 @@ def attn_bwd(q, k, v, o, do, lse, causal: bool, schedule: int, scale: float = 0.
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    for name, t, shp in (("dq", dq, (B, Hq, Sq, D)), ("dk", dk, (B, Hkv, Sk, D)), ("dv", dv, (B, Hkv, Sk, D))):
+        _check_bhsd(name, t, shp)
     op = ctypes.byref(opts) if opts is not None else None
     ptrs = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv))
     if window is None:
@@ -122,16 +127,23 @@ def bwd_delta(o, do, stream=None):
     return delta
 
 
-def workspace_bytes(B, Hq, Hkv, S, D) -> int:
+def workspace_bytes(B, Hq, Hkv, S, D, mask: int = MASK_FULL, schedule: int = AUTO) -> int:
     n = ctypes.c_size_t()
-    _lib.check(_lib.lib().dash_attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, ctypes.byref(n)))
+    _lib.check(_lib.lib().dash_attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, mask, schedule, ctypes.byref(n)))
     return n.value
 
 
+def check_async_error(stream=None) -> None:
+    """Synchronise the stream and raise DashError(ERR_TIMEOUT) if a backward
+    call on the device gave up on a dQ semaphore since the last report."""
+    _lib.check(_lib.lib().dash_check_async_error(_stream(stream)))
+
+
 def device_info(device: int = 0):
-    cu, lds, clk = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
-    _lib.check(_lib.lib().dash_device_info(device, ctypes.byref(cu), ctypes.byref(lds), ctypes.byref(clk)))
-    return {"num_cu": cu.value, "lds_bytes": lds.value, "clock_khz": clk.value}
+    cu, xcd, lds, clk = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _lib.check(_lib.lib().dash_device_info(device, ctypes.byref(cu), ctypes.byref(xcd), ctypes.byref(lds),
+                                           ctypes.byref(clk)))
+    return {"num_cu": cu.value, "num_xcd": xcd.value, "lds_bytes": lds.value, "clock_khz": clk.value}
 
 
 def bf16_from_bits(bits, device="cuda") -> torch.Tensor:

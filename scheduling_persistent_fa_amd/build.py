@@ -47,5 +47,43 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
     return LIB
 
 
+def resource_table() -> str:
+    """Markdown table of the compiler's resource use per kernel of kernels.hip
+    (registers, scratch spill, LDS, occupancy), from
+    -Rpass-analysis=kernel-resource-usage on a device-only compile."""
+    import re
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "--cuda-device-only", "-c",
+           *DEVICE_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-o", os.devnull, os.path.join(CSRC, "kernels.hip")]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(r.stderr)
+    rows, cur = [], None
+    for line in r.stderr.splitlines():
+        m = re.search(r"remark:\s+(.*?): (.*?) \[-Rpass-analysis", line)
+        if not m:
+            continue
+        key, val = m.group(1).strip(), m.group(2).strip()
+        if key == "Function Name":
+            cur = {"name": val}
+            rows.append(cur)
+        elif cur is not None:
+            cur[key] = val
+    names = [r_["name"] for r_ in rows]
+    cxxfilt = shutil.which("c++filt") or shutil.which("llvm-cxxfilt")
+    if cxxfilt:
+        out = subprocess.run([cxxfilt], input="\n".join(names), capture_output=True, text=True).stdout.split("\n")
+        for r_, n in zip(rows, out):
+            r_["name"] = n.replace("dash::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+    cols = ["VGPRs", "AGPRs", "ScratchSize [bytes/lane]", "VGPRs Spill", "LDS Size [bytes/block]",
+            "Occupancy [waves/SIMD]"]
+    lines = ["| kernel | " + " | ".join(cols) + " |", "|---" * (len(cols) + 1) + "|"]
+    for r_ in rows:
+        lines.append(f"| `{r_['name']}` | " + " | ".join(r_.get(c, "") for c in cols) + " |")
+    return "\n".join(lines)
+
+
 if __name__ == "__main__":
-    build(verbose=True, resource_usage="--resource-usage" in sys.argv)
+    if "--resource-table" in sys.argv:
+        print(resource_table())
+    else:
+        build(verbose=True, resource_usage="--resource-usage" in sys.argv)

@@ -1,8 +1,10 @@
 // C ABI of libdash_attn.so (declared in include/dash_attn.h).
 //
 // Everything is validated before anything is enqueued.  The library owns a
-// per-device cache of uploaded step lists and, when the caller passes no
-// workspace, a grow-only per-device workspace; both live until process exit.
+// bounded per-device cache of uploaded step lists, one grow-only workspace per
+// (device, stream) for callers that pass none, and one host-visible word per
+// device in which the dQ finalize kernel records a semaphore give-up; all of
+// it lives until process exit (evicted step lists are freed earlier).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -38,7 +40,7 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 struct DeviceInfo {
-  int num_cu = 0, lds = 0, clock_khz = 0;
+  int num_cu = 0, num_xcd = 0, lds = 0, clock_khz = 0;
 };
 
 std::mutex g_mu;
@@ -55,27 +57,88 @@ int device_info(int dev, DeviceInfo* out) {
     d.num_cu = p.multiProcessorCount;
     d.lds = (int)p.sharedMemPerBlock;
     d.clock_khz = p.clockRate;
+    e = hipDeviceGetAttribute(&d.num_xcd, hipDeviceAttributeNumberOfXccs, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(NumberOfXccs)");
     it = g_devinfo.emplace(dev, d).first;
   }
   *out = it->second;
   return DASH_OK;
 }
 
-// Uploaded step lists, keyed by everything that shapes them.
+// Uploaded step lists, keyed by everything that shapes them.  The host copy
+// stays alive with the entry, so that the asynchronous upload never reads
+// freed memory.  At most kSchedCacheEntries entries are kept; the least
+// recently used one is evicted (after a device synchronisation, since queued
+// kernels may still read it).
 struct DevSchedule {
   int32_t* steps = nullptr;
   int32_t* offsets = nullptr;
   long long num_steps = 0;
+  std::shared_ptr<dash::Schedule> host;
+  unsigned long long last_use = 0;
+  // Recorded after the upload on the uploading stream; a call on another
+  // stream waits for it until it is seen complete (then it is released).
+  hipEvent_t uploaded = nullptr;
+  hipStream_t upload_stream = nullptr;
 };
 // dev, mask, kind, Nq, Nk, g, groups, P, xcd, walk, cap, band_l, band_r
 using SchedKey = std::tuple<int, int, int, int, int, int, int, int, int, int, int, int, int>;
 std::map<SchedKey, DevSchedule> g_sched;
+unsigned long long g_sched_clock = 0;
+constexpr size_t kSchedCacheEntries = 64;
 
+// Library-managed workspaces, one per (device, stream): calls on different
+// streams never share semaphores or dQ accumulators.  Calls on one stream are
+// ordered by the stream, so they can share one.
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
 };
-std::map<int, Workspace> g_ws;
+std::map<std::pair<int, void*>, Workspace> g_ws;
+
+// Per device: a host-visible word that the dQ finalize kernel sets when a
+// workgroup of the persistent kernel gave up waiting on a semaphore (pinned,
+// mapped host memory), and the co-resident workgroup capacity per kernel
+// family (occupancy queries are not repeated per call).
+struct DeviceState {
+  int* sticky_host = nullptr;
+  int* sticky_dev = nullptr;
+  std::map<std::tuple<int, int, bool>, int> per_cu;  // (D, T, atomic) -> workgroups per CU
+};
+std::map<int, DeviceState> g_dev;
+
+// Pinned word of `dev`, allocated on first use (nullptr if that fails).
+int sticky_word(int dev, int** host, int** devp) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  DeviceState& d = g_dev[dev];
+  if (!d.sticky_host) {
+    void* h = nullptr;
+    hipError_t e = hipHostMalloc(&h, 64, hipHostMallocMapped | hipHostMallocCoherent);
+    if (e != hipSuccess) return hip_fail(e, "hipHostMalloc(error word)");
+    void* dp = nullptr;
+    e = hipHostGetDevicePointer(&dp, h, 0);
+    if (e != hipSuccess) { (void)hipHostFree(h); return hip_fail(e, "hipHostGetDevicePointer(error word)"); }
+    std::memset(h, 0, 64);
+    d.sticky_host = (int*)h;
+    d.sticky_dev = (int*)dp;
+  }
+  *host = d.sticky_host;
+  *devp = d.sticky_dev;
+  return DASH_OK;
+}
+
+// Takes (and clears) a give-up that an earlier call on `dev` recorded.
+int take_sticky_error(int dev) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_dev.find(dev);
+  if (it == g_dev.end() || !it->second.sticky_host) return DASH_OK;
+  volatile int* w = it->second.sticky_host;
+  if (*w == 0) return DASH_OK;
+  *w = 0;
+  return fail(DASH_ERR_TIMEOUT,
+              "an earlier backward call on this device gave up waiting on a dQ semaphore; its dQ, dK and dV were "
+              "set to NaN");
+}
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -223,14 +286,24 @@ const char* dash_status_string(int status) {
 
 const char* dash_last_error(void) { return g_last_error.c_str(); }
 
-int dash_device_info(int device, int* num_cu, int* lds_bytes, int* clock_khz) {
+int dash_device_info(int device, int* num_cu, int* num_xcd, int* lds_bytes, int* clock_khz) {
   DeviceInfo d;
   int st = device_info(device, &d);
   if (st) return st;
   if (num_cu) *num_cu = d.num_cu;
+  if (num_xcd) *num_xcd = d.num_xcd;
   if (lds_bytes) *lds_bytes = d.lds;
   if (clock_khz) *clock_khz = d.clock_khz;
   return DASH_OK;
+}
+
+int dash_check_async_error(void* stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  return take_sticky_error(dev);
 }
 
 int dash_schedule_build(int mask, int schedule, int N, int g, int groups, int P, int xcd_local, int atomic_walk,
@@ -287,9 +360,12 @@ int dash_schedule_validate(const dash_schedule* s) {
   return err.empty() ? DASH_OK : fail(DASH_ERR_INVALID_SCHEDULE, err);
 }
 
-int dash_schedule_simulate(const dash_schedule* s, double c, double r, double* makespan, double* total_wait) {
+int dash_schedule_simulate(const dash_schedule* s, double c, double r, uint64_t jitter_seed, double* makespan,
+                           double* total_wait) {
   if (!s) return fail(DASH_ERR_INVALID_ARG, "null schedule");
-  if (!dash::simulate_schedule(s->s, c, r, makespan, total_wait)) return fail(DASH_ERR_INVALID_SCHEDULE, "deadlock");
+  if (!(c >= 0.0) || !(r >= 0.0)) return fail(DASH_ERR_INVALID_ARG, "step costs must be non-negative");
+  if (!dash::simulate_schedule(s->s, c, r, jitter_seed, makespan, total_wait))
+    return fail(DASH_ERR_INVALID_SCHEDULE, "deadlock");
   return DASH_OK;
 }
 
@@ -344,9 +420,11 @@ int dash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
   return dash_attn_fwd_qk(q, k, v, o, lse, B, Hq, Hkv, S, S, D, softmax_scale, mask, stream);
 }
 
-int dash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D, size_t* bytes) {
+int dash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D, int mask, int schedule, size_t* bytes) {
   if (!bytes) return fail(DASH_ERR_INVALID_ARG, "null output");
   if (B < 0 || Hq <= 0 || Hkv <= 0 || S < 0 || D <= 0) return fail(DASH_ERR_INVALID_ARG, "sizes must not be negative");
+  if (mask != DASH_MASK_FULL && mask != DASH_MASK_CAUSAL) return fail(DASH_ERR_INVALID_ARG, "unknown mask");
+  if (schedule < DASH_SCHED_SERIAL || schedule > DASH_SCHED_AUTO) return fail(DASH_ERR_INVALID_ARG, "unknown schedule");
   // Any key length and tile: at most round_up(S, T) + T virtual rows per head.
   *bytes = ws_layout(B, Hq, S, ((S + 127) / 128) * 128 + 128, D).total;
   return DASH_OK;
@@ -369,134 +447,197 @@ static int zero_bf16(void* p, long long elems, int D, hipStream_t st) {
   return e == hipSuccess ? DASH_OK : hip_fail(e, "zero-fill launch");
 }
 
-static int bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
-                    void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk, int D, float softmax_scale,
-                    const Mask& mask, int schedule, const dash_bwd_opts* opts, void* stream) {
-  const void* ptrs[] = {q, k, v, o, dO, lse, dq, dk, dv};
+// Everything a backward call decides before it touches a buffer: validated
+// sizes and options, the tile grid, the schedule, and the workspace layout.
+struct BwdPlan {
+  dash_bwd_opts op;
+  int dev = 0;
+  DeviceInfo di;
+  TileGrid tg;
+  int B = 0, Hq = 0, Hkv = 0, Sq = 0, Sk = 0, D = 0;
+  int T = 0, P = 0, g = 1, groups = 1, schedule = 0, xcd = 1, walk = -1, band_l = -1, band_r = -1;
+  bool atomic = false, empty = false;
+  float scale = 0.f;
+  long long kv_elems = 0;
+  WsLayout L;
+  SchedKey key;
+};
+
+// Validates a backward call and fills `pl` (no device work, no allocation).
+// pl->empty: no query rows, only dK = dV = 0 to write.
+static int bwd_plan(const void* const* ptrs, int B, int Hq, int Hkv, int Sq, int Sk, int D, float softmax_scale,
+                    const Mask& mask, int schedule, const dash_bwd_opts* opts, BwdPlan* pl) {
   int st = check_sizes(B, Hq, Hkv, Sq, Sk, D, mask);
   if (st != DASH_OK && st != kEmpty) return st;
   if (schedule < DASH_SCHED_SERIAL || schedule > DASH_SCHED_AUTO) return fail(DASH_ERR_INVALID_ARG, "unknown schedule");
-  const long long kv_elems = (long long)B * Hkv * Sk * D;
+  pl->B = B;
+  pl->Hq = Hq;
+  pl->Hkv = Hkv;
+  pl->Sq = Sq;
+  pl->Sk = Sk;
+  pl->D = D;
+  pl->kv_elems = (long long)B * Hkv * Sk * D;
   if (st == kEmpty) {
-    // No query rows: dQ is empty and dK = dV = 0 (no key receives any gradient).
-    if (kv_elems == 0) return DASH_OK;
-    const void* kv_ptrs[] = {dk, dv};
-    st = check_ptrs(kv_ptrs, 2);
-    if (st) return st;
-    st = zero_bf16(dk, kv_elems, D, (hipStream_t)stream);
-    return st ? st : zero_bf16(dv, kv_elems, D, (hipStream_t)stream);
+    pl->empty = true;
+    if (pl->kv_elems == 0) return DASH_OK;
+    return check_ptrs(ptrs + 7, 2);  // dk, dv
   }
   st = check_ptrs(ptrs, 9);
   if (st) return st;
-  dash_bwd_opts op;
+  dash_bwd_opts& op = pl->op;
   std::memset(&op, 0, sizeof(op));
   if (opts) {
     if (opts->struct_size == 0 || opts->struct_size > sizeof(dash_bwd_opts))
       return fail(DASH_ERR_INVALID_ARG, "dash_bwd_opts.struct_size must be sizeof(dash_bwd_opts)");
     std::memcpy(&op, opts, opts->struct_size);
   }
-  hipStream_t strm = (hipStream_t)stream;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  hipError_t e = hipGetDevice(&pl->dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  DeviceInfo di;
-  st = device_info(dev, &di);
+  st = device_info(pl->dev, &pl->di);
   if (st) return st;
 
   const int T = op.tile ? op.tile : (std::min(Sq, Sk) < 512 ? 64 : 128);
   if (T != 64 && T != 128) return fail(DASH_ERR_UNSUPPORTED, "tile must be 64 or 128");
-  const TileGrid tg = tile_grid(Sq, Sk, T, mask.aligned());
-  const int Nq = tg.Nq, Nk = tg.Nk;
+  pl->T = T;
+  pl->tg = tile_grid(Sq, Sk, T, mask.aligned());
+  const int Nq = pl->tg.Nq, Nk = pl->tg.Nk;
   // band extents in tiles: a window of w rows reaches ceil(w / T) tiles off the diagonal tile
-  const int band_l = mask.kind == dash::kMaskBand && mask.wl >= 0 ? (mask.wl + T - 1) / T : -1;
-  const int band_r = mask.kind == dash::kMaskBand && mask.wr >= 0 ? (mask.wr + T - 1) / T : -1;
-  const int P = op.num_workgroups > 0 ? op.num_workgroups : di.num_cu;
+  pl->band_l = mask.kind == dash::kMaskBand && mask.wl >= 0 ? (mask.wl + T - 1) / T : -1;
+  pl->band_r = mask.kind == dash::kMaskBand && mask.wr >= 0 ? (mask.wr + T - 1) / T : -1;
   if (op.num_workgroups < 0) return fail(DASH_ERR_INVALID_ARG, "negative workgroup count");
   if (op.max_gang < 0) return fail(DASH_ERR_INVALID_ARG, "negative gang cap");
-  const int g = Hq / Hkv;
+  pl->P = op.num_workgroups > 0 ? op.num_workgroups : pl->di.num_cu;
+  pl->g = Hq / Hkv;
   if (schedule == DASH_SCHED_AUTO) {
     int cap = 0;
-    std::string err = dash::choose_schedule(mask.kind, Nq, Nk, D, g, P, &schedule, &cap, band_l, band_r);
+    std::string err = dash::choose_schedule(mask.kind, Nq, Nk, D, pl->g, pl->P, &schedule, &cap, pl->band_l, pl->band_r);
     if (!err.empty()) return fail(DASH_ERR_INVALID_ARG, err);
     if (op.max_gang == 0) op.max_gang = cap;
   }
-  const int groups = B * Hkv;
-  const bool atomic = schedule == DASH_SCHED_ATOMIC;
-  const int xcd = op.xcd_local >= 0 ? 1 : 0;
-  const int walk = atomic ? op.atomic_walk : -1;
-  const float scale = default_scale(softmax_scale, D);
+  pl->schedule = schedule;
+  pl->groups = B * Hkv;
+  pl->atomic = schedule == DASH_SCHED_ATOMIC;
+  if (op.debug_delay_seed && pl->atomic) return fail(DASH_ERR_INVALID_ARG, "delay injection needs a deterministic schedule");
+  pl->xcd = op.xcd_local >= 0 ? 1 : 0;
+  pl->walk = pl->atomic ? op.atomic_walk : -1;
+  pl->scale = default_scale(softmax_scale, D);
+  pl->L = ws_layout(B, Hq, Sq, pl->tg.Sw, D);
+  pl->key = SchedKey{pl->dev, mask.kind, schedule, Nq, Nk, pl->g, pl->groups, pl->P, pl->xcd,
+                     pl->atomic ? (pl->walk < 0 ? -1 : pl->walk) : -1, op.max_gang, pl->band_l, pl->band_r};
 
   // Co-residency: the semaphore waits need every workgroup resident at once.
-  if (!atomic) {
-    bool fits = false;
-    e = dash::bwd_kernel_fits(D, T, false, di.num_cu, P, &fits);
-    if (e != hipSuccess) return hip_fail(e, "occupancy query");
-    if (!fits) return fail(DASH_ERR_UNSUPPORTED, "persistent grid larger than the co-resident capacity");
-  }
-
-  // Step lists (validated once, then cached on the device).
-  DevSchedule ds;
-  {
-    std::lock_guard<std::mutex> lk(g_mu);
-    SchedKey key{dev, mask.kind, schedule, Nq, Nk, g, groups, P, xcd, atomic ? (walk < 0 ? -1 : walk) : -1, op.max_gang,
-                 band_l, band_r};
-    auto it = g_sched.find(key);
-    if (it == g_sched.end()) {
-      dash::Schedule s;
-      std::string err = dash::build_schedule(mask.kind, schedule, Nq, Nk, g, groups, P, xcd != 0, walk, op.max_gang, &s,
-                                             band_l, band_r);
-      if (!err.empty()) return fail(DASH_ERR_UNSUPPORTED, err);
-      err = dash::validate_schedule(s);
-      if (!err.empty()) return fail(DASH_ERR_INVALID_SCHEDULE, err);
-      DevSchedule d;
-      d.num_steps = (long long)s.steps.size();
-      e = hipMalloc((void**)&d.steps, std::max<size_t>(16, s.steps.size() * sizeof(dash::StepRec)));
-      if (e != hipSuccess) return hip_fail(e, "hipMalloc(steps)");
-      e = hipMalloc((void**)&d.offsets, s.offsets.size() * sizeof(int32_t));
-      if (e != hipSuccess) { (void)hipFree(d.steps); return hip_fail(e, "hipMalloc(offsets)"); }
-      e = hipMemcpy(d.steps, s.steps.data(), s.steps.size() * sizeof(dash::StepRec), hipMemcpyHostToDevice);
-      if (e == hipSuccess)
-        e = hipMemcpy(d.offsets, s.offsets.data(), s.offsets.size() * sizeof(int32_t), hipMemcpyHostToDevice);
-      if (e != hipSuccess) { (void)hipFree(d.steps); (void)hipFree(d.offsets); return hip_fail(e, "hipMemcpy(schedule)"); }
-      it = g_sched.emplace(key, d).first;
+  if (!pl->atomic) {
+    int per_cu = -1;
+    {
+      std::lock_guard<std::mutex> lk(g_mu);
+      auto& m = g_dev[pl->dev].per_cu;
+      auto it = m.find(std::make_tuple(D, T, false));
+      if (it != m.end()) per_cu = it->second;
     }
-    ds = it->second;
-  }
-
-  // Workspace.
-  const WsLayout L = ws_layout(B, Hq, Sq, tg.Sw, D);
-  char* ws = nullptr;
-  if (op.workspace) {
-    if (reinterpret_cast<uintptr_t>(op.workspace) % 256) return fail(DASH_ERR_WORKSPACE, "workspace not 256-byte aligned");
-    if (op.workspace_bytes < L.total) return fail(DASH_ERR_WORKSPACE, "workspace too small");
-    ws = (char*)op.workspace;
-  } else {
-    std::lock_guard<std::mutex> lk(g_mu);
-    Workspace& w = g_ws[dev];
-    if (w.bytes < L.total) {
-      // The previous buffer may still be in use by queued work on any stream.
-      if (w.ptr) {
-        e = hipDeviceSynchronize();
-        if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-        (void)hipFree(w.ptr);
-        w.ptr = nullptr;
-        w.bytes = 0;
-      }
-      e = hipMalloc(&w.ptr, L.total);
-      if (e != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
-      w.bytes = L.total;
+    if (per_cu < 0) {
+      e = dash::bwd_kernel_per_cu(D, T, false, &per_cu);
+      if (e != hipSuccess) return hip_fail(e, "occupancy query");
+      std::lock_guard<std::mutex> lk(g_mu);
+      g_dev[pl->dev].per_cu[std::make_tuple(D, T, false)] = per_cu;
     }
-    ws = (char*)w.ptr;
+    if ((long long)per_cu * pl->di.num_cu < pl->P)
+      return fail(DASH_ERR_UNSUPPORTED, "persistent grid larger than the co-resident capacity");
   }
+  return DASH_OK;
+}
+
+// Builds and validates the step lists of a plan (host memory only).
+static int build_host_schedule(const BwdPlan& pl, int mask_kind, std::shared_ptr<dash::Schedule>* out) {
+  auto s = std::make_shared<dash::Schedule>();
+  std::string err = dash::build_schedule(mask_kind, pl.schedule, pl.tg.Nq, pl.tg.Nk, pl.g, pl.groups, pl.P, pl.xcd != 0,
+                                         pl.walk, pl.op.max_gang, s.get(), pl.band_l, pl.band_r);
+  if (!err.empty()) return fail(DASH_ERR_UNSUPPORTED, err);
+  err = dash::validate_schedule(*s);
+  if (!err.empty()) return fail(DASH_ERR_INVALID_SCHEDULE, err);
+  *out = std::move(s);
+  return DASH_OK;
+}
+
+// The plan's step lists on its device: from the cache, or built, validated
+// and uploaded on `strm` (asynchronously; the host copy stays in the cache).
+static int device_schedule(const BwdPlan& pl, int mask_kind, hipStream_t strm, DevSchedule* out) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_sched.find(pl.key);
+  if (it == g_sched.end()) {
+    if (g_sched.size() >= kSchedCacheEntries) {
+      auto lru = g_sched.begin();
+      for (auto j = g_sched.begin(); j != g_sched.end(); ++j)
+        if (j->second.last_use < lru->second.last_use) lru = j;
+      hipError_t e = hipDeviceSynchronize();  // queued kernels may still read the evicted lists
+      if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+      (void)hipFree(lru->second.steps);
+      (void)hipFree(lru->second.offsets);
+      if (lru->second.uploaded) (void)hipEventDestroy(lru->second.uploaded);
+      g_sched.erase(lru);
+    }
+    std::shared_ptr<dash::Schedule> s;
+    int st = build_host_schedule(pl, mask_kind, &s);
+    if (st) return st;
+    DevSchedule d;
+    d.num_steps = (long long)s->steps.size();
+    hipError_t e = hipMalloc((void**)&d.steps, std::max<size_t>(16, s->steps.size() * sizeof(dash::StepRec)));
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc(steps)");
+    e = hipMalloc((void**)&d.offsets, s->offsets.size() * sizeof(int32_t));
+    if (e != hipSuccess) { (void)hipFree(d.steps); return hip_fail(e, "hipMalloc(offsets)"); }
+    e = hipMemcpyAsync(d.steps, s->steps.data(), s->steps.size() * sizeof(dash::StepRec), hipMemcpyHostToDevice, strm);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(d.offsets, s->offsets.data(), s->offsets.size() * sizeof(int32_t), hipMemcpyHostToDevice, strm);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&d.uploaded, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventRecord(d.uploaded, strm);
+    if (e != hipSuccess) {
+      (void)hipFree(d.steps);
+      (void)hipFree(d.offsets);
+      if (d.uploaded) (void)hipEventDestroy(d.uploaded);
+      return hip_fail(e, "hipMemcpyAsync(schedule)");
+    }
+    d.upload_stream = strm;
+    d.host = std::move(s);
+    it = g_sched.emplace(pl.key, std::move(d)).first;
+  }
+  DevSchedule& d = it->second;
+  if (d.uploaded && d.upload_stream != strm) {
+    // The lists may still be in flight on the uploading stream.
+    hipError_t e = hipEventQuery(d.uploaded);
+    if (e == hipSuccess) {
+      (void)hipEventDestroy(d.uploaded);
+      d.uploaded = nullptr;
+    } else if (e == hipErrorNotReady) {
+      e = hipStreamWaitEvent(strm, d.uploaded, 0);
+      if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent(schedule upload)");
+    } else {
+      return hip_fail(e, "hipEventQuery(schedule upload)");
+    }
+  }
+  d.last_use = ++g_sched_clock;
+  *out = d;
+  return DASH_OK;
+}
+
+// Enqueues the three kernels of a planned call on `strm` with workspace `ws`
+// (pl.L.total bytes) and step lists `ds`; `sticky` is the device address of
+// the host-visible give-up word (may be null).
+static int bwd_enqueue(const BwdPlan& pl, const void* const* ptrs, const Mask& mask, char* ws, const DevSchedule& ds,
+                       int* sticky, hipStream_t strm) {
+  const void *q = ptrs[0], *k = ptrs[1], *v = ptrs[2], *o = ptrs[3], *dO = ptrs[4];
+  const float* lse = (const float*)ptrs[5];
+  void *dq = const_cast<void*>(ptrs[6]), *dk = const_cast<void*>(ptrs[7]), *dv = const_cast<void*>(ptrs[8]);
+  const dash_bwd_opts& op = pl.op;
+  const WsLayout& L = pl.L;
+  const int D = pl.D;
   float* ws_dq = (float*)(ws + L.ws_dq);
   float* delta = (float*)(ws + L.delta);
   int* sem = (int*)(ws + L.sem);
   int* err = (int*)(ws + L.err);
-  const long long rows = (long long)B * Hq * Sq;
+  const long long rows = (long long)pl.B * pl.Hq * pl.Sq;
   const long long n_sem = (long long)((L.err - L.sem) / 4) + 4;  // semaphores, padding and the error word
-
-  const long long ws_elems = (long long)B * Hq * tg.Sw * D;
-  e = dash::launch_delta(o, dO, delta, rows, D, sem, n_sem, atomic ? ws_dq : nullptr, atomic ? ws_elems : 0, strm);
+  const long long ws_elems = (long long)pl.B * pl.Hq * pl.tg.Sw * D;
+  hipError_t e = dash::launch_delta(o, dO, delta, rows, D, sem, n_sem, pl.atomic ? ws_dq : nullptr,
+                                    pl.atomic ? ws_elems : 0, strm);
   if (e != hipSuccess) return hip_fail(e, "preprocess launch");
 
   dash::BwdLaunch bl;
@@ -515,27 +656,29 @@ static int bwd_impl(const void* q, const void* k, const void* v, const void* o, 
   bl.steps = ds.steps;
   bl.offsets = ds.offsets;
   bl.stall = op.stall_cycles_out;
+  bl.xcc = op.xcc_id_out;
+  bl.delay_seed = op.debug_delay_seed;
   const unsigned long long budget_cycles = op.spin_timeout_cycles ? op.spin_timeout_cycles : (1ULL << 33);
   // wait budget in 100 MHz real-time ticks, from shader cycles at the device clock
-  bl.spin_ticks = (long long)((double)budget_cycles * 1e5 / std::max(1, di.clock_khz));
+  bl.spin_ticks = (long long)((double)budget_cycles * 1e5 / std::max(1, pl.di.clock_khz));
   if (bl.spin_ticks < 1) bl.spin_ticks = 1;
-  bl.scale = scale;
-  bl.Sq = Sq;
-  bl.Sk = Sk;
+  bl.scale = pl.scale;
+  bl.Sq = pl.Sq;
+  bl.Sk = pl.Sk;
   bl.D = D;
-  bl.T = T;
-  bl.g = g;
+  bl.T = pl.T;
+  bl.g = pl.g;
   bl.wl = mask.wl;
   bl.wr = mask.wr;
-  bl.qshift = tg.qshift;
-  bl.nblk = tg.Sw / 64;
-  bl.diag_off = tg.diag_off;
-  bl.P = P;
-  bl.atomic = atomic;
+  bl.qshift = pl.tg.qshift;
+  bl.nblk = pl.tg.Sw / 64;
+  bl.diag_off = pl.tg.diag_off;
+  bl.P = pl.P;
+  bl.atomic = pl.atomic;
   // Key/value tiles that no query tile sees have no chain: their dK/dV are zero.
-  if (band_l >= 0 && tg.diag_off > band_l) {
-    st = zero_bf16(dk, kv_elems, D, strm);
-    if (!st) st = zero_bf16(dv, kv_elems, D, strm);
+  if (pl.band_l >= 0 && pl.tg.diag_off > pl.band_l) {
+    int st = zero_bf16(dk, pl.kv_elems, D, strm);
+    if (!st) st = zero_bf16(dv, pl.kv_elems, D, strm);
     if (st) return st;
   }
   if (op.event_start) {
@@ -548,7 +691,22 @@ static int bwd_impl(const void* q, const void* k, const void* v, const void* o, 
     e = hipEventRecord((hipEvent_t)op.event_stop, strm);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord(stop)");
   }
-  e = dash::launch_dq_finalize(ws_dq, dq, ws_elems, D, scale, atomic, tg.Sw / 64, tg.qshift, Sq, strm);
+  dash::FinalizeLaunch fl;
+  fl.ws = ws_dq;
+  fl.dq = dq;
+  fl.dk = dk;
+  fl.dv = dv;
+  fl.err = err;
+  fl.sticky = sticky;
+  fl.ws_elems = ws_elems;
+  fl.kv_elems = pl.kv_elems;
+  fl.D = D;
+  fl.scale = pl.scale;
+  fl.atomic_layout = pl.atomic;
+  fl.nblk = pl.tg.Sw / 64;
+  fl.qshift = pl.tg.qshift;
+  fl.Sq = pl.Sq;
+  e = dash::launch_dq_finalize(fl, strm);
   if (e != hipSuccess) return hip_fail(e, "finalize launch");
 
   if (op.sync_check) {
@@ -557,9 +715,62 @@ static int bwd_impl(const void* q, const void* k, const void* v, const void* o, 
     int h_err = 0;
     e = hipMemcpy(&h_err, err, sizeof(int), hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(e, "hipMemcpy(error word)");
-    if (h_err) return fail(DASH_ERR_TIMEOUT, "a workgroup timed out waiting on a dQ semaphore");
+    if (h_err) {
+      (void)take_sticky_error(pl.dev);  // reported here, not again by the next call
+      return fail(DASH_ERR_TIMEOUT, "a workgroup timed out waiting on a dQ semaphore; dQ, dK and dV were set to NaN");
+    }
   }
   return DASH_OK;
+}
+
+static int bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                    void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk, int D, float softmax_scale,
+                    const Mask& mask, int schedule, const dash_bwd_opts* opts, void* stream) {
+  const void* ptrs[] = {q, k, v, o, dO, lse, dq, dk, dv};
+  BwdPlan pl;
+  int st = bwd_plan(ptrs, B, Hq, Hkv, Sq, Sk, D, softmax_scale, mask, schedule, opts, &pl);
+  if (st) return st;
+  hipStream_t strm = (hipStream_t)stream;
+  if (pl.empty) {
+    // No query rows: dQ is empty and dK = dV = 0 (no key receives any gradient).
+    if (pl.kv_elems == 0) return DASH_OK;
+    st = zero_bf16(dk, pl.kv_elems, D, strm);
+    return st ? st : zero_bf16(dv, pl.kv_elems, D, strm);
+  }
+  st = take_sticky_error(pl.dev);
+  if (st) return st;
+  int *sticky_host = nullptr, *sticky_dev = nullptr;
+  st = sticky_word(pl.dev, &sticky_host, &sticky_dev);
+  if (st) return st;
+  DevSchedule ds;
+  st = device_schedule(pl, mask.kind, strm, &ds);
+  if (st) return st;
+
+  char* ws = nullptr;
+  const dash_bwd_opts& op = pl.op;
+  if (op.workspace) {
+    if (reinterpret_cast<uintptr_t>(op.workspace) % 256) return fail(DASH_ERR_WORKSPACE, "workspace not 256-byte aligned");
+    if (op.workspace_bytes < pl.L.total) return fail(DASH_ERR_WORKSPACE, "workspace too small");
+    ws = (char*)op.workspace;
+  } else {
+    std::lock_guard<std::mutex> lk(g_mu);
+    Workspace& w = g_ws[std::make_pair(pl.dev, stream)];
+    if (w.bytes < pl.L.total) {
+      // The previous buffer may still be in use by work queued on this stream.
+      if (w.ptr) {
+        hipError_t e = hipStreamSynchronize(strm);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+        (void)hipFree(w.ptr);
+        w.ptr = nullptr;
+        w.bytes = 0;
+      }
+      hipError_t e = hipMalloc(&w.ptr, pl.L.total);
+      if (e != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
+      w.bytes = pl.L.total;
+    }
+    ws = (char*)w.ptr;
+  }
+  return bwd_enqueue(pl, ptrs, mask, ws, ds, sticky_dev, strm);
 }
 
 int dash_attn_bwd_qk(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,

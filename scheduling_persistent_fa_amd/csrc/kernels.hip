@@ -404,6 +404,8 @@ struct BwdArgs {
   const int4* steps;
   const int* offsets;
   unsigned long long* stall;
+  int* xcc;          // optional: chiplet id per workgroup
+  unsigned delay_seed;
   long long spin_ticks;
   float scale;       // softmax scale
   float scale_log2;  // softmax scale * log2(e)
@@ -417,6 +419,27 @@ struct BwdArgs {
 // Semaphore words per 64-row dQ block: one per wave that holds dQ tiles.
 constexpr int kSemPerBlock = 8;
 
+// Chiplet (XCC) of the executing wave: bits 3:0 of hardware register 20
+// (XCC_ID) on gfx950.
+__device__ __forceinline__ int xcc_id() { return __builtin_amdgcn_s_getreg((3 << 11) | 20) & 15; }
+
+// Delay injection (the testing instantiation only): 0..63 sleeps of 64
+// clocks, from a hash of (seed, workgroup, step, sub-step, wave, site) --
+// MurmurHash3's 32-bit finaliser (Appleby) -- so every run of a seed
+// perturbs the timing the same way and different seeds differently.  All
+// inputs are wave-uniform, so the loop is a scalar loop.
+__device__ __forceinline__ void debug_delay(unsigned seed, int wg, int i, int sub, int w, int site) {
+  unsigned h = seed ^ ((unsigned)wg * 0x9E3779B1u) ^ ((unsigned)i * 0x85EBCA77u) ^
+               ((unsigned)(sub * 64 + w * 4 + site) * 0xC2B2AE3Du);
+  h ^= h >> 16;
+  h *= 0x85EBCA6Bu;
+  h ^= h >> 13;
+  h *= 0xC2B2AE35u;
+  h ^= h >> 16;
+  const int n = (int)__builtin_amdgcn_readfirstlane(h & 63u);
+  for (int k = 0; k < n; ++k) __builtin_amdgcn_s_sleep(1);
+}
+
 template <int T>
 constexpr int bwd_threads() {
   return 64 * 2 * (T / 32);
@@ -424,7 +447,9 @@ constexpr int bwd_threads() {
 
 // LEFT: the window has a left edge (a band other than causal / full): each
 // element then needs a second comparison, which the other masks skip.
-template <int D, int T, bool ATOMIC, bool LEFT>
+// DELAY: seeded sleeps before each semaphore wait and release (a separate
+// instantiation for testing the ordering protocol under perturbed timing).
+template <int D, int T, bool ATOMIC, bool LEFT, bool DELAY>
 __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
   constexpr int NP = T / 32;          // wave pairs; pair p owns key/value rows 32p .. 32p+31
   constexpr int NW = 2 * NP;          // waves
@@ -477,6 +502,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
   unsigned long long stall = 0;
   const unsigned long long t_start = __builtin_amdgcn_s_memtime();
   if (threadIdx.x == 0) *s_flag = 0;
+  if (a.xcc && threadIdx.x == 0) a.xcc[wg] = xcc_id();
 
   // Per-lane LDS byte offsets.
   const int tr_row = 8 * h2 + ((lane & 15) >> 2), tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -641,6 +667,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
       if constexpr (!ATOMIC) {
         if (release_now) {
           wait_vmem_all();
+          if constexpr (DELAY) debug_delay(a.delay_seed, wg, i, 0, w, 0);
           if (lane == 0) __hip_atomic_store(p_sem, p_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           // Nothing is pending any more: the finish below writes to the dummy tiles.
           p_ws = a.dummy;
@@ -803,6 +830,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
         // Release the block finished after the S/dP phase as soon as its writes
         // have had the dK/dV contraction to complete (successors wait on it).
         wait_vmem_all();
+        if constexpr (DELAY) debug_delay(a.delay_seed, wg, i, sub, w, 1);
         if (r_sem != nullptr && lane == 0) __hip_atomic_store(r_sem, r_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         r_sem = nullptr;
       }
@@ -861,6 +889,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
       if constexpr (!ATOMIC) {
         // Wait for this block's predecessor, then start reading its partial.  (The
         // early value is consumed on every path, so it is never left pending.)
+        if constexpr (DELAY) debug_delay(a.delay_seed, wg, i, sub, w, 2);
         const bool ready = __builtin_amdgcn_readfirstlane(sem_seen) == ord;
         bool give_up = false;
         if (has_tiles && ord > 0 && !ready) {
@@ -937,6 +966,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
         }
       }
       wait_vmem_all();
+      if constexpr (DELAY) debug_delay(a.delay_seed, wg, end, 0, w, 3);
       if (lane == 0) __hip_atomic_store(p_sem, p_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -952,11 +982,29 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
 // atomic layout: tile as [register][lane].  Workspace blocks hold virtual
 // rows (query row + qshift, nblk blocks per head); rows outside 0 .. Sq-1
 // are not written.
+//
+// If the persistent kernel gave up on a semaphore wait (*err != 0), the
+// workspace is incomplete: dQ, dK and dV are all written with NaN instead,
+// and the host-visible word `sticky` (if any) is set, so that the failure
+// shows in the outputs and in the next call's status rather than as
+// plausible wrong gradients.
 template <int D, bool X4>
 __global__ __launch_bounds__(256) void dq_finalize_kernel(const float* __restrict__ ws, __bf16* __restrict__ dq,
                                                           long long n_groups, float scale, int nblk, int qshift,
-                                                          int Sq) {
+                                                          int Sq, const int* __restrict__ err, int* sticky,
+                                                          __bf16* __restrict__ dk, __bf16* __restrict__ dv,
+                                                          long long kv_elems) {
   const long long f = (long long)blockIdx.x * 256 + threadIdx.x;
+  const bool failed = *err != 0;
+  if (failed) {
+    if (f == 0 && sticky) __hip_atomic_store(sticky, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const __bf16 nan = __builtin_bit_cast(__bf16, (unsigned short)0x7FC0);
+    const long long stride = (long long)gridDim.x * 256;
+    for (long long i = f; i < kv_elems; i += stride) {
+      dk[i] = nan;
+      dv[i] = nan;
+    }
+  }
   if (f >= n_groups) return;
   constexpr int GROUPS_PER_BLOCK = 64 * D / 4;
   const long long blk = f / GROUPS_PER_BLOCK;  // (head, 64-row block)
@@ -977,7 +1025,9 @@ __global__ __launch_bounds__(256) void dq_finalize_kernel(const float* __restric
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e)
-    if (row0 + e >= 0 && row0 + e < Sq) out[(size_t)(row0 + e) * D + col] = (__bf16)(v[e] * scale);
+    if (row0 + e >= 0 && row0 + e < Sq)
+      out[(size_t)(row0 + e) * D + col] = failed ? __builtin_bit_cast(__bf16, (unsigned short)0x7FC0)
+                                                 : (__bf16)(v[e] * scale);
 }
 
 }  // namespace
@@ -1040,6 +1090,8 @@ hipError_t launch_bwd(const BwdLaunch& L, hipStream_t st) {
   a.steps = (const int4*)L.steps;
   a.offsets = L.offsets;
   a.stall = L.stall;
+  a.xcc = L.xcc;
+  a.delay_seed = L.delay_seed;
   a.spin_ticks = L.spin_ticks;
   a.scale = L.scale;
   a.scale_log2 = L.scale * kLog2e;
@@ -1053,17 +1105,20 @@ hipError_t launch_bwd(const BwdLaunch& L, hipStream_t st) {
   a.diag_off = L.diag_off;
   dim3 grid(L.P);
   const bool left = a.wl < kUnbounded;
-#define DASH_BWD_CASE(D_, T_)                                                                        \
-  if (L.D == D_ && L.T == T_) {                                                                      \
-    const dim3 block(bwd_threads<T_>());                                                             \
-    if (L.atomic) {                                                                                  \
-      if (left) hipLaunchKernelGGL((bwd_kernel<D_, T_, true, true>), grid, block, 0, st, a);         \
-      else hipLaunchKernelGGL((bwd_kernel<D_, T_, true, false>), grid, block, 0, st, a);             \
-    } else {                                                                                         \
-      if (left) hipLaunchKernelGGL((bwd_kernel<D_, T_, false, true>), grid, block, 0, st, a);        \
-      else hipLaunchKernelGGL((bwd_kernel<D_, T_, false, false>), grid, block, 0, st, a);            \
-    }                                                                                                \
-    return hipGetLastError();                                                                        \
+#define DASH_BWD_CASE(D_, T_)                                                                          \
+  if (L.D == D_ && L.T == T_) {                                                                        \
+    const dim3 block(bwd_threads<T_>());                                                               \
+    if (L.atomic) {                                                                                    \
+      if (left) hipLaunchKernelGGL((bwd_kernel<D_, T_, true, true, false>), grid, block, 0, st, a);    \
+      else hipLaunchKernelGGL((bwd_kernel<D_, T_, true, false, false>), grid, block, 0, st, a);        \
+    } else if (L.delay_seed) {                                                                         \
+      if (left) hipLaunchKernelGGL((bwd_kernel<D_, T_, false, true, true>), grid, block, 0, st, a);    \
+      else hipLaunchKernelGGL((bwd_kernel<D_, T_, false, false, true>), grid, block, 0, st, a);        \
+    } else {                                                                                           \
+      if (left) hipLaunchKernelGGL((bwd_kernel<D_, T_, false, true, false>), grid, block, 0, st, a);   \
+      else hipLaunchKernelGGL((bwd_kernel<D_, T_, false, false, false>), grid, block, 0, st, a);       \
+    }                                                                                                  \
+    return hipGetLastError();                                                                          \
   }
   DASH_BWD_CASE(128, 128)
   DASH_BWD_CASE(64, 128)
@@ -1078,41 +1133,44 @@ namespace {
 template <int D, int T, bool ATOMIC>
 hipError_t min_occupancy(int* per_cu) {
   const int nt = bwd_threads<T>();
-  int v[2] = {0, 0};
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&v[0], bwd_kernel<D, T, ATOMIC, false>, nt, 0);
-  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&v[1], bwd_kernel<D, T, ATOMIC, true>, nt, 0);
-  *per_cu = std::min(v[0], v[1]);
+  int v[4] = {0, 0, 1 << 30, 1 << 30};
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&v[0], bwd_kernel<D, T, ATOMIC, false, false>, nt, 0);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&v[1], bwd_kernel<D, T, ATOMIC, true, false>, nt, 0);
+  if constexpr (!ATOMIC) {
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&v[2], bwd_kernel<D, T, false, false, true>, nt, 0);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&v[3], bwd_kernel<D, T, false, true, true>, nt, 0);
+  }
+  *per_cu = std::min(std::min(v[0], v[1]), std::min(v[2], v[3]));
   return e;
 }
 }  // namespace
 
-hipError_t bwd_kernel_fits(int D, int T, bool atomic, int num_cu, int P, bool* fits) {
-  int per_cu = 0;
+hipError_t bwd_kernel_per_cu(int D, int T, bool atomic, int* per_cu) {
   hipError_t e = hipErrorInvalidValue;
 #define DASH_OCC_CASE(D_, T_) \
-  if (D == D_ && T == T_) e = atomic ? min_occupancy<D_, T_, true>(&per_cu) : min_occupancy<D_, T_, false>(&per_cu);
+  if (D == D_ && T == T_) e = atomic ? min_occupancy<D_, T_, true>(per_cu) : min_occupancy<D_, T_, false>(per_cu);
   DASH_OCC_CASE(128, 128)
   DASH_OCC_CASE(64, 128)
   DASH_OCC_CASE(128, 64)
   DASH_OCC_CASE(64, 64)
 #undef DASH_OCC_CASE
-  if (e != hipSuccess) return e;
-  *fits = (long long)per_cu * num_cu >= P;
-  return hipSuccess;
+  return e;
 }
 
-hipError_t launch_dq_finalize(const float* ws, void* dq, long long ws_elems, int D, float scale, bool atomic_layout,
-                              int nblk, int qshift, int Sq, hipStream_t st) {
-  const long long n_f4 = ws_elems / 4;
-  const unsigned blocks = (unsigned)((n_f4 + 255) / 256);
-#define DASH_FIN(D_, X4_)                                                                                    \
-  hipLaunchKernelGGL((dq_finalize_kernel<D_, X4_>), dim3(blocks), dim3(256), 0, st, ws, (__bf16*)dq, n_f4, scale, \
-                     nblk, qshift, Sq)
-  if (D == 128) {
-    if (atomic_layout) DASH_FIN(128, false);
+hipError_t launch_dq_finalize(const FinalizeLaunch& F, hipStream_t st) {
+  const long long n_f4 = F.ws_elems / 4;
+  const unsigned blocks = (unsigned)std::max<long long>(1, (n_f4 + 255) / 256);
+  auto dq = (__bf16*)F.dq;
+  auto dk = (__bf16*)F.dk;
+  auto dv = (__bf16*)F.dv;
+#define DASH_FIN(D_, X4_)                                                                                          \
+  hipLaunchKernelGGL((dq_finalize_kernel<D_, X4_>), dim3(blocks), dim3(256), 0, st, F.ws, dq, n_f4, F.scale, F.nblk, \
+                     F.qshift, F.Sq, F.err, F.sticky, dk, dv, F.kv_elems)
+  if (F.D == 128) {
+    if (F.atomic_layout) DASH_FIN(128, false);
     else DASH_FIN(128, true);
   } else {
-    if (atomic_layout) DASH_FIN(64, false);
+    if (F.atomic_layout) DASH_FIN(64, false);
     else DASH_FIN(64, true);
   }
 #undef DASH_FIN

@@ -23,6 +23,8 @@ struct BwdLaunch {
   const int32_t* steps;    // 4 ints per step
   const int32_t* offsets;  // P + 1
   unsigned long long* stall;
+  int* xcc;                // optional: per workgroup, the chiplet (XCC) it ran on
+  uint32_t delay_seed;     // non-zero: seeded sleeps around the dQ waits and releases (testing only)
   long long spin_ticks;    // wait budget in 100 MHz real-time ticks
   float scale;
   int Sq, Sk, D, T, g, P;
@@ -38,8 +40,24 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, floa
 hipError_t launch_delta(const void* o, const void* dO, float* delta, long long rows, int D, int* zero_i32,
                         long long n_zero_i32, float* zero_f32, long long n_zero_f32, hipStream_t st);
 hipError_t launch_bwd(const BwdLaunch& L, hipStream_t st);
-hipError_t bwd_kernel_fits(int D, int T, bool atomic, int num_cu, int P, bool* fits);
-hipError_t launch_dq_finalize(const float* ws, void* dq, long long ws_elems, int D, float scale, bool atomic_layout,
-                              int nblk, int qshift, int Sq, hipStream_t st);
+// Co-resident workgroups per compute unit of the persistent kernel family
+// (the minimum over its variants).
+hipError_t bwd_kernel_per_cu(int D, int T, bool atomic, int* per_cu);
+
+struct FinalizeLaunch {
+  const float* ws;     // fp32 dQ accumulator, fragment order
+  void* dq;
+  void* dk;            // written with NaN (with dv and dq) when *err is set
+  void* dv;
+  const int* err;      // error word of the persistent kernel
+  int* sticky;         // optional host-visible word set to 1 when *err is set
+  long long ws_elems;  // workspace floats
+  long long kv_elems;  // elements of dk (and of dv)
+  int D;
+  float scale;
+  bool atomic_layout;
+  int nblk, qshift, Sq;
+};
+hipError_t launch_dq_finalize(const FinalizeLaunch& F, hipStream_t st);
 
 }  // namespace dash

@@ -373,7 +373,27 @@ std::string build_schedule(int mask, int kind, int Nq, int Nk, int g, int groups
   return {};
 }
 
-bool simulate_schedule(const Schedule& s, double c, double r, double* makespan, double* total_wait) {
+namespace {
+// SplitMix64's output function (Steele, Lea and Flood, "Fast splittable
+// pseudorandom number generators", OOPSLA 2014), used as a counter-based
+// generator: the draw for (seed, workgroup w, list position i) mixes
+// seed ^ (w << 32 | i) advanced by one golden-ratio increment.
+uint64_t splitmix64(uint64_t x) {
+  uint64_t z = x + 0x9e3779b97f4a7c15ULL;
+  z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ULL;
+  z = (z ^ (z >> 27)) * 0x94d049bb133111ebULL;
+  return z ^ (z >> 31);
+}
+}  // namespace
+
+double jitter_factor(uint64_t seed, int w, int i) {
+  if (seed == 0) return 1.0;
+  const uint64_t x = seed ^ ((static_cast<uint64_t>(static_cast<uint32_t>(w)) << 32) | static_cast<uint32_t>(i));
+  return 0.5 + static_cast<double>(splitmix64(x) >> 11) * 0x1.0p-53;
+}
+
+bool simulate_schedule(const Schedule& s, double c, double r, uint64_t jitter_seed, double* makespan,
+                       double* total_wait) {
   const size_t tiles = static_cast<size_t>(s.g) * s.groups * s.Nq;
   std::vector<int32_t> count(tiles, 0);
   std::vector<double> done_at(tiles, 0.0);
@@ -390,7 +410,7 @@ bool simulate_schedule(const Schedule& s, double c, double r, double* makespan, 
         const size_t key = static_cast<size_t>(st.head) * s.Nq + st.qi;
         const int32_t ord = st.ordflags & kOrdMask;
         if (count[key] != ord) break;
-        const double ready = t[w] + c;
+        const double ready = t[w] + c * jitter_factor(jitter_seed, w, idx[w]);
         const double start = std::max(ready, done_at[key]);
         wait += start - ready;
         t[w] = start + r;
@@ -469,7 +489,7 @@ std::string validate_schedule(const Schedule& s) {
     ordseen[k] = 1;
   }
   double mk, wt;
-  if (!simulate_schedule(s, 1.0, 1.0, &mk, &wt)) return "deadlock";
+  if (!simulate_schedule(s, 1.0, 1.0, 0, &mk, &wt)) return "deadlock";
   return {};
 }
 

@@ -62,7 +62,11 @@ std::string choose_schedule(int mask, int Nq, int Nk, int D, int g, int P, int* 
                             int band_l = -1, int band_r = -1);
 // Whether the band shift covers a band (see build_schedule).
 bool band_shift_applies(int Nq, int Nk, int band_l, int band_r);
-// Unit-cost DAG simulation; returns false on deadlock.
-bool simulate_schedule(const Schedule& s, double c, double r, double* makespan, double* total_wait);
+// Unit-cost DAG simulation; returns false on deadlock.  With jitter_seed != 0
+// step i of workgroup w costs c * jitter_factor(jitter_seed, w, i) of compute
+// (uniform in [0.5, 1.5)); 0 keeps every step at c.
+bool simulate_schedule(const Schedule& s, double c, double r, uint64_t jitter_seed, double* makespan,
+                       double* total_wait);
+double jitter_factor(uint64_t seed, int w, int i);
 
 }  // namespace dash

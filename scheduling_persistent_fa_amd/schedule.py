@@ -70,9 +70,11 @@ class Schedule:
     def validate(self) -> None:
         _lib.check(_lib.lib().dash_schedule_validate(self._h))
 
-    def simulate(self, c: float, r: float):
+    def simulate(self, c: float, r: float, jitter_seed: int = 0):
+        """(makespan, total wait) of the unit-cost DAG model; a non-zero
+        ``jitter_seed`` scales each step's compute cost into [0.5, 1.5) c."""
         mk, wt = ctypes.c_double(), ctypes.c_double()
-        _lib.check(_lib.lib().dash_schedule_simulate(self._h, c, r, ctypes.byref(mk), ctypes.byref(wt)))
+        _lib.check(_lib.lib().dash_schedule_simulate(self._h, c, r, jitter_seed, ctypes.byref(mk), ctypes.byref(wt)))
         return mk.value, wt.value
 
     def lists(self):

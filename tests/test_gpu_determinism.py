@@ -1,7 +1,8 @@
 """GPU determinism: deterministic schedules give bit-identical dQ/dK/dV over
-50 runs, independent of the workgroup count; serial and descending-Q share
-their dQ accumulation order and so their dQ bits; the atomic ceiling agrees
-with them within tolerance."""
+50 runs on every workload, and under seeded delays injected around the dQ
+semaphore waits; independent of the workgroup count where the order does not
+depend on it; serial and descending-Q share their dQ accumulation order and
+so their dQ bits; the atomic ceiling agrees with them within tolerance."""
 import hashlib
 
 import numpy as np
@@ -26,36 +27,88 @@ def _digest(*ts):
     return h.hexdigest()
 
 
-CASES = [
-    ("causal_b4_h16_s2048_d128", 4, 16, 16, 2048, 128, True, 1.0, [SERIAL, DESC_Q, SYM_SHIFT]),
-    ("full_b2_h24_s4096_d64", 2, 24, 24, 4096, 64, False, 1.0, [SERIAL, DESC_Q, SHIFT]),
-    ("gqa_causal_b1_hq32_hkv8_s8192_d128", 1, 32, 8, 8192, 128, True, 0.5, [DESC_Q, SYM_SHIFT]),
+CASES = [  # name, B, Hq, Hkv, S, D, causal, std, tile, workgroups, schedules
+    ("full_b1_h1_s256_d64_4wg", 1, 1, 1, 256, 64, False, 1.0, 64, 4, [SERIAL, DESC_Q, SHIFT]),
+    ("causal_b4_h16_s2048_d128", 4, 16, 16, 2048, 128, True, 1.0, 0, 0, [SERIAL, DESC_Q, SYM_SHIFT]),
+    ("full_b2_h24_s4096_d64", 2, 24, 24, 4096, 64, False, 1.0, 0, 0, [SERIAL, DESC_Q, SHIFT]),
+    ("full_b1_h16_s16384_d128", 1, 16, 16, 16384, 128, False, 1.0, 0, 0, [SERIAL, DESC_Q, SHIFT]),
+    ("causal_b1_h16_s16384_d128", 1, 16, 16, 16384, 128, True, 1.0, 0, 0, [SERIAL, DESC_Q, SYM_SHIFT]),
+    ("gqa_causal_b1_hq32_hkv8_s8192_d128", 1, 32, 8, 8192, 128, True, 0.5, 0, 0, [SERIAL, DESC_Q, SYM_SHIFT]),
 ]
 
 
+def _same_bits(a, b) -> bool:
+    return all(torch.equal(x.view(torch.int16), y.view(torch.int16)) for x, y in zip(a, b))
+
+
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_fifty_runs_bit_identical(case):
-    name, B, Hq, Hkv, S, D, causal, std, scheds = case
+    # Every deterministic schedule of every workload, in the benchmark's launch
+    # configuration: 50 runs, each compared on the device with the first.
+    from scheduling_persistent_fa_amd.attention import check_async_error
+    name, B, Hq, Hkv, S, D, causal, std, tile, wgs, scheds = case
     pb = DeviceProblem(B, Hq, Hkv, S, D, causal, std=std)
     o, lse = attn_fwd(pb.q, pb.k, pb.v, causal)
     outs = {}
     for sched in scheds:
         say(f"[determinism] {name} {_lib.SCHEDULE_NAMES[sched]} x{RUNS}")
-        dq, dk, dv = attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, causal, sched, opts=make_opts(sync_check=True))
-        ref = _digest(dq, dk, dv)
-        first = (dq.clone(), dk.clone(), dv.clone())
-        for _ in range(RUNS - 1):
-            attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, causal, sched, dq=dq, dk=dk, dv=dv)
-            assert _digest(dq, dk, dv) == ref
+        op = make_opts(num_workgroups=wgs, tile=tile)
+        first = attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, causal, sched, opts=op)
+        first = tuple(t.clone() for t in first)
+        dq, dk, dv = (torch.empty_like(t) for t in first)
+        for run in range(1, RUNS):
+            dq.fill_(float("nan"))
+            attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, causal, sched, dq=dq, dk=dk, dv=dv, opts=op)
+            assert _same_bits((dq, dk, dv), first), (name, _lib.SCHEDULE_NAMES[sched], run)
+        check_async_error()
+        for t in first:
+            assert torch.isfinite(t.float()).all()
         outs[sched] = first
     if SERIAL in outs and DESC_Q in outs:
         # same ordinals (ascending key/value order) -> same dQ bits
         assert torch.equal(outs[SERIAL][0].view(torch.int16), outs[DESC_Q][0].view(torch.int16))
     # the non-deterministic ceiling agrees with a deterministic schedule within tolerance
-    dqa, dka, dva = attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, causal, ATOMIC)
+    got = attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, causal, ATOMIC, opts=make_opts(num_workgroups=wgs, tile=tile))
     base = outs[scheds[0]]
-    for got, ref in zip((dqa, dka, dva), base):
-        assert rel_err(to_f64(got), to_f64(ref)) <= TOL
+    for g_, ref in zip(got, base):
+        assert rel_err(to_f64(g_), to_f64(ref)) <= TOL
+
+
+DELAY_CASES = [  # name, B, H, S, D, causal, window, schedules
+    ("causal_b4_h16_s2048_d128", 4, 16, 2048, 128, True, None, [SERIAL, DESC_Q, SYM_SHIFT]),
+    ("full_b2_h8_s2048_d128", 2, 8, 2048, 128, False, None, [SERIAL, DESC_Q, SHIFT]),
+    ("sliding_b2_h4_s2048_w512_d128", 2, 4, 2048, 128, True, (511, 0), [SERIAL, DESC_Q, SHIFT]),
+]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("case", DELAY_CASES, ids=[c[0] for c in DELAY_CASES])
+def test_seeded_delays_do_not_change_the_bits(case):
+    # Delay injection: a build of the persistent kernel that sleeps a seeded
+    # 0..63 x 64 clocks before every semaphore wait and release.  The order of
+    # every dQ accumulation is fixed by the schedule, so any timing must give
+    # the undelayed bits ([summary] §1: reproducibility from a fixed order).
+    name, B, H, S, D, causal, window, scheds = case
+    pb = DeviceProblem(B, H, H, S, D, causal, seed=3)
+    o, lse = attn_fwd(pb.q, pb.k, pb.v, causal, window=window)
+    for sched in scheds:
+        ref = attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, causal, sched, opts=make_opts(sync_check=True),
+                       window=window)
+        ref = tuple(t.clone() for t in ref)
+        for seed in (1, 2, 0xBEEF, 0x9E3779B9):
+            say(f"[delay] {name} {_lib.SCHEDULE_NAMES[sched]} seed {seed:#x}")
+            got = attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, causal, sched,
+                           opts=make_opts(delay_seed=seed, sync_check=True), window=window)
+            assert _same_bits(got, ref), (name, _lib.SCHEDULE_NAMES[sched], seed)
+
+
+def test_delay_injection_needs_a_deterministic_schedule():
+    pb = DeviceProblem(1, 1, 1, 512, 64, False)
+    o, lse = attn_fwd(pb.q, pb.k, pb.v, False)
+    with pytest.raises(_lib.DashError) as ei:
+        attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, False, ATOMIC, opts=make_opts(delay_seed=5))
+    assert ei.value.status == _lib.ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("sched,causal,wgs", [(SERIAL, True, [256, 128, 37]), (DESC_Q, False, [256, 100]),
@@ -79,7 +132,7 @@ def test_semaphores_count_every_contribution():
     B, Hq, S, D, T = 1, 2, 1024, 128, 128
     pb = DeviceProblem(B, Hq, Hq, S, D, True)
     o, lse = attn_fwd(pb.q, pb.k, pb.v, True)
-    ws = torch.zeros(workspace_bytes(B, Hq, Hq, S, D) // 4, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(workspace_bytes(B, Hq, Hq, S, D, 1) // 4, dtype=torch.int32, device="cuda")
     assert ws.data_ptr() % 256 == 0
     attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, True, SYM_SHIFT, opts=make_opts(workspace=ws, sync_check=True))
     torch.cuda.synchronize()

@@ -1,8 +1,8 @@
 """GPU parity: the HIP path (through the C ABI) against the float64 oracle.
 
-Small shapes span several tiles and are compared element by element; the
-workload shapes at full size are compared on sampled rows, in the launch
-configuration the benchmark times (one workgroup per compute unit).
+Small shapes span several tiles and are compared element by element; so
+are the workload shapes at full size, in the launch configuration the
+benchmark times (one workgroup per compute unit).
 Tolerance: max|err| / max|ref| <= 2e-2 for dQ, dK, dV and O; LSE and Delta
 within 2e-2 * max(1, max|ref|).
 """
@@ -64,86 +64,54 @@ def test_small_shapes_match_oracle(case):
             assert e <= TOL, (name, _lib.SCHEDULE_NAMES[sched], nm, e)
 
 
-FULL_SIZE = [
-    ("causal_b4_h16_s2048_d128", 4, 16, 16, 2048, 128, True, 1.0, [SERIAL, DESC_Q, SYM_SHIFT, ATOMIC]),
-    ("full_b2_h24_s4096_d64", 2, 24, 24, 4096, 64, False, 1.0, [SERIAL, DESC_Q, SHIFT, ATOMIC]),
-    ("full_b1_h16_s16384_d128", 1, 16, 16, 16384, 128, False, 1.0, [SERIAL, DESC_Q, SHIFT, ATOMIC]),
-    ("causal_b1_h16_s16384_d128", 1, 16, 16, 16384, 128, True, 1.0, [SERIAL, DESC_Q, SYM_SHIFT, ATOMIC]),
-    ("gqa_causal_b1_hq32_hkv8_s8192_d128", 1, 32, 8, 8192, 128, True, 0.5, [SERIAL, DESC_Q, SYM_SHIFT, ATOMIC]),
+FULL_SIZE = [  # name, B, Hq, Hkv, Sq, Sk, D, causal, window, std, schedules
+    ("causal_b4_h16_s2048_d128", 4, 16, 16, 2048, 2048, 128, True, None, 1.0, [SERIAL, DESC_Q, SYM_SHIFT, ATOMIC]),
+    ("full_b2_h24_s4096_d64", 2, 24, 24, 4096, 4096, 64, False, None, 1.0, [SERIAL, DESC_Q, SHIFT, ATOMIC]),
+    ("full_b1_h16_s16384_d128", 1, 16, 16, 16384, 16384, 128, False, None, 1.0, [SERIAL, DESC_Q, SHIFT, ATOMIC]),
+    ("causal_b1_h16_s16384_d128", 1, 16, 16, 16384, 16384, 128, True, None, 1.0,
+     [SERIAL, DESC_Q, SYM_SHIFT, ATOMIC]),
+    ("gqa_causal_b1_hq32_hkv8_s8192_d128", 1, 32, 8, 8192, 8192, 128, True, None, 0.5,
+     [SERIAL, DESC_Q, SYM_SHIFT, ATOMIC]),
+    # the rectangular and windowed workloads of the benchmark
+    ("cross_b1_h16_q4096_k16384_d128", 1, 16, 16, 4096, 16384, 128, False, None, 1.0, [DESC_Q, SHIFT, ATOMIC]),
+    ("causal_b1_h16_q4096_k16384_d128", 1, 16, 16, 4096, 16384, 128, True, None, 1.0, [DESC_Q, SYM_SHIFT, ATOMIC]),
+    ("sliding_b1_h16_s16384_w4096_d128", 1, 16, 16, 16384, 16384, 128, True, (4095, 0), 1.0,
+     [SERIAL, DESC_Q, SHIFT, ATOMIC]),
 ]
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("case", FULL_SIZE, ids=[c[0] for c in FULL_SIZE])
-def test_workload_shapes_on_sampled_rows(case):
-    name, B, Hq, Hkv, S, D, causal, std, scheds = case
+def test_workload_shapes_every_element(case):
+    # Full size, in the benchmark's launch configuration (one workgroup per
+    # compute unit), every element of dQ, dK and dV of every schedule against
+    # the float64 oracle, and every output finite.
+    from tests._oracle_full import full_reference
+    name, B, Hq, Hkv, Sq, Sk, D, causal, window, std, scheds = case
     say(f"[parity-full] {name}")
-    pb = DeviceProblem(B, Hq, Hkv, S, D, causal, std=std)
-    o, lse = attn_fwd(pb.q, pb.k, pb.v, causal)
-    torch.cuda.synchronize()
-    q64, k64, v64, do64 = pb.f64("q"), pb.f64("k"), pb.f64("v"), pb.f64("do")
-    g = Hq // Hkv
-    b, hk = B - 1, Hkv - 1                      # last batch, last kv head
-    heads = list(range(hk * g, hk * g + g))
-    rows = sorted({0, 1, 127, 128, S // 2 + 5, S - 129, S - 1})
-    stats = {hq: A.head_stats(q64, k64, v64, do64, b, hq, pb.scale, causal) for hq in heads}
-    say("  oracle stats done")
-    ref_dq = A.dq_rows(q64, k64, v64, do64, b, heads[-1], rows, pb.scale, causal)
-    ref_dk, ref_dv = A.dkdv_rows(q64, k64, v64, do64, b, hk, rows, pb.scale, causal, stats=stats)
-    lse_ref = stats[heads[-1]][0]
-    got_lse = to_f64(lse[b, heads[-1]])
-    assert np.abs(got_lse - lse_ref).max() <= TOL * max(1.0, np.abs(lse_ref).max())
-    for sched in scheds:
-        say(f"  schedule {_lib.SCHEDULE_NAMES[sched]}")
-        dq, dk, dv = attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, causal, sched, opts=make_opts(sync_check=True))
-        torch.cuda.synchronize()
-        e_dq = rel_err(to_f64(dq[b, heads[-1], rows]), ref_dq)
-        e_dk = rel_err(to_f64(dk[b, hk, rows]), ref_dk)
-        e_dv = rel_err(to_f64(dv[b, hk, rows]), ref_dv)
-        say(f"    rel err dq {e_dq:.2e} dk {e_dk:.2e} dv {e_dv:.2e}")
-        assert max(e_dq, e_dk, e_dv) <= TOL
-        # every output finite
-        for t in (dq, dk, dv):
-            assert torch.isfinite(t.float()).all()
-
-
-# The rectangular and windowed benchmark workloads at full size (bench.py's
-# launch configuration), on sampled query rows and key rows.
-FULL_SIZE_EXT = [  # name, B, Hq, Hkv, Sq, Sk, D, causal, window, schedules
-    ("cross_b1_h16_q4096_k16384_d128", 1, 16, 16, 4096, 16384, 128, False, None, [DESC_Q, SHIFT, ATOMIC]),
-    ("causal_b1_h16_q4096_k16384_d128", 1, 16, 16, 4096, 16384, 128, True, None, [DESC_Q, SYM_SHIFT, ATOMIC]),
-    ("sliding_b1_h16_s16384_w4096_d128", 1, 16, 16, 16384, 16384, 128, True, (4095, 0), [SERIAL, DESC_Q, SHIFT, ATOMIC]),
-]
-
-
-@pytest.mark.parametrize("case", FULL_SIZE_EXT, ids=[c[0] for c in FULL_SIZE_EXT])
-def test_extended_workloads_on_sampled_rows(case):
-    name, B, Hq, Hkv, Sq, Sk, D, causal, window, scheds = case
-    say(f"[parity-full] {name}")
-    pb = DeviceProblem(B, Hq, Hkv, Sq, D, causal, Sk=Sk)
+    pb = DeviceProblem(B, Hq, Hkv, Sq, D, causal, std=std, Sk=Sk)
     o, lse = attn_fwd(pb.q, pb.k, pb.v, causal, window=window)
     torch.cuda.synchronize()
+    # LSE of the last head against the oracle's row statistics
     q64, k64, v64, do64 = pb.f64("q"), pb.f64("k"), pb.f64("v"), pb.f64("do")
-    b, hk, hq = 0, Hkv - 1, Hq - 1
-    qrows = sorted({0, 1, 127, 128, Sq // 2 + 5, Sq - 129, Sq - 1})
-    krows = sorted({0, 1, 127, 128, Sk // 3 + 7, Sk // 2 + 5, Sk - 129, Sk - 1})
-    stats = {hq: A.head_stats(q64, k64, v64, do64, b, hq, pb.scale, causal, window=window)}
-    say("  oracle stats done")
-    ref_dq = A.dq_rows(q64, k64, v64, do64, b, hq, qrows, pb.scale, causal, window=window)
-    ref_dk, ref_dv = A.dkdv_rows(q64, k64, v64, do64, b, hk, krows, pb.scale, causal, stats=stats, window=window)
-    got_lse = to_f64(lse[b, hq])
-    assert np.abs(got_lse - stats[hq][0]).max() <= TOL * max(1.0, np.abs(stats[hq][0]).max())
-    for sched in scheds:
-        say(f"  schedule {_lib.SCHEDULE_NAMES[sched]}")
+    lse_ref = A.head_stats(q64, k64, v64, do64, B - 1, Hq - 1, pb.scale, causal, window=window)[0]
+    assert np.abs(to_f64(lse[B - 1, Hq - 1]) - lse_ref).max() <= TOL * max(1.0, np.abs(lse_ref).max())
+    del q64, k64, v64, do64
+    outs = {}
+    for sched in scheds:  # GPU runs first; the oracle afterwards on the host
         dq, dk, dv = attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, causal, sched, opts=make_opts(sync_check=True),
                               window=window)
         torch.cuda.synchronize()
-        e_dq = rel_err(to_f64(dq[b, hq, qrows]), ref_dq)
-        e_dk = rel_err(to_f64(dk[b, hk, krows]), ref_dk)
-        e_dv = rel_err(to_f64(dv[b, hk, krows]), ref_dv)
-        say(f"    rel err dq {e_dq:.2e} dk {e_dk:.2e} dv {e_dv:.2e}")
-        assert max(e_dq, e_dk, e_dv) <= TOL
         for t in (dq, dk, dv):
-            assert torch.isfinite(t.float()).all()
+            assert torch.isfinite(t.float()).all(), (name, _lib.SCHEDULE_NAMES[sched])
+        outs[sched] = tuple(t.float().cpu().numpy() for t in (dq, dk, dv))
+        del dq, dk, dv
+    say("  GPU runs done; oracle over every head")
+    ref = full_reference(pb.inp, causal, window=window, label=name)
+    for sched, got in outs.items():
+        errs = [rel_err(g_, ref[nm]) for g_, nm in zip(got, ("dq", "dk", "dv"))]
+        say(f"  {_lib.SCHEDULE_NAMES[sched]}: rel err dq {errs[0]:.2e} dk {errs[1]:.2e} dv {errs[2]:.2e}")
+        assert max(errs) <= TOL, (name, _lib.SCHEDULE_NAMES[sched], errs)
 
 
 def test_unsupported_shapes_are_rejected_before_launch():
@@ -168,19 +136,85 @@ def test_unsupported_shapes_are_rejected_before_launch():
     assert ei.value.status == _lib.ERR_UNSUPPORTED
 
 
-def test_wait_budget_exhaustion_is_reported_and_recovers():
-    # A one-cycle wait budget makes the first waiting workgroup give up; every
-    # workgroup then leaves its loop and the call reports a timeout.
+def test_wait_budget_exhaustion_is_loud_and_recovers():
+    # A one-cycle wait budget makes the first waiting workgroup give up (forced
+    # from the host; every workgroup still exits).  The failure must show:
+    # with sync_check the call returns the timeout; without it the outputs are
+    # NaN and the next call (or dash_check_async_error) reports it.  A normal
+    # call afterwards is correct again.
+    from scheduling_persistent_fa_amd.attention import check_async_error
     pb = DeviceProblem(1, 2, 2, 2048, 128, False)
     o, lse = attn_fwd(pb.q, pb.k, pb.v, False)
+    dq, dk, dv = (torch.zeros_like(t) for t in (pb.q, pb.k, pb.v))
     with pytest.raises(_lib.DashError) as ei:
-        attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, False, SERIAL,
+        attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, False, SERIAL, dq=dq, dk=dk, dv=dv,
                  opts=make_opts(spin_timeout_cycles=1, sync_check=True))
     assert ei.value.status == _lib.ERR_TIMEOUT
+    for t in (dq, dk, dv):
+        assert torch.isnan(t.float()).all()
+    check_async_error()  # already reported by the call itself
+    # without sync_check: the call returns, the outputs are NaN, the next call fails
+    dq, dk, dv = attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, False, SERIAL, opts=make_opts(spin_timeout_cycles=1))
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        assert torch.isnan(t.float()).all()
+    with pytest.raises(_lib.DashError) as ei:
+        attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, False, SERIAL)
+    assert ei.value.status == _lib.ERR_TIMEOUT
+    # and through dash_check_async_error
+    attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, False, DESC_Q, opts=make_opts(spin_timeout_cycles=1))
+    with pytest.raises(_lib.DashError) as ei:
+        check_async_error()
+    assert ei.value.status == _lib.ERR_TIMEOUT
+    check_async_error()  # reported once
     ref = A.backward(pb.f64("q"), pb.f64("k"), pb.f64("v"), pb.f64("do"), pb.scale, False)
     dq, dk, dv = attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, False, SERIAL, opts=make_opts(sync_check=True))
     torch.cuda.synchronize()
     assert rel_err(to_f64(dq), ref["dq"]) <= TOL and rel_err(to_f64(dk), ref["dk"]) <= TOL
+    assert rel_err(to_f64(dv), ref["dv"]) <= TOL
+
+
+def test_concurrent_streams_use_separate_workspaces():
+    # Two backward calls in flight at once on two streams, each with the
+    # library-managed workspace and 16 workgroups (so both grids are resident
+    # together): each must give the bits of the same call run alone.
+    B, H, S, D = 1, 4, 2048, 128
+    pa = DeviceProblem(B, H, H, S, D, True, seed=1)
+    pbb = DeviceProblem(B, H, H, S, D, True, seed=2)
+    oa, la = attn_fwd(pa.q, pa.k, pa.v, True)
+    ob, lb = attn_fwd(pbb.q, pbb.k, pbb.v, True)
+    op = make_opts(num_workgroups=16)
+    ref_a = attn_bwd(pa.q, pa.k, pa.v, oa, pa.do, la, True, SERIAL, opts=op)
+    ref_b = attn_bwd(pbb.q, pbb.k, pbb.v, ob, pbb.do, lb, True, SERIAL, opts=op)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for rep in range(3):
+        say(f"[streams] rep {rep}")
+        got_a = attn_bwd(pa.q, pa.k, pa.v, oa, pa.do, la, True, SERIAL, opts=op, stream=s1)
+        got_b = attn_bwd(pbb.q, pbb.k, pbb.v, ob, pbb.do, lb, True, SERIAL, opts=op, stream=s2)
+        torch.cuda.synchronize()
+        for x, y in zip(got_a + got_b, ref_a + ref_b):
+            assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+def test_workgroups_record_their_chiplet():
+    # Each workgroup reads its chiplet (XCC) id from the hardware register.
+    # The gang placement assumes round-robin dispatch: workgroup w on chiplet
+    # w mod (number of chiplets).
+    from scheduling_persistent_fa_amd.attention import device_info
+    info = device_info()
+    P, nx = info["num_cu"], info["num_xcd"]
+    say(f"[xcc] {P} compute units, {nx} chiplets")
+    assert nx >= 1 and P % nx == 0
+    pb = DeviceProblem(1, 4, 4, 2048, 128, False)
+    o, lse = attn_fwd(pb.q, pb.k, pb.v, False)
+    xcc = torch.full((P,), -1, dtype=torch.int32, device="cuda")
+    attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, False, SHIFT, opts=make_opts(xcc=xcc, sync_check=True))
+    torch.cuda.synchronize()
+    ids = xcc.cpu().numpy()
+    assert ((ids >= 0) & (ids < nx)).all()
+    assert np.bincount(ids, minlength=nx).tolist() == [P // nx] * nx
+    assert (ids == np.arange(P) % nx).all(), ids[:32]
 
 
 @pytest.mark.parametrize("causal", [False, True])

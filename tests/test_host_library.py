@@ -83,6 +83,32 @@ def test_host_simulator_matches_oracle(mask, sched, N, g, groups, P, cap):
         assert lib_s.simulate(c, r) == pytest.approx(Sch.simulate(ora, c, r), rel=1e-12, abs=1e-9)
 
 
+@pytest.mark.parametrize("mask,sched,N,g,groups,P,cap", CASES[:8] + CASES[-4:])
+def test_jittered_simulation_matches_oracle(mask, sched, N, g, groups, P, cap):
+    # Same seeded step costs on both sides (SplitMix64 per (seed, workgroup,
+    # position)): same makespan and waiting time.  The lists are compared up
+    # to placement, so each side simulates its own lists.
+    lib_s = Schedule(mask, sched, N, g, groups, P, max_gang=cap, xcd_local=False)
+    ora = Sch.build(mask, sched, N, g, groups, P, max_gang=cap)
+    assert lib_s.lists() == _oracle_tuples(ora)  # contiguous placement on both sides
+    for seed in (1, 12345, 2**63 + 5):
+        assert lib_s.simulate(1.0, 0.5, seed) == pytest.approx(Sch.simulate(ora, 1.0, 0.5, seed), rel=1e-12, abs=1e-9)
+
+
+@pytest.mark.parametrize("mask,sched,N,g,groups", [(1, 0, 16, 1, 64), (1, 1, 16, 1, 64), (1, 3, 16, 1, 64),
+                                                   (0, 2, 32, 1, 48), (0, 2, 128, 1, 16), (1, 3, 128, 1, 16),
+                                                   (1, 3, 64, 4, 8), (1, 0, 64, 4, 8), (0, 1, 128, 1, 16)])
+def test_thousand_jittered_runs_never_deadlock(mask, sched, N, g, groups):
+    # The workload shapes on 256 workgroups: under 1000 different seeded
+    # timings every list still runs to completion (the order a schedule fixes
+    # is acyclic whatever the step costs).
+    s = Schedule(mask, sched, N, g, groups, 256)
+    base, _ = s.simulate(1.0, 1.0)
+    for seed in range(1, 1001):
+        mk, wait = s.simulate(1.0, 1.0, seed)  # raises on deadlock
+        assert mk > 0 and wait >= 0
+
+
 def test_full_size_schedules_validate():
     # the workloads' shapes: (mask, schedule, N, g, groups) with 256 workgroups
     for mask, sched, N, g, groups in [(1, 0, 16, 1, 64), (1, 1, 16, 1, 64), (1, 3, 16, 1, 64),
@@ -135,10 +161,10 @@ def test_bwd_argument_errors_need_no_gpu():
     assert L.dash_attn_bwd(*bad, 1, 1, 1, 128, 64, 0.0, 0, 0, None, None) == _lib.ERR_INVALID_ARG
     assert b"aligned" in L.dash_last_error()
     n = ctypes.c_size_t()
-    assert L.dash_attn_bwd_workspace_bytes(2, 24, 24, 4096, 64, ctypes.byref(n)) == 0
+    assert L.dash_attn_bwd_workspace_bytes(2, 24, 24, 4096, 64, 0, _lib.SHIFT, ctypes.byref(n)) == 0
     assert n.value >= 2 * 24 * 4096 * 64 * 4
     # ragged lengths: room for up to one extra tile of virtual query rows per head
-    assert L.dash_attn_bwd_workspace_bytes(1, 2, 1, 100, 64, ctypes.byref(n)) == 0
+    assert L.dash_attn_bwd_workspace_bytes(1, 2, 1, 100, 64, 1, _lib.AUTO, ctypes.byref(n)) == 0
     assert n.value >= 2 * (128 + 128) * 64 * 4
 
 
@@ -359,3 +385,22 @@ def test_gang_placement_is_a_bijection_with_chiplet_runs(sched, N, g, groups, P)
                 assert w % 8 == (m // 16) % 8
             else:
                 assert w == p * (P // gang) + k
+
+
+def test_schedule_generator_is_clean_under_asan_and_ubsan(tmp_path):
+    # The host scheduler built with g++ under AddressSanitizer and
+    # UndefinedBehaviorSanitizer (host code only), driven over every mask,
+    # schedule, grid up to 7 x 9, gang cap and band, plus the workload shapes.
+    import shutil
+    import subprocess
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not found")
+    exe = tmp_path / "sched_san"
+    src = [os.path.join(ROOT, "tests", "sanitize", "schedule_driver.cpp"),
+           os.path.join(ROOT, "scheduling_persistent_fa_amd", "csrc", "schedule.cpp")]
+    subprocess.run([gxx, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                    "-fno-omit-frame-pointer", "-o", str(exe), *src], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "0 failures" in r.stdout

@@ -322,3 +322,30 @@ def test_band_shift_rejects_unsupported_bands():
     for N, Nk, band in [(8, 8, (3, 0)), (8, 10, (4, 0)), (8, 8, (2, 1)), (4, 4, (4, 0))]:
         with pytest.raises(Sch.ScheduleError):
             Sch.build(Sch.BAND, SHIFT, N, 1, 1, 4, Nk=Nk, band=band)
+
+
+def test_splitmix64_matches_its_published_sequence():
+    # SplitMix64 seeded with 0 (Steele, Lea and Flood, OOPSLA 2014; the
+    # reference generator's first three outputs): the state advances by the
+    # golden-ratio increment before each output.
+    G = 0x9E3779B97F4A7C15
+    assert [Sch.splitmix64((i * G) % 2**64) for i in range(3)] == [
+        0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+
+
+def test_jitter_factors_span_half_to_three_halves():
+    xs = [Sch.jitter(99, w, i) for w in range(8) for i in range(500)]
+    assert min(xs) >= 0.5 and max(xs) < 1.5
+    assert 0.95 < sum(xs) / len(xs) < 1.05
+    assert Sch.jitter(0, 3, 4) == 1.0
+
+
+def test_jittered_shift_keeps_its_lockstep_order():
+    # Under any timing the shift gang still reduces each dQ tile in ordinal
+    # order (the simulation would raise on a deadlock), and the makespan is at
+    # least the slowest member's own work.
+    lists = Sch.build(FULL, SHIFT, 8, 1, 2, 8)
+    for seed in range(1, 50):
+        mk, _ = Sch.simulate(lists, 1.0, 0.25, seed)
+        own = max(sum(Sch.jitter(seed, w, i) + 0.25 for i in range(len(l))) for w, l in enumerate(lists))
+        assert mk >= own - 1e-9
