@@ -230,6 +230,31 @@ int dash_attn_bwd_window(const void* q, const void* k, const void* v, const void
                          int window_left, int window_right, int schedule,
                          const dash_bwd_opts* opts, void* stream);
 
+/*
+ * Allocation-free backward pass, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, results and bits as dash_attn_bwd_qk,
+ * but it calls no hipMalloc, hipFree or other allocating device routine: the
+ * workspace (fp32 dQ accumulator, Delta, semaphores, error word) and the
+ * step lists live in a static device array of 144 MiB per GPU (allocated
+ * when the library's code object holding it is first used in the process,
+ * held until the process ends).  Problems whose workspace plus step lists
+ * exceed it return DASH_ERR_WORKSPACE before anything is launched (B1 Hq16
+ * S16384 D128 needs about 133 MiB).  opts->workspace must be NULL
+ * (DASH_ERR_INVALID_ARG).  Step lists are built in host memory on a shape's
+ * first call and copied into the array with hipMemcpyAsync on `stream` when
+ * the shape differs from the previous call's on the device.
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (on different streams, or from several threads) race and give wrong
+ * results; calls on one stream are ordered.  A semaphore give-up writes NaN
+ * to dQ, dK, dV and is reported by dash_check_async_error (or by this call
+ * with sync_check), not by the next call.
+ */
+int dash_attn_bwd_qk_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                             const float* lse, void* dq, void* dk, void* dv,
+                             int B, int Hq, int Hkv, int Sq, int Sk, int D, float softmax_scale, int mask,
+                             int schedule, const dash_bwd_opts* opts, void* stream);
+
 /* Bytes of device workspace dash_attn_bwd needs for these sizes (fp32 dQ
  * accumulator over the query tiles' rows, Delta, semaphores, error word,
  * scratch tiles); an upper bound valid for any key length and tile when

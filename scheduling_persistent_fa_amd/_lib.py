@@ -37,7 +37,7 @@ EXPORTS = (
     "dash_schedule_validate", "dash_schedule_simulate", "dash_schedule_free", "dash_schedule_choose",
     "dash_schedule_choose_qk", "dash_schedule_choose_band",
     "dash_status_string",
-    "dash_last_error", "dash_device_info", "dash_check_async_error",
+    "dash_last_error", "dash_device_info", "dash_check_async_error", "dash_attn_bwd_qk_noalloc",
 )
 
 
@@ -77,6 +77,7 @@ def _declare(lib):
     lib.dash_attn_fwd_qk.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
     lib.dash_attn_bwd.argtypes = [vp] * 9 + [i, i, i, i, i, f, i, i, ctypes.POINTER(BwdOpts), vp]
     lib.dash_attn_bwd_qk.argtypes = [vp] * 9 + [i, i, i, i, i, i, f, i, i, ctypes.POINTER(BwdOpts), vp]
+    lib.dash_attn_bwd_qk_noalloc.argtypes = [vp] * 9 + [i, i, i, i, i, i, f, i, i, ctypes.POINTER(BwdOpts), vp]
     lib.dash_attn_fwd_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
     lib.dash_attn_bwd_window.argtypes = [vp] * 9 + [i, i, i, i, i, i, f, i, i, i, ctypes.POINTER(BwdOpts), vp]
     lib.dash_schedule_build_band.argtypes = [i, i, i, i, i, i, i, i, i, i, i, ctypes.POINTER(vp)]

@@ -118,6 +118,25 @@ def attn_bwd(q, k, v, o, do, lse, causal: bool, schedule: int, scale: float = 0.
     return dq, dk, dv
 
 
+def attn_bwd_noalloc(q, k, v, o, do, lse, causal: bool, schedule: int, dq, dk, dv, scale: float = 0.0,
+                     opts: _lib.BwdOpts | None = None, stream=None):
+    """dash_attn_bwd_qk_noalloc: the backward pass into caller-allocated dq,
+    dk, dv with the library's static scratch (no device allocation)."""
+    B, Hq, Sq, D = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    for name, t, shp in (("q", q, (B, Hq, Sq, D)), ("k", k, (B, Hkv, Sk, D)), ("v", v, (B, Hkv, Sk, D)),
+                         ("o", o, (B, Hq, Sq, D)), ("do", do, (B, Hq, Sq, D)), ("dq", dq, (B, Hq, Sq, D)),
+                         ("dk", dk, (B, Hkv, Sk, D)), ("dv", dv, (B, Hkv, Sk, D))):
+        _check_bhsd(name, t, shp)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Sq) or not lse.is_contiguous():
+        raise ValueError("lse: expected contiguous float32 [B,Hq,Sq]")
+    op = ctypes.byref(opts) if opts is not None else None
+    _lib.check(_lib.lib().dash_attn_bwd_qk_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, Sq, Sk, D,
+        float(scale), MASK_CAUSAL if causal else MASK_FULL, schedule, op, _stream(stream)))
+    return dq, dk, dv
+
+
 def bwd_delta(o, do, stream=None):
     B, H, S, D = o.shape
     _check_bhsd("o", o, (B, H, S, D))

@@ -267,6 +267,21 @@ TileGrid tile_grid(int Sq, int Sk, int T, bool aligned) {
 
 float default_scale(float s, int D) { return s > 0.f ? s : 1.0f / std::sqrt((float)D); }
 
+// The allocation-free entry point keeps everything in the per-device static
+// scratch array of noalloc.hip: [0, 256) the give-up word, then the
+// workspace, then the step lists.  Per device it remembers whose step lists
+// the scratch holds, so a repeated shape copies nothing.  Host copies of the
+// lists it uploaded stay alive (the copies are asynchronous), at most
+// kSchedCacheEntries of them; evicting one synchronises the device first.
+constexpr size_t kNoallocStickyBytes = 256;
+struct NoallocDevice {
+  bool have_key = false;
+  SchedKey key;
+};
+std::map<int, NoallocDevice> g_noalloc;
+std::map<SchedKey, std::pair<std::shared_ptr<dash::Schedule>, unsigned long long>> g_noalloc_host;
+unsigned long long g_noalloc_clock = 0;
+
 }  // namespace
 
 extern "C" {
@@ -303,6 +318,28 @@ int dash_check_async_error(void* stream) {
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   e = hipStreamSynchronize((hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  bool noalloc_used = false;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    noalloc_used = g_noalloc.count(dev) != 0;
+  }
+  if (noalloc_used) {  // the allocation-free entry point's give-up word, in its scratch
+    char* base = nullptr;
+    e = dash::noalloc_scratch(dev, &base);
+    if (e != hipSuccess) return hip_fail(e, "no-alloc scratch");
+    int word = 0;
+    e = hipMemcpy(&word, base, sizeof(int), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpy(no-alloc error word)");
+    if (word) {
+      const int zero = 0;
+      e = hipMemcpy(base, &zero, sizeof(int), hipMemcpyHostToDevice);
+      if (e != hipSuccess) return hip_fail(e, "hipMemcpy(no-alloc error word)");
+      (void)take_sticky_error(dev);
+      return fail(DASH_ERR_TIMEOUT,
+                  "an earlier backward call on this device gave up waiting on a dQ semaphore; its dQ, dK and dV "
+                  "were set to NaN");
+    }
+  }
   return take_sticky_error(dev);
 }
 
@@ -793,6 +830,90 @@ int dash_attn_bwd_window(const void* q, const void* k, const void* v, const void
                          const dash_bwd_opts* opts, void* stream) {
   return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, Sq, Sk, D, softmax_scale,
                   mask_from_window(window_left, window_right, Sq, Sk), schedule, opts, stream);
+}
+
+int dash_attn_bwd_qk_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                             const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk,
+                             int D, float softmax_scale, int mask, int schedule, const dash_bwd_opts* opts,
+                             void* stream) {
+  const void* ptrs[] = {q, k, v, o, dO, lse, dq, dk, dv};
+  const Mask mk = mask_from_enum(mask);
+  BwdPlan pl;
+  int st = bwd_plan(ptrs, B, Hq, Hkv, Sq, Sk, D, softmax_scale, mk, schedule, opts, &pl);
+  if (st) return st;
+  hipStream_t strm = (hipStream_t)stream;
+  if (pl.empty) {
+    if (pl.kv_elems == 0) return DASH_OK;
+    st = zero_bf16(dk, pl.kv_elems, D, strm);
+    return st ? st : zero_bf16(dv, pl.kv_elems, D, strm);
+  }
+  if (pl.op.workspace)
+    return fail(DASH_ERR_INVALID_ARG, "the allocation-free entry point uses its own scratch: opts->workspace must be NULL");
+
+  // Step lists on the host (built and validated on a shape's first call).
+  std::shared_ptr<dash::Schedule> hs;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_noalloc_host.find(pl.key);
+    if (it != g_noalloc_host.end()) {
+      it->second.second = ++g_noalloc_clock;
+      hs = it->second.first;
+    }
+  }
+  if (!hs) {
+    st = build_host_schedule(pl, mk.kind, &hs);
+    if (st) return st;
+  }
+  const size_t steps_bytes = hs->steps.size() * sizeof(dash::StepRec);
+  const size_t off_ws = kNoallocStickyBytes;
+  const size_t off_steps = align256(off_ws + pl.L.total);
+  const size_t off_offsets = align256(off_steps + steps_bytes);
+  const size_t need = off_offsets + hs->offsets.size() * sizeof(int32_t);
+  if (need > dash::kNoallocScratchBytes)
+    return fail(DASH_ERR_WORKSPACE, "problem needs " + std::to_string(need) +
+                                        " bytes of scratch; the allocation-free entry point has " +
+                                        std::to_string(dash::kNoallocScratchBytes));
+  char* base = nullptr;
+  hipError_t e = dash::noalloc_scratch(pl.dev, &base);
+  if (e != hipSuccess) return hip_fail(e, "no-alloc scratch (hipGetSymbolAddress)");
+
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    NoallocDevice& nd = g_noalloc[pl.dev];
+    if (!nd.have_key || !(nd.key == pl.key)) {
+      if (!g_noalloc_host.count(pl.key)) {
+        if (g_noalloc_host.size() >= kSchedCacheEntries) {
+          auto lru = g_noalloc_host.begin();
+          for (auto j = g_noalloc_host.begin(); j != g_noalloc_host.end(); ++j)
+            if (j->second.second < lru->second.second) lru = j;
+          e = hipDeviceSynchronize();  // its copy may still be in flight
+          if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+          g_noalloc_host.erase(lru);
+        }
+        g_noalloc_host.emplace(pl.key, std::make_pair(hs, ++g_noalloc_clock));
+      }
+      e = hipMemcpyAsync(base + off_steps, hs->steps.data(), steps_bytes, hipMemcpyHostToDevice, strm);
+      if (e == hipSuccess)
+        e = hipMemcpyAsync(base + off_offsets, hs->offsets.data(), hs->offsets.size() * sizeof(int32_t),
+                           hipMemcpyHostToDevice, strm);
+      if (e != hipSuccess) {
+        nd.have_key = false;
+        return hip_fail(e, "hipMemcpyAsync(no-alloc step lists)");
+      }
+      nd.have_key = true;
+      nd.key = pl.key;
+    }
+  }
+  DevSchedule ds;
+  ds.steps = (int32_t*)(base + off_steps);
+  ds.offsets = (int32_t*)(base + off_offsets);
+  ds.num_steps = (long long)hs->steps.size();
+  st = bwd_enqueue(pl, ptrs, mk, base + off_ws, ds, (int*)base, strm);
+  if (st == DASH_ERR_TIMEOUT) {  // reported by sync_check: clear the give-up word, it is not reported again
+    const int zero = 0;
+    (void)hipMemcpy(base, &zero, sizeof(int), hipMemcpyHostToDevice);
+  }
+  return st;
 }
 
 }  // extern "C"

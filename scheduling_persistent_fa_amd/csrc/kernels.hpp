@@ -60,4 +60,11 @@ struct FinalizeLaunch {
 };
 hipError_t launch_dq_finalize(const FinalizeLaunch& F, hipStream_t st);
 
+// Scratch of the allocation-free entry point (noalloc.hip): a static device
+// array of this many bytes per GPU.
+constexpr size_t kNoallocScratchBytes = size_t(144) << 20;
+// Device address of `dev`'s scratch array; `dev` must be the current device.
+// The first call per device resolves it with hipGetSymbolAddress.
+hipError_t noalloc_scratch(int dev, char** out);
+
 }  // namespace dash
