@@ -222,6 +222,8 @@ int check_sizes(int B, int Hq, int Hkv, int Sq, int Sk, int D, const Mask& mask)
     return fail(DASH_ERR_INVALID_ARG, "a causal or windowed mask needs Sk >= Sq (it is aligned at the bottom right)");
   if (D != 64 && D != 128) return fail(DASH_ERR_UNSUPPORTED, "head dimension must be 64 or 128");
   if (Sq > (1 << 24) || Sk > (1 << 24)) return fail(DASH_ERR_UNSUPPORTED, "sequence longer than 2^24 rows");
+  if ((long long)Sq * D * 2 >= (1LL << 31))  // one head's query rows are addressed with 32-bit offsets
+    return fail(DASH_ERR_UNSUPPORTED, "one head's query rows exceed 2 GiB");
   if ((long long)B * Hq * (std::max(Sq, Sk) + 256LL) * D >= (1LL << 40))
     return fail(DASH_ERR_UNSUPPORTED, "problem too large");
   if (B == 0 || Sq == 0) return kEmpty;

@@ -19,6 +19,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "kernels.hpp"
 
@@ -467,12 +468,13 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
   constexpr int PQ = 2 * D;           // LDS pitch (bytes) of Q / dO / K rows, unpadded (see lds_swizzle)
   constexpr int PS = (M + 8) * 2;     // LDS pitch (bytes) of P^T / dS^T rows
   constexpr int QBUF = M * PQ;
+  constexpr int DSBUF = T * PS;
   constexpr int OFF_Q = 0;                       // [2][M][PQ]
   constexpr int OFF_DO = OFF_Q + 2 * QBUF;       // [2][M][PQ]
   constexpr int OFF_K = OFF_DO + 2 * QBUF;       // [T][PQ]
   constexpr int OFF_PT = OFF_K + T * PQ;         // [T][PS]  P^T
-  constexpr int OFF_DS = OFF_PT + T * PS;        // [T][PS]  dS^T
-  constexpr int OFF_STAT = OFF_DS + T * PS;      // [2][2][M] f32: LSE (log2 domain), Delta
+  constexpr int OFF_DS = OFF_PT + T * PS;        // [2][T][PS]  dS^T, double-buffered (contracted for dQ one sub-step late)
+  constexpr int OFF_STAT = OFF_DS + 2 * DSBUF;   // [2][2][M] f32: LSE (log2 domain), Delta
   constexpr int OFF_FLAG = OFF_STAT + 4 * M * 4;
   constexpr int SMEM = OFF_FLAG + 16;
   constexpr int QCH = M * D / 8 / NT;            // 16-byte chunks per thread of one Q (or dO) block
@@ -536,17 +538,21 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
   float pstat = 0.f;
   const int st_tid = threadIdx.x < 2 * M ? threadIdx.x : 0;
   const float st_mul = st_tid < M ? kLog2e : 1.f;
+  // Q / dO rows through buffer descriptors over the head's rows: a row
+  // outside 0 .. Sq-1 lies outside the descriptor's range and reads as zeros
+  // (its LSE of +inf below already makes every contribution of it zero).
   auto load_block = [&](int head, int vrow0) {  // vrow0: first virtual row of the block
-    const __bf16* qh = a.q + (size_t)head * Sq * D;
-    const __bf16* doh = a.dO + (size_t)head * Sq * D;
     const int row0 = vrow0 - qshift;
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16*>(uniform_ptr(a.q + (size_t)head * Sq * D)), (short)0, Sq * D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rdo = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16*>(uniform_ptr(a.dO + (size_t)head * Sq * D)), (short)0, Sq * D * 2, 0x00020000);
 #pragma unroll
     for (int i = 0; i < QCH; ++i) {
       const int ch = threadIdx.x + i * NT;
-      const int row = min(max(row0 + ch / (D / 8), 0), Sq - 1);
-      const size_t e = (size_t)row * D + (ch % (D / 8)) * 8;
-      pq[i] = *(const bf16x8*)(qh + e);
-      pdo[i] = *(const bf16x8*)(doh + e);
+      const int off = (row0 + ch / (D / 8)) * (2 * D) + (ch % (D / 8)) * 16;  // negative: out of range
+      pq[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+      pdo[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rdo, off, 0, 0));
     }
     const int srow = row0 + (st_tid & (M - 1));
     const bool valid = srow >= 0 && srow < Sq;
@@ -589,39 +595,111 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
     }
   };
   int buf = 0;
-  // dQ read-modify-write pipelined by one sub-step (deterministic schedules):
-  // the block computed in sub-step s is read (after the wait) at the end of
-  // s, added and written after the S/dP phase of s+1, and its semaphore is
-  // released after the dK/dV contraction of s+1, once the writes are
-  // complete.  When s+1 starts a new chain, the block is finished and
-  // released before that chain's K/V loads instead (see the chain start).
-  f32x16 pdq[TPW], pprev[TPW];
+  // dQ of each 64-row block is contracted one sub-step late: the block of
+  // sub-step s (its dS^T kept in one of two LDS buffers) is contracted in the
+  // S/dP phase of sub-step s+1, interleaved with that sub-step's softmax, so
+  // that each wave keeps the matrix core busy while its exponentials run on
+  // the vector ALU.  Deterministic schedules then add the
+  // predecessor's partial (read at the end of sub-step s, after the wait on
+  // the block's semaphore) and write the sum back; the semaphore is released
+  // after the dK/dV contraction of s+1, once the writes are complete.  When
+  // s+1 starts a new key/value chain the block is contracted, written and
+  // released at the chain start instead, before K is replaced.
+  f32x16 pprev[TPW];
   // The vector-memory sequence of a sub-step is the same on every path (a
   // missing prefetch re-reads the current block, a missing write goes to the
   // dummy tiles), so the compiler's wait counts stay exact and no wait drains
   // more than the operation it is for.
-  float* p_ws = a.dummy;  // block whose partial is pending (the dummy tiles if none)
-  int* p_sem = nullptr;   // its semaphore, if it is a real block
+  float* p_ws = a.dummy;  // block whose contraction is pending (the dummy tiles if none)
+  int* p_sem = nullptr;   // its semaphore, if it is a real block (deterministic)
   int p_val = 0;
-  int* r_sem = nullptr;  // semaphore to release once this wave's writes are complete
+  int p_buf = 0;          // LDS buffer holding its dS^T
+  bool p_real = false;    // atomic variant: a block is pending
+  int* r_sem = nullptr;   // semaphore to release once this wave's writes are complete
   int r_val = 0;
   constexpr bool EVEN = (NQT % NW) == 0;  // every wave holds NQT / NW dQ tiles
   const bool has_tiles = EVEN || w < NQT;
-  // Pending block's partial plus its predecessor's sum, to its workspace tiles
-  // (tiles of other waves' indices past the last go to the dummy tiles).
-  auto finish_pending = [&]() {
+#pragma unroll
+  for (int ti = 0; ti < TPW; ++ti) pprev[ti] = f32x16{};
+
+  // dQ partial = dS K over all T key/value rows of the pending block, for
+  // this wave's C tiles (chain starts and the drain; the sub-step loop
+  // interleaves the same contraction with its softmax).  The K^T and dS^T
+  // operands of chunk c+1 are read while chunk c's MFMA runs.
+  auto dq_contract = [&](f32x16 (&dq)[TPW]) {
+    if (!has_tiles) return;
+    const int dbw = w % DB;
+    const int ko0 = opaque(t_dk[0] ^ ((hf * DH ^ dbw) << 6)), ko1 = opaque(t_dk[1] ^ ((hf * DH ^ dbw) << 6));
+    const LDS char* pds0 = base + OFF_DS + p_buf * DSBUF + o_trs;
+    auto ka_at = [&](int c) {
+      return cat8(lds_tr4(base + OFF_K + ko0 + 16 * c * PQ), lds_tr4(base + OFF_K + ko1 + 16 * c * PQ));
+    };
 #pragma unroll
     for (int ti = 0; ti < TPW; ++ti) {
-      const int t_idx = w + NW * ti;
-      const __amdgpu_buffer_rsrc_t rs = ws_rsrc(uniform_ptr((EVEN || t_idx < NQT) ? p_ws : a.dummy) + t_idx * 1024);
+      const int qb = (w + NW * ti) / DB;
+      const LDS char* pds = pds0 + qb * 64;
+      f32x16 acc = f32x16{};
+      bf16x8 ka[2], sa[2];
+      ka[0] = ka_at(0);
+      sa[0] = lds_tr8_at(pds, PS);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        f32x4 v4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = pdq[ti][4 * q4 + e] + pprev[ti][4 * q4 + e];
-        __builtin_amdgcn_raw_buffer_store_b128(v4, rs, (q4 * 64 + lane) * 16, 0, kDeviceScope);
+      for (int c = 0; c < KC; ++c) {
+        if (c + 1 < KC) {
+          ka[(c + 1) & 1] = ka_at(c + 1);
+          sa[(c + 1) & 1] = lds_tr8_at(pds + 16 * (c + 1) * PS, PS);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        acc = mfma32(sa[c & 1], ka[c & 1], acc);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_s_setprio(0);
+      dq[ti] = acc;
     }
+  };
+  // Write out the pending block's contracted partial: deterministic
+  // schedules add the predecessor's partial (zeros for a first contribution)
+  // and store the sum to the block's tiles, to the dummy tiles when nothing is
+  // pending, and mark its semaphore for release; the atomic variant adds with
+  // fp32 atomics when a block is pending.
+  auto dq_store = [&](const f32x16 (&dq)[TPW]) {
+    if constexpr (ATOMIC) {
+      if (p_real) {
+#pragma unroll
+        for (int ti = 0; ti < TPW; ++ti) {
+          const int t_idx = w + NW * ti;
+          if (EVEN || t_idx < NQT) {
+            float* p = p_ws + t_idx * 1024 + lane;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              __hip_atomic_fetch_add(p + r * 64, dq[ti][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+      }
+    } else {
+      if (has_tiles) {
+#pragma unroll
+        for (int ti = 0; ti < TPW; ++ti) {
+          const int t_idx = w + NW * ti;
+          const __amdgpu_buffer_rsrc_t rs =
+              ws_rsrc(uniform_ptr((EVEN || t_idx < NQT) ? p_ws : a.dummy) + t_idx * 1024);
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            f32x4 v4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v4[e] = dq[ti][4 * q4 + e] + pprev[ti][4 * q4 + e];
+            __builtin_amdgcn_raw_buffer_store_b128(v4, rs, (q4 * 64 + lane) * 16, 0, kDeviceScope);
+          }
+        }
+      }
+      r_sem = p_sem;
+      r_val = p_val;
+    }
+  };
+  auto dq_finish = [&]() {
+    f32x16 dq[TPW];
+    dq_contract(dq);
+    dq_store(dq);
   };
   if (beg < end) {
     const int4 r0 = step_at(beg);
@@ -640,22 +718,17 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
     const __bf16* vh = a.v + ((size_t)kvh * Sk + (size_t)kj * T) * D;
     const int kv_valid = Sk - kj * T;  // key/value rows of this tile inside the sequence (>= T but on the last)
     if (first) {
-      // New chain: its V rows to registers and its K tile to LDS.  The previous
-      // chain's dK/dV are written only after that, so that waiting for these
-      // loads never waits for those writes to drain.
-      //
-      // The previous chain's last block is finished first and released as soon
-      // as these loads have arrived, rather than a sub-step into the new chain:
-      // where members change chains at different rounds (the causal symmetric
-      // shift), the block's successor is mid-chain and would otherwise wait for
-      // this chain start, and every later block of that successor with it.
-      bool release_now = false;
-      if constexpr (!ATOMIC) {
-        if (__builtin_amdgcn_readfirstlane((int)(p_sem != nullptr))) {
-          release_now = true;
-          finish_pending();
-        }
-      }
+      // New chain.  The previous chain's last block is contracted (its dS^T
+      // and K are still in LDS) and written first, and released as soon as
+      // the new chain's loads have arrived, rather than a sub-step into the
+      // new chain: where members change chains at different rounds (the
+      // causal symmetric shift), the block's successor is mid-chain and would
+      // otherwise wait for this chain start.  Then the new chain's V rows go
+      // to registers and its K tile to LDS; the previous chain's dK/dV are
+      // written only after that, so that waiting for these loads never waits
+      // for those writes to drain.
+      const bool flush = __builtin_amdgcn_readfirstlane((int)(ATOMIC ? p_real : p_sem != nullptr));
+      if (flush) dq_finish();
 #pragma unroll
       for (int c = 0; c < DC; ++c) vb[c] = *(const bf16x8*)(vh + (size_t)min(kv_local, kv_valid - 1) * D + 16 * c + 8 * h2);
       bf16x8 kt[KCH];
@@ -665,16 +738,19 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
         kt[u] = *(const bf16x8*)(kh + (size_t)row * D + col);
       }
       if constexpr (!ATOMIC) {
-        if (release_now) {
+        if (flush) {
           wait_vmem_all();
           if constexpr (DELAY) debug_delay(a.delay_seed, wg, i, 0, w, 0);
-          if (lane == 0) __hip_atomic_store(p_sem, p_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          // Nothing is pending any more: the finish below writes to the dummy tiles.
-          p_ws = a.dummy;
-          p_sem = nullptr;
+          if (r_sem != nullptr && lane == 0) __hip_atomic_store(r_sem, r_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          r_sem = nullptr;
         }
       }
-      __syncthreads();  // previous chain's dQ contraction is done with sK
+      // Nothing is pending any more: the contraction in the next S/dP phase
+      // writes to the dummy tiles.
+      p_ws = a.dummy;
+      p_sem = nullptr;
+      p_real = false;
+      __syncthreads();  // every wave is done with the previous chain's K
 #pragma unroll
       for (int u = 0; u < KCH; ++u) {
         const int ch = threadIdx.x + u * NT, row = ch / (D / 8), col = (ch % (D / 8)) * 8;
@@ -696,7 +772,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
     const bool mask_on = dd > a.wr - (T - 1) || dd < (T - 1) - a.wl || kv_valid < T;
 
     for (int sub = 0; sub < SUBS; ++sub) {
-      __syncthreads();  // B1: Q/dO/LSE/Delta of this block (and sK) visible; P^T, dS^T free
+      __syncthreads();  // B1: Q/dO/LSE/Delta of this block (and sK) visible; P^T and this dS^T buffer free
       if (*s_flag) {    // a wave gave up waiting in the previous sub-step
         aborted = true;
         break;
@@ -715,6 +791,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
       const LDS float* slse = (const LDS float*)(base + OFF_STAT + buf * 2 * M * 4);
       const LDS float* sdel = slse + M;
 
+      f32x16 dqp[TPW];
       {
         // S = Q K^T and dP = dO V^T for query rows 32*hf .. +31 x this pair's 32 key/value columns.
         f32x16 s = f32x16{}, dp = f32x16{};
@@ -728,9 +805,9 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
           bk[sl] = lds_row8(base + OFF_K + (rk ^ (c << 5)));
         };
         fetch(0, 0);
-        // Each of the three contractions runs at raised wave priority, so that
-        // while one wave of a SIMD issues matrix-core instructions the other
-        // wave's vector and LDS work fills the gaps (about 1% at B1 H16 S16384).
+        // Each contraction runs at raised wave priority, so that while one wave
+        // of a SIMD issues matrix-core instructions the other wave's vector and
+        // LDS work fills the gaps.
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int c = 0; c < DC; ++c) {
@@ -741,7 +818,12 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_setprio(0);
-        // P = exp2(S*scale*log2e - LSE*log2e); dS = P * (dP - Delta); both to LDS transposed.
+        // P = exp2(S*scale*log2e - LSE*log2e); dS = P * (dP - Delta); both to LDS
+        // transposed, four rows of this lane at a time.  Interleaved with it, the
+        // pending block's dQ partial = dS K (its dS^T in the other buffer): after
+        // each group of four rows the wave issues the next dQ MFMAs, which run on
+        // the matrix core while the next group's exponentials run on the vector
+        // ALU.
         // Element (8j + e) of this lane has key - diagonal key = rel - (8j + e); under
         // mask_on P is zero where that exceeds wr (hi > 8j + e) or falls below -wl
         // (lo < 8j + e), and in every row of a key/value column past Sk.  The bounds are
@@ -751,40 +833,77 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
         int hi = kv_local >= kv_valid ? kUnbounded : rel - a.wr;
         int lo = rel + a.wl;
         asm volatile("" : "+v"(hi), "+v"(lo));
+        LDS char* ds_out = base + OFF_DS + buf * DSBUF + o_stt;
+        constexpr int NDQ = TPW * KC;  // dQ MFMAs of this wave
+        static_assert(NDQ % 4 == 0, "dQ chunks per group of rows");
+        constexpr int PER_J = NDQ / 4;
+        static_assert(SHARE_K, "a wave's dQ tiles share one d block");
+        const int dbw = w % DB;
+        const int ko0 = opaque(t_dk[0] ^ ((hf * DH ^ dbw) << 6)), ko1 = opaque(t_dk[1] ^ ((hf * DH ^ dbw) << 6));
+        const LDS char* pds0 = base + OFF_DS + p_buf * DSBUF + o_trs;
+#pragma unroll
+        for (int ti = 0; ti < TPW; ++ti) dqp[ti] = f32x16{};
+        // Two copies of the loop: tile pairs that need no element mask (every
+        // pair of a full mask, all but the diagonal pairs of a causal one) skip
+        // the per-element comparisons.
+        auto softmax_dq = [&](auto masked_tag) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
+        f32x4 l4[2], d4[2];
+        l4[0] = *(const LDS f32x4*)((const LDS char*)slse + o_stat);
+        d4[0] = *(const LDS f32x4*)((const LDS char*)sdel + o_stat);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const f32x4 l4 = *(const LDS f32x4*)((const LDS char*)slse + o_stat + 32 * j);
-          const f32x4 d4 = *(const LDS f32x4*)((const LDS char*)sdel + o_stat + 32 * j);
+          // operands of this group's dQ MFMAs (their latency hides behind the exponentials)
+          bf16x8 ka[PER_J], sa[PER_J];
+          if (has_tiles) {
+#pragma unroll
+            for (int u = 0; u < PER_J; ++u) {
+              const int uu = j * PER_J + u, ti = uu / KC, c = uu % KC;
+              const int qb = (w + NW * ti) / DB;
+              ka[u] = cat8(lds_tr4(base + OFF_K + ko0 + 16 * c * PQ), lds_tr4(base + OFF_K + ko1 + 16 * c * PQ));
+              sa[u] = lds_tr8_at(pds0 + qb * 64 + 16 * c * PS, PS);
+            }
+          }
+          if (j + 1 < 4) {
+            l4[(j + 1) & 1] = *(const LDS f32x4*)((const LDS char*)slse + o_stat + 32 * (j + 1));
+            d4[(j + 1) & 1] = *(const LDS f32x4*)((const LDS char*)sdel + o_stat + 32 * (j + 1));
+          }
           bf16x4 tp, ts;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * j + e;
-            float p = __builtin_amdgcn_exp2f(s[r] * a.scale_log2 - l4[e]);
-            if (mask_on && (hi > 8 * j + e || (LEFT && lo < 8 * j + e))) p = 0.f;
+            float p = __builtin_amdgcn_exp2f(s[r] * a.scale_log2 - l4[j & 1][e]);
+            if (MASKED && (hi > 8 * j + e || (LEFT && lo < 8 * j + e))) p = 0.f;
             tp[e] = (__bf16)p;
-            ts[e] = (__bf16)(p * (dp[r] - d4[e]));
+            ts[e] = (__bf16)(p * (dp[r] - d4[j & 1][e]));
           }
           *(LDS bf16x4*)(base + OFF_PT + o_stt + 16 * j) = tp;
-          *(LDS bf16x4*)(base + OFF_DS + o_stt + 16 * j) = ts;
+          *(LDS bf16x4*)(ds_out + 16 * j) = ts;
+          if (has_tiles) {
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int u = 0; u < PER_J; ++u) {
+              const int uu = j * PER_J + u, ti = uu / KC;
+              dqp[ti] = mfma32(sa[u], ka[u], dqp[ti]);
+            }
+            __builtin_amdgcn_s_setprio(0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
+        };
+        if (mask_on) softmax_dq(std::true_type{});
+        else softmax_dq(std::false_type{});
       }
-      if constexpr (!ATOMIC) {
-        // Finish the pending block: its predecessor's partial has arrived (zeros
-        // for a first contribution).  The sum is formed on every path so that no
-        // path leaves the reads pending.
-        if (has_tiles) finish_pending();  // compile-time true when the tiles divide evenly over the waves
-        r_sem = p_sem;
-        r_val = p_val;
-      }
+      dq_store(dqp);
       __syncthreads();  // B2: P^T, dS^T complete
 
       const int blk = qi * SUBS + sub;
       float* wsb = a.ws + ((size_t)head * nblk + blk) * (size_t)(M * D);
       int* semp = a.sem + ((size_t)head * nblk + blk) * kSemPerBlock + w;
       // First look at this block's semaphore now, so that its latency is hidden
-      // behind the dK/dV and dQ contractions (in the lockstep schedules the
-      // predecessor has usually released it by now); the wait below only polls
-      // if not.
+      // behind the dK/dV contraction (in the lockstep schedules the predecessor
+      // has usually released it by now); the wait below only polls if not.
       int sem_seen = 0;
       if constexpr (!ATOMIC) sem_seen = __hip_atomic_load(semp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       // dV += P^T dO, dK += dS^T Q over the block's 64 query rows, d half hf.
@@ -793,9 +912,10 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
       // keep that order), which hides part of the LDS latency.
       {
         bf16x8 ap[2], ads[2];
+        const LDS char* ds_in = base + OFF_DS + buf * DSBUF + o_rowt;
         const int td[2] = {opaque(buf * QBUF + t_dk[0]), opaque(buf * QBUF + t_dk[1])};
         ap[0] = lds_row8(base + OFF_PT + o_rowt);
-        ads[0] = lds_row8(base + OFF_DS + o_rowt);
+        ads[0] = lds_row8(ds_in);
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int c = 0; c < QC; ++c) {
@@ -810,7 +930,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
           bq[0] = tr_dkdv(false, 0);
           if (c + 1 < QC) {
             ap[sl ^ 1] = lds_row8(base + OFF_PT + o_rowt + 32 * (c + 1));
-            ads[sl ^ 1] = lds_row8(base + OFF_DS + o_rowt + 32 * (c + 1));
+            ads[sl ^ 1] = lds_row8(ds_in + 32 * (c + 1));
           }
 #pragma unroll
           for (int j = 0; j < DH; ++j) {
@@ -827,66 +947,24 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
         __builtin_amdgcn_s_setprio(0);
       }
       if constexpr (!ATOMIC) {
-        // Release the block finished after the S/dP phase as soon as its writes
+        // Release the block written in the S/dP phase as soon as its writes
         // have had the dK/dV contraction to complete (successors wait on it).
         wait_vmem_all();
         if constexpr (DELAY) debug_delay(a.delay_seed, wg, i, sub, w, 1);
         if (r_sem != nullptr && lane == 0) __hip_atomic_store(r_sem, r_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         r_sem = nullptr;
       }
-      // dQ partial = dS K over all T key/value rows, for this wave's C tiles
-      // (after the dK/dV contraction, so that the partial is not live there).
-      f32x16 dq[TPW];
-      {
-        bf16x8 bk[KC];
-#pragma unroll
-        for (int ti = 0; ti < TPW; ++ti) {
-          const int t_idx = w + NW * ti;
-          if (EVEN || t_idx < NQT) {
-            const int qb = t_idx / DB, db = t_idx % DB;
-            if (ti == 0 || !SHARE_K) {
-              const int o0 = opaque(t_dk[0] ^ ((hf * DH ^ db) << 6)), o1 = opaque(t_dk[1] ^ ((hf * DH ^ db) << 6));
-#pragma unroll
-              for (int c = 0; c < KC; ++c)
-                bk[c] = cat8(lds_tr4(base + OFF_K + o0 + 16 * c * PQ), lds_tr4(base + OFF_K + o1 + 16 * c * PQ));
-            }
-            const LDS char* pds = base + OFF_DS + o_trs + qb * 64;
-            f32x16 acc = f32x16{};
-            // the dS^T operand of chunk c+1 is read while chunk c's MFMA runs
-            bf16x8 ads2[2];
-            ads2[0] = lds_tr8_at(pds, PS);
-            __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-            for (int c = 0; c < KC; ++c) {
-              if (c + 1 < KC) ads2[(c + 1) & 1] = lds_tr8_at(pds + 16 * (c + 1) * PS, PS);
-              __builtin_amdgcn_sched_barrier(0);
-              acc = mfma32(ads2[c & 1], bk[c], acc);
-              __builtin_amdgcn_sched_barrier(0);
-            }
-            __builtin_amdgcn_s_setprio(0);
-            dq[ti] = acc;
-          }
-        }
-      }
 
-      if constexpr (ATOMIC) {
-#pragma unroll
-        for (int ti = 0; ti < TPW; ++ti) {
-          const int t_idx = w + NW * ti;
-          if (EVEN || t_idx < NQT) {
-            float* p = wsb + t_idx * 1024 + lane;
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              __hip_atomic_fetch_add(p + r * 64, dq[ti][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-        }
-      }
-
-      // The other buffer is free (read before B1): stage the prefetched block.
+      // The other Q/dO buffer is free (read before B1): stage the prefetched block.
       store_block(buf ^ 1);
-      buf ^= 1;
 
-      if constexpr (!ATOMIC) {
+      // This block is now the pending one.
+      p_buf = buf;
+      buf ^= 1;
+      if constexpr (ATOMIC) {
+        p_ws = wsb;
+        p_real = true;
+      } else {
         // Wait for this block's predecessor, then start reading its partial.  (The
         // early value is consumed on every path, so it is never left pending.)
         if constexpr (DELAY) debug_delay(a.delay_seed, wg, i, sub, w, 2);
@@ -919,7 +997,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
             asm volatile("" ::: "memory");  // the reads stay after the wait above
             // A first contribution (ordinal 0) has no predecessor: an empty
             // buffer range makes these loads return zeros without reading
-            // memory, so the sum below needs no select.
+            // memory, so the sum needs no select.
             const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
                 wsb + (t_idx < NQT ? t_idx : t_idx % NQT) * 1024, (short)0, ord > 0 ? 4096 : 0, 0x00020000);
 #pragma unroll
@@ -930,8 +1008,6 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
             }
           }
         }
-#pragma unroll
-        for (int ti = 0; ti < TPW; ++ti) pdq[ti] = dq[ti];
         const bool real = has_tiles && !give_up;
         p_ws = real ? wsb : a.dummy;
         p_sem = real ? semp : nullptr;
@@ -947,27 +1023,18 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
     }
   }
   if (epi_pending && !aborted) write_dkdv(epi_kvh, epi_kj);
-  if constexpr (!ATOMIC) {
-    __syncthreads();
-    if (*s_flag) aborted = true;
-    if (!aborted && p_sem != nullptr) {
-      // Drain: the last block of this wave.
-#pragma unroll
-      for (int ti = 0; ti < TPW; ++ti) {
-        const int t_idx = w + NW * ti;
-        if (EVEN || t_idx < NQT) {
-          pdq[ti] += pprev[ti];
-          const __amdgpu_buffer_rsrc_t rs = ws_rsrc(p_ws + t_idx * 1024);
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const f32x4 v4 = {pdq[ti][4 * q4], pdq[ti][4 * q4 + 1], pdq[ti][4 * q4 + 2], pdq[ti][4 * q4 + 3]};
-            __builtin_amdgcn_raw_buffer_store_b128(v4, rs, (q4 * 64 + lane) * 16, 0, kDeviceScope);
-          }
-        }
+  // Drain: the last block of this wave (K and its dS^T are still in LDS).
+  __syncthreads();
+  if (*s_flag) aborted = true;
+  if (!aborted) {
+    const bool flush = __builtin_amdgcn_readfirstlane((int)(ATOMIC ? p_real : p_sem != nullptr));
+    if (flush) {
+      dq_finish();
+      if constexpr (!ATOMIC) {
+        wait_vmem_all();
+        if constexpr (DELAY) debug_delay(a.delay_seed, wg, end, 0, w, 3);
+        if (r_sem != nullptr && lane == 0) __hip_atomic_store(r_sem, r_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      wait_vmem_all();
-      if constexpr (DELAY) debug_delay(a.delay_seed, wg, end, 0, w, 3);
-      if (lane == 0) __hip_atomic_store(p_sem, p_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   if (a.stall && threadIdx.x == 0) {
