@@ -576,21 +576,24 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
   bool epi_pending = false;
   int epi_kvh = 0, epi_kj = 0;
   auto write_dkdv = [&](int kvh_, int kj_) {
-    const size_t o_lane = (size_t)opaque((kv0 + 4 * h2) * D + hf * DH * 32 + c32);
-    __bf16* dkh = a.dk + ((size_t)kvh_ * Sk + (size_t)kj_ * T) * D + o_lane;
-    __bf16* dvh = a.dv + ((size_t)kvh_ * Sk + (size_t)kj_ * T) * D + o_lane;
-    __bf16* sink = (__bf16*)a.dummy + o_lane;  // rows past Sk (same offsets, 32 KiB)
+    // Buffer descriptors over the tile's rows inside the sequence: stores to
+    // rows past Sk fall outside the range and are dropped.
     const int kv_valid = Sk - kj_ * T;
+    const int nbytes = min(kv_valid, T) * D * 2;
+    const size_t tile0 = ((size_t)kvh_ * Sk + (size_t)kj_ * T) * D;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(a.dk + tile0), (short)0, nbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(a.dv + tile0), (short)0, nbytes, 0x00020000);
+    const int tid_e = opaque((int)threadIdx.x);  // recomputed here, not kept live
+    const int l_e = tid_e & 63, w_e = tid_e >> 6;
+    const int o_lane = 2 * ((32 * (w_e >> 1) + 4 * (l_e >> 5)) * D + (w_e & 1) * DH * 32 + (l_e & 31));
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const bool ok = kv0 + 4 * h2 + 8 * (r >> 2) + (r & 3) < kv_valid;
-      __bf16* pk = ok ? dkh : sink;
-      __bf16* pv = ok ? dvh : sink;
 #pragma unroll
       for (int j = 0; j < DH; ++j) {
-        const int off = (8 * (r >> 2) + (r & 3)) * D + j * 32;
-        pk[off] = (__bf16)(dk_acc[j][r] * a.scale);
-        pv[off] = (__bf16)dv_acc[j][r];
+        const int off = o_lane + 2 * ((8 * (r >> 2) + (r & 3)) * D + j * 32);
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)(dk_acc[j][r] * a.scale)), rk,
+                                              off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)dv_acc[j][r]), rv, off, 0, 0);
       }
     }
   };
@@ -729,13 +732,30 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
       // for those writes to drain.
       const bool flush = __builtin_amdgcn_readfirstlane((int)(ATOMIC ? p_real : p_sem != nullptr));
       if (flush) dq_finish();
+      // Buffer descriptors over the tile's rows inside the sequence: rows past
+      // Sk read as zeros (they are masked out of P).  Per-lane offsets are
+      // recomputed from the lane's index here rather than kept live.
+      {
+        const int nbytes = min(kv_valid, T) * D * 2;
+        const __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(uniform_ptr(vh)), (short)0, nbytes, 0x00020000);
+        const int tid = opaque((int)threadIdx.x);
+        const int vo = (kv0 + (tid & 31)) * (2 * D) + 16 * ((tid >> 5) & 1);
 #pragma unroll
-      for (int c = 0; c < DC; ++c) vb[c] = *(const bf16x8*)(vh + (size_t)min(kv_local, kv_valid - 1) * D + 16 * c + 8 * h2);
+        for (int c = 0; c < DC; ++c)
+          vb[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, vo + 32 * c, 0, 0));
+      }
       bf16x8 kt[KCH];
+      {
+        const int nbytes = min(kv_valid, T) * D * 2;
+        const __amdgpu_buffer_rsrc_t rk =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(uniform_ptr(kh)), (short)0, nbytes, 0x00020000);
+        // chunk (tid + u * NT) of the row-major tile; the whole offset stays in
+        // the range-checked vector offset
+        const int ko = opaque((int)threadIdx.x) * 16;
 #pragma unroll
-      for (int u = 0; u < KCH; ++u) {
-        const int ch = threadIdx.x + u * NT, row = min(ch / (D / 8), kv_valid - 1), col = (ch % (D / 8)) * 8;
-        kt[u] = *(const bf16x8*)(kh + (size_t)row * D + col);
+        for (int u = 0; u < KCH; ++u)
+          kt[u] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, ko + u * NT * 16, 0, 0));
       }
       if constexpr (!ATOMIC) {
         if (flush) {
@@ -751,9 +771,10 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
       p_sem = nullptr;
       p_real = false;
       __syncthreads();  // every wave is done with the previous chain's K
+      const int tid_k = opaque((int)threadIdx.x);  // staging addresses recomputed here, not kept live
 #pragma unroll
       for (int u = 0; u < KCH; ++u) {
-        const int ch = threadIdx.x + u * NT, row = ch / (D / 8), col = (ch % (D / 8)) * 8;
+        const int ch = tid_k + u * NT, row = ch / (D / 8), col = (ch % (D / 8)) * 8;
         *(LDS bf16x8*)(base + OFF_K + qk_chunk(row, col / 8)) = kt[u];
       }
       if (epi_pending) write_dkdv(epi_kvh, epi_kj);
