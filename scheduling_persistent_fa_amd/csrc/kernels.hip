@@ -818,7 +818,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
         f32x16 s = f32x16{}, dp = f32x16{};
         // One 16-wide d chunk at a time, double-buffered: chunk c+1's Q, dO and
         // K operands are read while chunk c's two MFMAs run.
-        bf16x8 aq[2], ado[2], bk[2];
+        bf16x8 aq[3], ado[3], bk[3];
         const int rq = opaque(buf * QBUF + r_q), rk = opaque(r_k);
         auto fetch = [&](int c, int sl) {
           aq[sl] = lds_row8(base + OFF_Q + (rq ^ (c << 5)));
@@ -826,16 +826,17 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
           bk[sl] = lds_row8(base + OFF_K + (rk ^ (c << 5)));
         };
         fetch(0, 0);
+        if (DC > 1) fetch(1, 1);
         // Each contraction runs at raised wave priority, so that while one wave
         // of a SIMD issues matrix-core instructions the other wave's vector and
         // LDS work fills the gaps.
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int c = 0; c < DC; ++c) {
-          if (c + 1 < DC) fetch(c + 1, (c + 1) & 1);
+          if (c + 2 < DC) fetch(c + 2, (c + 2) % 3);
           __builtin_amdgcn_sched_barrier(0);
-          s = mfma32(aq[c & 1], bk[c & 1], s);
-          dp = mfma32(ado[c & 1], vb[c], dp);
+          s = mfma32(aq[c % 3], bk[c % 3], s);
+          dp = mfma32(ado[c % 3], vb[c], dp);
           __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_setprio(0);
@@ -937,33 +938,38 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
         const int td[2] = {opaque(buf * QBUF + t_dk[0]), opaque(buf * QBUF + t_dk[1])};
         ap[0] = lds_row8(base + OFF_PT + o_rowt);
         ads[0] = lds_row8(ds_in);
+        // d block j of this wave's half of dO (is_do) or Q, query chunk c
+        auto tr_dkdv = [&](bool is_do, int c, int j) {
+          const LDS char* b_ = base + (is_do ? OFF_DO : OFF_Q) + 16 * c * PQ;
+          return cat8(lds_tr4(b_ + (td[0] ^ (j << 6))), lds_tr4(b_ + (td[1] ^ (j << 6))));
+        };
+        // B operands of query chunk c+1 are read while chunk c's MFMAs run.
+        bf16x8 bdo[2][DH], bq[2][DH];
+#pragma unroll
+        for (int j = 0; j < DH; ++j) {
+          bdo[0][j] = tr_dkdv(true, 0, j);
+          bq[0][j] = tr_dkdv(false, 0, j);
+        }
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int c = 0; c < QC; ++c) {
           const int sl = c & 1;
-          bf16x8 bdo[DH], bq[DH];
-          // d block j of this wave's half of dO (is_do) or Q, query chunk c
-          auto tr_dkdv = [&](bool is_do, int j) {
-            const LDS char* b_ = base + (is_do ? OFF_DO : OFF_Q) + 16 * c * PQ;
-            return cat8(lds_tr4(b_ + (td[0] ^ (j << 6))), lds_tr4(b_ + (td[1] ^ (j << 6))));
-          };
-          bdo[0] = tr_dkdv(true, 0);
-          bq[0] = tr_dkdv(false, 0);
           if (c + 1 < QC) {
             ap[sl ^ 1] = lds_row8(base + OFF_PT + o_rowt + 32 * (c + 1));
             ads[sl ^ 1] = lds_row8(ds_in + 32 * (c + 1));
+#pragma unroll
+            for (int j = 0; j < DH; ++j) {
+              bdo[sl ^ 1][j] = tr_dkdv(true, c + 1, j);
+              bq[sl ^ 1][j] = tr_dkdv(false, c + 1, j);
+            }
           }
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int j = 0; j < DH; ++j) {
-            if (j + 1 < DH) {
-              bdo[j + 1] = tr_dkdv(true, j + 1);
-              bq[j + 1] = tr_dkdv(false, j + 1);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            dv_acc[j] = mfma32(ap[sl], bdo[j], dv_acc[j]);
-            dk_acc[j] = mfma32(ads[sl], bq[j], dk_acc[j]);
-            __builtin_amdgcn_sched_barrier(0);
+            dv_acc[j] = mfma32(ap[sl], bdo[sl][j], dv_acc[j]);
+            dk_acc[j] = mfma32(ads[sl], bq[sl][j], dk_acc[j]);
           }
+          __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_setprio(0);
       }
