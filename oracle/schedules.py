@@ -7,7 +7,8 @@ schedule generator, and the tests compare the two element by element.
 Vocabulary.  N tiles per sequence (query and key/value alike).  A *step* is
 one (query head, query tile qi, key/value tile kj) pair.  A *chain* is every
 step of one key/value tile of one key/value group (batch b, kv head hk): the
-g query heads of the group in ascending order, each walking its query tiles.
+query tiles of the walk, and at each of them the g query heads of the group
+in ascending order.
 A chain runs contiguously on one workgroup so that its dK/dV stay in
 registers ([summary] §2.1, restrictions).  The *ordinal* of a step is its
 position in the accumulation sequence of its dQ tile (head, qi); a fixed
@@ -106,8 +107,10 @@ def kv_walk(mask: int, sched: int, N: int, kj: int, Nk: int | None = None, band=
     return tiles[::-1] if sched == DESC_Q else tiles
 
 
-def _chain(group: int, g: int, kj: int, per_head_walk: list[int]) -> list[tuple[int, int, int]]:
-    return [(group * g + u, qi, kj) for u in range(g) for qi in per_head_walk]
+def _chain(group: int, g: int, kj: int, walk: list[int]) -> list[tuple[int, int, int]]:
+    """The steps of one chain: for each query tile of the walk, the g query
+    heads of the group in ascending order (query-tile-major)."""
+    return [(group * g + u, qi, kj) for qi in walk for u in range(g)]
 
 
 def _flagged(chain: list[tuple[int, int, int, int]]) -> list[Step]:

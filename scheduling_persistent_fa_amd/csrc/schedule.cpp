@@ -97,11 +97,11 @@ std::string build_list_scheduled(const Schedule& s, std::vector<std::vector<Step
       if (lo > hi) continue;  // seen by no query tile: no chain
       chain.clear();
       ords.clear();
-      for (int u = 0; u < s.g; ++u) {
-        for (int t = 0; t <= hi - lo; ++t) {
-          const int qi = (s.walk == kDescQ) ? (hi - t) : (lo + t);
-          int klo, khi;
-          visible_k(s, qi, &klo, &khi);
+      for (int t = 0; t <= hi - lo; ++t) {
+        const int qi = (s.walk == kDescQ) ? (hi - t) : (lo + t);
+        int klo, khi;
+        visible_k(s, qi, &klo, &khi);
+        for (int u = 0; u < s.g; ++u) {
           chain.push_back({grp * s.g + u, qi, kj});
           ords.push_back(kj - klo);  // ascending key/value order for every dQ tile
         }
@@ -173,8 +173,8 @@ std::string build_gang(const Schedule& s, std::vector<std::vector<StepRec>>& per
   for (int p = 0; p < gang; ++p) {
     int pos = 0;
     for (auto& ch : member[p])
-      for (int u = 0; u < s.g; ++u)
-        for (int qi : ch.second) bucket[static_cast<size_t>(u) * N + qi].push_back({pos++, ch.first});
+      for (int qi : ch.second)
+        for (int u = 0; u < s.g; ++u) bucket[static_cast<size_t>(u) * N + qi].push_back({pos++, ch.first});
   }
   std::vector<int32_t> rank(static_cast<size_t>(s.g) * N * s.Nk, -1);  // [u][qi][kj]
   for (int u = 0; u < s.g; ++u)
@@ -193,8 +193,8 @@ std::string build_gang(const Schedule& s, std::vector<std::vector<StepRec>>& per
       for (auto& ch : member[p]) {
         chain.clear();
         ords.clear();
-        for (int u = 0; u < s.g; ++u)
-          for (int qi : ch.second) {
+        for (int qi : ch.second)
+          for (int u = 0; u < s.g; ++u) {
             chain.push_back({grp * s.g + u, qi, ch.first});
             ords.push_back(rank[(static_cast<size_t>(u) * N + qi) * s.Nk + ch.first]);
           }
@@ -257,8 +257,8 @@ std::string build_band_shift(const Schedule& s, std::vector<std::vector<StepRec>
       const long long i = grp * U + u;
       long long pos = (i / s.P) * L;
       for (const Chain& ch : units[u])
-        for (int h = 0; h < s.g; ++h)
-          for (int qi : ch.second) bucket[static_cast<size_t>(h) * N + qi].push_back({pos++, ch.first});
+        for (int qi : ch.second)
+          for (int h = 0; h < s.g; ++h) bucket[static_cast<size_t>(h) * N + qi].push_back({pos++, ch.first});
     }
     for (size_t hq = 0; hq < bucket.size(); ++hq) {
       auto& v = bucket[hq];
@@ -271,8 +271,8 @@ std::string build_band_shift(const Schedule& s, std::vector<std::vector<StepRec>
       for (const Chain& ch : units[u]) {
         chain.clear();
         ords.clear();
-        for (int h = 0; h < s.g; ++h)
-          for (int qi : ch.second) {
+        for (int qi : ch.second)
+          for (int h = 0; h < s.g; ++h) {
             chain.push_back({grp * s.g + h, qi, ch.first});
             ords.push_back(rank[(static_cast<size_t>(h) * N + qi) * s.Nk + ch.first]);
           }

@@ -2,9 +2,12 @@
 // Plain C++17, no HIP dependency.
 //
 // A step is one (query head, query tile qi, key/value tile kj) pair.  A chain
-// is every step of one key/value tile of one key/value group (the group's g
-// query heads in ascending order); it runs contiguously on one workgroup so
-// dK/dV stay in registers ("Resumo Técnico: DASH ...", §2.1, restrictions).
+// is every step of one key/value tile of one key/value group: its query tiles
+// in the schedule's walk, and at each query tile the group's g query heads in
+// ascending order.  A chain runs contiguously on one workgroup so dK/dV stay
+// in registers ("Resumo Técnico: DASH ...", §2.1, restrictions).  Taking the
+// heads inside the walk keeps the lock-step spacing of the walk: two chains
+// of one gang reach a dQ tile at least g steps apart.
 // Each step carries its ordinal: the position of its contribution in the
 // accumulation sequence of its dQ tile, which fixes the summation order.
 #pragma once

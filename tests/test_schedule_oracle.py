@@ -231,6 +231,28 @@ def test_rectangular_gangs_never_meet_on_a_query_tile(mask, sched, nq, nk):
     assert len(pairs) == sum(len(l) for l in lists)
 
 
+@pytest.mark.parametrize("mask,sched,N", [(FULL, SHIFT, 4), (FULL, SHIFT, 8), (CAUSAL, SYM_SHIFT, 4),
+                                           (CAUSAL, SYM_SHIFT, 8), (CAUSAL, SYM_SHIFT, 16)])
+@pytest.mark.parametrize("g", [2, 4])
+def test_gqa_chains_keep_a_dq_tile_g_steps_apart(mask, sched, N, g):
+    # A chain takes the g heads of a group at each query tile of its walk, so
+    # lock-step position t of the walk becomes positions g*t .. g*t + g - 1:
+    # consecutive contributors to one dQ tile stand at least g positions
+    # apart, and a release latency of up to g - 1 steps costs no waiting.
+    P = N if sched == SHIFT else N // 2
+    lists = Sch.build(mask, sched, N, g, 1, P)
+    Sch.validate(lists, mask, N, g, 1)
+    pos = {}
+    for l in lists:
+        for t, s in enumerate(l):
+            pos.setdefault((s.head, s.qi), []).append((s.ord, t))
+    for tile, lst in pos.items():
+        ts = [t for _, t in sorted(lst)]
+        assert all(b - a >= g for a, b in zip(ts, ts[1:])), (tile, ts)
+    _, wait = Sch.simulate(lists, 1.0, float(g - 1))
+    assert wait == 0.0
+
+
 def test_rectangular_shift_contributions_are_one_per_step_when_nk_le_nq():
     # Latin rectangle: with Nk <= Nq no two members of a shift gang touch one
     # dQ tile at the same step, and tile qi gets its t-th contribution at step t.
