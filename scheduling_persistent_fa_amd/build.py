@@ -31,7 +31,8 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
     sources = [os.path.join(CSRC, f) for f in ("kernels.hip", "noalloc.hip", "api.cpp", "schedule.cpp")]
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Wall", "-Wshadow", "-Wno-unused-function", *DEVICE_FLAGS, "-o", tmp, *sources]
+           "-Wall", "-Wshadow", "-Wno-unused-function", *DEVICE_FLAGS, "-o", tmp, *sources,
+           "-lrocprofiler-sdk-roctx"]
     if resource_usage:
         cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
     if verbose:

@@ -6,10 +6,12 @@
 // device in which the dQ finalize kernel records a semaphore give-up; all of
 // it lives until process exit (evicted step lists are freed earlier).
 #include <hip/hip_runtime.h>
+#include <rocprofiler-sdk-roctx/roctx.h>
 
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <memory>
@@ -29,6 +31,25 @@ struct dash_schedule {
 namespace {
 
 thread_local std::string g_last_error;
+
+// Host phases of each call as roctx ranges (rocprofv3 --marker-trace shows
+// them beside the kernels; without a tool attached they cost a branch).
+struct Range {
+  explicit Range(const char* name) { roctxRangePushA(name); }
+  ~Range() { roctxRangePop(); }
+  Range(const Range&) = delete;
+  Range& operator=(const Range&) = delete;
+};
+
+// DASH_LOG=1 in the environment: one line per backward call and per step
+// list built, on stderr.
+bool log_on() {
+  static const bool on = [] {
+    const char* v = std::getenv("DASH_LOG");
+    return v != nullptr && v[0] != '\0' && v[0] != '0';
+  }();
+  return on;
+}
 
 int fail(int status, const std::string& msg) {
   g_last_error = msg;
@@ -430,6 +451,7 @@ int dash_schedule_choose(int mask, int N, int D, int g, int P, int* schedule, in
 
 static int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
                     int Sq, int Sk, int D, float softmax_scale, const Mask& mask, void* stream) {
+  Range r("dash_attn_fwd");
   const void* ptrs[] = {q, k, v, o, lse};
   int st = check_sizes(B, Hq, Hkv, Sq, Sk, D, mask);
   if (st == kEmpty) return DASH_OK;  // no query rows: nothing to write
@@ -587,12 +609,16 @@ static int bwd_plan(const void* const* ptrs, int B, int Hq, int Hkv, int Sq, int
 
 // Builds and validates the step lists of a plan (host memory only).
 static int build_host_schedule(const BwdPlan& pl, int mask_kind, std::shared_ptr<dash::Schedule>* out) {
+  Range r("dash: build and validate step lists");
   auto s = std::make_shared<dash::Schedule>();
   std::string err = dash::build_schedule(mask_kind, pl.schedule, pl.tg.Nq, pl.tg.Nk, pl.g, pl.groups, pl.P, pl.xcd != 0,
                                          pl.walk, pl.op.max_gang, s.get(), pl.band_l, pl.band_r);
   if (!err.empty()) return fail(DASH_ERR_UNSUPPORTED, err);
   err = dash::validate_schedule(*s);
   if (!err.empty()) return fail(DASH_ERR_INVALID_SCHEDULE, err);
+  if (log_on())
+    std::fprintf(stderr, "[dash] step lists: schedule %d, %d x %d tiles, g %d, %d groups, %d workgroups, %zu steps\n",
+                 pl.schedule, pl.tg.Nq, pl.tg.Nk, pl.g, pl.groups, pl.P, s->steps.size());
   *out = std::move(s);
   return DASH_OK;
 }
@@ -617,6 +643,7 @@ static int device_schedule(const BwdPlan& pl, int mask_kind, hipStream_t strm, D
     std::shared_ptr<dash::Schedule> s;
     int st = build_host_schedule(pl, mask_kind, &s);
     if (st) return st;
+    Range r("dash: upload step lists");
     DevSchedule d;
     d.num_steps = (long long)s->steps.size();
     hipError_t e = hipMalloc((void**)&d.steps, std::max<size_t>(16, s->steps.size() * sizeof(dash::StepRec)));
@@ -662,6 +689,13 @@ static int device_schedule(const BwdPlan& pl, int mask_kind, hipStream_t strm, D
 // the host-visible give-up word (may be null).
 static int bwd_enqueue(const BwdPlan& pl, const void* const* ptrs, const Mask& mask, char* ws, const DevSchedule& ds,
                        int* sticky, hipStream_t strm) {
+  Range r("dash: enqueue backward kernels");
+  if (log_on())
+    std::fprintf(stderr,
+                 "[dash] bwd B %d Hq %d Hkv %d Sq %d Sk %d D %d mask %d window (%d, %d) schedule %d tile %d "
+                 "workgroups %d gang cap %d workspace %zu bytes\n",
+                 pl.B, pl.Hq, pl.Hkv, pl.Sq, pl.Sk, pl.D, mask.kind, mask.wl, mask.wr, pl.schedule, pl.T, pl.P,
+                 pl.op.max_gang, (size_t)pl.L.total);
   const void *q = ptrs[0], *k = ptrs[1], *v = ptrs[2], *o = ptrs[3], *dO = ptrs[4];
   const float* lse = (const float*)ptrs[5];
   void *dq = const_cast<void*>(ptrs[6]), *dk = const_cast<void*>(ptrs[7]), *dv = const_cast<void*>(ptrs[8]);
@@ -765,6 +799,7 @@ static int bwd_enqueue(const BwdPlan& pl, const void* const* ptrs, const Mask& m
 static int bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
                     void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk, int D, float softmax_scale,
                     const Mask& mask, int schedule, const dash_bwd_opts* opts, void* stream) {
+  Range r("dash_attn_bwd");
   const void* ptrs[] = {q, k, v, o, dO, lse, dq, dk, dv};
   BwdPlan pl;
   int st = bwd_plan(ptrs, B, Hq, Hkv, Sq, Sk, D, softmax_scale, mask, schedule, opts, &pl);
@@ -838,6 +873,7 @@ int dash_attn_bwd_qk_noalloc(const void* q, const void* k, const void* v, const 
                              const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk,
                              int D, float softmax_scale, int mask, int schedule, const dash_bwd_opts* opts,
                              void* stream) {
+  Range r("dash_attn_bwd_qk_noalloc");
   const void* ptrs[] = {q, k, v, o, dO, lse, dq, dk, dv};
   const Mask mk = mask_from_enum(mask);
   BwdPlan pl;

@@ -174,6 +174,31 @@ def test_wait_budget_exhaustion_is_loud_and_recovers():
     assert rel_err(to_f64(dv), ref["dv"]) <= TOL
 
 
+def test_dash_log_reports_each_call():
+    # DASH_LOG=1: the library writes one line per step-list build and per
+    # backward call to stderr (checked in a child process, so that the
+    # setting, read once per process, does not leak into the other tests).
+    import os
+    import subprocess
+    import sys
+    code = ("import torch\n"
+            "from tests._gpu_helpers import DeviceProblem\n"
+            "from scheduling_persistent_fa_amd.attention import attn_fwd, attn_bwd, SYM_SHIFT\n"
+            "pb = DeviceProblem(1, 2, 2, 512, 128, True)\n"
+            "o, lse = attn_fwd(pb.q, pb.k, pb.v, True)\n"
+            "for _ in range(2):\n"
+            "    attn_bwd(pb.q, pb.k, pb.v, o, pb.do, lse, True, SYM_SHIFT)\n"
+            "torch.cuda.synchronize()\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, DASH_LOG="1")
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, env=env, capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stderr.splitlines() if l.startswith("[dash]")]
+    assert sum(l.startswith("[dash] step lists:") for l in lines) == 1, lines  # built once, then cached
+    bwd = [l for l in lines if l.startswith("[dash] bwd ")]
+    assert len(bwd) == 2 and "Sq 512 Sk 512 D 128" in bwd[0] and "schedule 3" in bwd[0], lines
+
+
 def test_concurrent_streams_use_separate_workspaces():
     # Two backward calls in flight at once on two streams, each with the
     # library-managed workspace and 16 workgroups (so both grids are resident
