@@ -792,6 +792,9 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
     const int dd = (kj - qi - diag_off) * T;
     const bool mask_on = dd > a.wr - (T - 1) || dd < (T - 1) - a.wl || kv_valid < T;
 
+    // Unrolled, so that each sub-step's code is specialised for its place in
+    // the tile (which block comes next, which buffers it uses).
+#pragma unroll
     for (int sub = 0; sub < SUBS; ++sub) {
       __syncthreads();  // B1: Q/dO/LSE/Delta of this block (and sK) visible; P^T and this dS^T buffer free
       if (*s_flag) {    // a wave gave up waiting in the previous sub-step
