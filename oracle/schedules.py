@@ -281,19 +281,26 @@ def band_shift_units(N: int, Nk: int, dl: int) -> list[list[tuple[int, list[int]
 
 def _band_shift(N: int, Nk: int, band, g: int, groups: int, P: int) -> list[list[Step]]:
     """Shift schedule on a sliding-window band: the units of every group are
-    dealt round-robin over the P workgroups ("pooled rounds"), unit i going
-    to workgroup i mod P in round i // P, so that the rounds stay full even
-    when P is not a multiple of the units per group.  A step's lock-step key
-    is its round times the unit length plus its position in the unit; each dQ
-    tile ranks its contributors by (key, kj)."""
+    dealt round-robin over the P workgroups ("pooled rounds"), the i-th unit
+    dealt going to workgroup i mod P in round i // P, so that the rounds stay
+    full even when P is not a multiple of the units per group.  The units
+    that keep the shift's lock-step slots (unclipped tiles, first/last
+    pairs) of all groups are dealt first, then the corner-triangle units of
+    all groups: a triangle unit in the same round as its group's unclipped
+    units would reach some dQ tiles at the same lock-step position as one of
+    them.  A step's lock-step key is its round times the unit length plus
+    its position in the unit; each dQ tile ranks its contributors by
+    (key, kj)."""
     dl, dr = band
     if dr != 0 or dl is None:
         raise ScheduleError("band shift needs a sliding-window band (dl, 0)")
     units = band_shift_units(N, Nk, dl)
     U, L = len(units), (dl + 1) * g
+    n_al = U - (dl // 2 if Nk - N < dl else 0)  # aligned units lead each group's list
+    order = [(grp, u) for grp in range(groups) for u in range(n_al)] + \
+            [(grp, u) for grp in range(groups) for u in range(n_al, U)]
     placed = []  # (workgroup, key0, group, unit)
-    for i in range(groups * U):
-        grp, u = divmod(i, U)
+    for i, (grp, u) in enumerate(order):
         placed.append((i % P, (i // P) * L, grp, units[u]))
     keys: dict[tuple[int, int], list[tuple[int, int]]] = {}
     for w, key0, grp, chains in placed:

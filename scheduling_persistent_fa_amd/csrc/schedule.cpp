@@ -244,9 +244,23 @@ std::string build_band_shift(const Schedule& s, std::vector<std::vector<StepRec>
   }
   const long long U = static_cast<long long>(units.size());
   const long long L = static_cast<long long>(dl + 1) * s.g;
-  // Groups are independent (their dQ tiles differ), so ranks are formed one
-  // group at a time: unit u of group grp is global unit i = grp * U + u, on
+  // Units are dealt in this order: the units that keep the shift's lock-step
+  // slots (unclipped tiles, first/last pairs) of every group, then the
+  // corner-triangle units of every group.  A triangle unit dealt into the
+  // same round as its group's unclipped units would reach some dQ tiles at
+  // the same lock-step position as one of them.  The i-th unit dealt goes to
   // workgroup i mod P in round i / P.
+  const long long n_al = U - (off < dl ? dl / 2 : 0);
+  auto dealt = [&](long long grp, long long u) {
+    return u < n_al ? grp * n_al + u : static_cast<long long>(s.groups) * n_al + grp * (U - n_al) + (u - n_al);
+  };
+  struct DealtUnit {
+    long long i;                  // position in the dealing order
+    std::vector<StepRec> steps;   // its chains, flagged and ranked
+  };
+  std::vector<DealtUnit> dealt_units;
+  // Groups are independent (their dQ tiles differ), so ranks are formed one
+  // group at a time.
   std::vector<std::vector<std::pair<long long, int>>> bucket(static_cast<size_t>(s.g) * N);  // (u, qi)
   std::vector<int32_t> rank(static_cast<size_t>(s.g) * N * s.Nk, -1);                       // [u][qi][kj]
   std::vector<Triple> chain;
@@ -254,7 +268,7 @@ std::string build_band_shift(const Schedule& s, std::vector<std::vector<StepRec>
   for (int grp = 0; grp < s.groups; ++grp) {
     for (auto& v : bucket) v.clear();
     for (long long u = 0; u < U; ++u) {
-      const long long i = grp * U + u;
+      const long long i = dealt(grp, u);
       long long pos = (i / s.P) * L;
       for (const Chain& ch : units[u])
         for (int qi : ch.second)
@@ -266,8 +280,8 @@ std::string build_band_shift(const Schedule& s, std::vector<std::vector<StepRec>
       for (size_t r = 0; r < v.size(); ++r) rank[hq * s.Nk + v[r].second] = static_cast<int32_t>(r);
     }
     for (long long u = 0; u < U; ++u) {
-      const long long i = grp * U + u;
-      const int w = gang_slot(0, static_cast<int>(i % s.P), 1, s.P, s);
+      const long long i = dealt(grp, u);
+      DealtUnit du{i, {}};
       for (const Chain& ch : units[u]) {
         chain.clear();
         ords.clear();
@@ -276,9 +290,17 @@ std::string build_band_shift(const Schedule& s, std::vector<std::vector<StepRec>
             chain.push_back({grp * s.g + h, qi, ch.first});
             ords.push_back(rank[(static_cast<size_t>(h) * N + qi) * s.Nk + ch.first]);
           }
-        push_chain(per_wg[w], chain, ords);
+        push_chain(du.steps, chain, ords);
       }
+      dealt_units.push_back(std::move(du));
     }
+  }
+  // Each workgroup runs its units in the order they were dealt (round by round).
+  std::sort(dealt_units.begin(), dealt_units.end(),
+            [](const DealtUnit& x, const DealtUnit& y) { return x.i < y.i; });
+  for (DealtUnit& du : dealt_units) {
+    const int w = gang_slot(0, static_cast<int>(du.i % s.P), 1, s.P, s);
+    per_wg[w].insert(per_wg[w].end(), du.steps.begin(), du.steps.end());
   }
   return {};
 }

@@ -340,6 +340,28 @@ def test_band_shift_schedule(N, Nk, dl, g, groups, P):
     assert wait == 0.0 and mk == L
 
 
+@pytest.mark.parametrize("N,Nk,dl,g,groups,P", [(128, 128, 32, 1, 16, 256), (16, 16, 4, 1, 4, 12), (16, 16, 4, 2, 4, 12),
+                                                 (16, 16, 4, 1, 4, 5), (32, 32, 8, 1, 4, 24), (20, 28, 4, 1, 3, 8)])
+def test_band_shift_triangle_units_never_meet_their_group(N, Nk, dl, g, groups, P):
+    # The corner-triangle units are dealt after every group's aligned units,
+    # so (with fewer workgroups than a group's aligned units) no round holds
+    # a triangle unit beside its own group's unclipped units: consecutive
+    # contributors to a dQ tile stand at least g lock-step positions apart,
+    # and a release latency below g steps costs no waiting.  (Dealt group by
+    # group instead, the sliding-window workload shape has 5.5 % of its
+    # contributions at the same position as their predecessor.)
+    lists = Sch.build(Sch.BAND, Sch.SHIFT, N, g, groups, P, Nk=Nk, band=(dl, 0))
+    Sch.validate(lists, Sch.BAND, N, g, groups, Nk=Nk, band=(dl, 0))
+    pos = {}
+    for l in lists:
+        for t, s in enumerate(l):
+            pos[(s.head, s.qi, s.ord)] = t
+    gaps = [t - pos[(h, q, o - 1)] for (h, q, o), t in pos.items() if o > 0]
+    assert min(gaps) >= g
+    _, wait = Sch.simulate(lists, 1.0, g - 0.25)
+    assert wait == 0.0
+
+
 def test_band_shift_rejects_unsupported_bands():
     for N, Nk, band in [(8, 8, (3, 0)), (8, 10, (4, 0)), (8, 8, (2, 1)), (4, 4, (4, 0))]:
         with pytest.raises(Sch.ScheduleError):
