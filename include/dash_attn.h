@@ -175,10 +175,10 @@ int dash_attn_fwd_window(const void* q, const void* k, const void* v, void* o, f
  * the dQ fp32 -> bf16 finalize.  For the deterministic schedules the result
  * is bitwise identical from run to run.  It is also independent of
  * num_workgroups whenever the accumulation order does not depend on it:
- * always for SERIAL and DESC_Q, for SHIFT / SYM_SHIFT while the gang is not
- * capped (a gang cap, given or chosen by AUTO, changes the order), and for
- * the band shift of dash_attn_bwd_window while each group's units fit in one
- * round.
+ * always for SERIAL and DESC_Q, and for SHIFT / SYM_SHIFT while the gang is
+ * not capped (a gang cap, given or chosen by AUTO, changes the order).  The
+ * order of the band shift of dash_attn_bwd_window depends on how its units
+ * fall into rounds of num_workgroups.
  * `opts` may be NULL.
  */
 int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
