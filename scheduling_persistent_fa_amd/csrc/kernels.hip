@@ -837,9 +837,13 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
 #pragma unroll
         for (int c = 0; c < DC; ++c) {
           if (c + 2 < DC) fetch(c + 2, (c + 2) % 3);
-          __builtin_amdgcn_sched_barrier(0);
           s = mfma32(aq[c % 3], bk[c % 3], s);
           dp = mfma32(ado[c % 3], vb[c], dp);
+          // chunk c+2's three reads between and after chunk c's two MFMAs
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_setprio(0);
@@ -966,11 +970,16 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
               bq[sl ^ 1][j] = tr_dkdv(false, c + 1, j);
             }
           }
-          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int j = 0; j < DH; ++j) {
             dv_acc[j] = mfma32(ap[sl], bdo[sl][j], dv_acc[j]);
             dk_acc[j] = mfma32(ads[sl], bq[sl][j], dk_acc[j]);
+          }
+          // chunk c+1's reads spread between chunk c's MFMAs
+#pragma unroll
+          for (int m = 0; m < 2 * DH; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, (2 + 8 * DH / 2 + 2 * DH - 1) / (2 * DH), 0);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
