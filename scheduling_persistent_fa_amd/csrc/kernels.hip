@@ -474,7 +474,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
   constexpr int OFF_K = OFF_DO + 2 * QBUF;       // [T][PQ]
   constexpr int OFF_PT = OFF_K + T * PQ;         // [T][PS]  P^T
   constexpr int OFF_DS = OFF_PT + T * PS;        // [2][T][PS]  dS^T, double-buffered (contracted for dQ one sub-step late)
-  constexpr int OFF_STAT = OFF_DS + 2 * DSBUF;   // [2][2][M] f32: LSE (log2 domain), Delta
+  constexpr int OFF_STAT = OFF_DS + 2 * DSBUF;   // [2][2][M] f32: LSE (log2 domain), -Delta
   constexpr int OFF_FLAG = OFF_STAT + 4 * M * 4;
   constexpr int SMEM = OFF_FLAG + 16;
   constexpr int QCH = M * D / 8 / NT;            // 16-byte chunks per thread of one Q (or dO) block
@@ -534,10 +534,12 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
   const int o_stat = opaque((32 * hf + 4 * h2) * 4);                   // LSE / Delta of this lane's rows
 
   // Prefetch registers for the next Q/dO block and one LSE-or-Delta value.
+  // LDS holds LSE·log2e (the exponent's offset) and −Delta (the initial value
+  // of the dP accumulator, so that the MFMAs produce dP − Delta).
   bf16x8 pq[QCH], pdo[QCH];
   float pstat = 0.f;
   const int st_tid = threadIdx.x < 2 * M ? threadIdx.x : 0;
-  const float st_mul = st_tid < M ? kLog2e : 1.f;
+  const float st_mul = st_tid < M ? kLog2e : -1.f;
   // Q / dO rows through buffer descriptors over the head's rows: a row
   // outside 0 .. Sq-1 lies outside the descriptor's range and reads as zeros
   // (its LSE of +inf below already makes every contribution of it zero).
@@ -817,8 +819,16 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
 
       f32x16 dqp[TPW];
       {
-        // S = Q K^T and dP = dO V^T for query rows 32*hf .. +31 x this pair's 32 key/value columns.
-        f32x16 s = f32x16{}, dp = f32x16{};
+        // S = Q K^T and dP - Delta = dO V^T - Delta for query rows 32*hf .. +31 x this
+        // pair's 32 key/value columns: the dP accumulator starts at -Delta of its row
+        // (row 8j + 4*h2 + e of the half in element 4j + e).
+        f32x16 s = f32x16{}, dp;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 nd = *(const LDS f32x4*)((const LDS char*)sdel + o_stat + 32 * j);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dp[4 * j + e] = nd[e];
+        }
         // One 16-wide d chunk at a time, double-buffered: chunk c+1's Q, dO and
         // K operands are read while chunk c's two MFMAs run.
         bf16x8 aq[3], ado[3], bk[3];
@@ -847,7 +857,8 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_setprio(0);
-        // P = exp2(S*scale*log2e - LSE*log2e); dS = P * (dP - Delta); both to LDS
+        // P = exp2(S*scale*log2e - LSE*log2e); dS = P * (dP - Delta), the second
+        // accumulator holding dP - Delta already; both to LDS
         // transposed, four rows of this lane at a time.  Interleaved with it, the
         // pending block's dQ partial = dS K (its dS^T in the other buffer): after
         // each group of four rows the wave issues the next dQ MFMAs, which run on
@@ -877,9 +888,8 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
         // the per-element comparisons.
         auto softmax_dq = [&](auto masked_tag) {
         constexpr bool MASKED = decltype(masked_tag)::value;
-        f32x4 l4[2], d4[2];
+        f32x4 l4[2];
         l4[0] = *(const LDS f32x4*)((const LDS char*)slse + o_stat);
-        d4[0] = *(const LDS f32x4*)((const LDS char*)sdel + o_stat);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           // operands of this group's dQ MFMAs (their latency hides behind the exponentials)
@@ -895,7 +905,6 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
           }
           if (j + 1 < 4) {
             l4[(j + 1) & 1] = *(const LDS f32x4*)((const LDS char*)slse + o_stat + 32 * (j + 1));
-            d4[(j + 1) & 1] = *(const LDS f32x4*)((const LDS char*)sdel + o_stat + 32 * (j + 1));
           }
           bf16x4 tp, ts;
 #pragma unroll
@@ -904,7 +913,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
             float p = __builtin_amdgcn_exp2f(s[r] * a.scale_log2 - l4[j & 1][e]);
             if (MASKED && (hi > 8 * j + e || (LEFT && lo < 8 * j + e))) p = 0.f;
             tp[e] = (__bf16)p;
-            ts[e] = (__bf16)(p * (dp[r] - d4[j & 1][e]));
+            ts[e] = (__bf16)(p * dp[r]);
           }
           *(LDS bf16x4*)(base + OFF_PT + o_stt + 16 * j) = tp;
           *(LDS bf16x4*)(ds_out + 16 * j) = ts;
