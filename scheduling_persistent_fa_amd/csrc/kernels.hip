@@ -799,7 +799,8 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
 #pragma unroll
     for (int sub = 0; sub < SUBS; ++sub) {
       __syncthreads();  // B1: Q/dO/LSE/Delta of this block (and sK) visible; P^T and this dS^T buffer free
-      if (*s_flag) {    // a wave gave up waiting in the previous sub-step
+      // Read once per step (an LDS round trip before the first operand reads).
+      if (sub == 0 && *s_flag) {  // a wave gave up waiting in the previous step
         aborted = true;
         break;
       }
@@ -1060,7 +1061,7 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
         p_ws = real ? wsb : a.dummy;
         p_sem = real ? semp : nullptr;
         p_val = ord + 1;
-        if (give_up && lane == 0) *s_flag = 1;  // everybody leaves after the next first barrier
+        if (give_up && lane == 0) *s_flag = 1;  // everybody leaves after the first barrier of the next step
       }
     }
 
