@@ -713,8 +713,12 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
   }
   bool aborted = false;
 
+  // Step records are read one step ahead, so that no sub-step waits for a
+  // scalar load of its own record or of the next block's.
+  int4 rec_next = beg < end ? step_at(beg) : make_int4(0, 0, 0, 0);
   for (int i = beg; i < end && !aborted; ++i) {
-    const int4 rec = step_at(i);
+    const int4 rec = rec_next;
+    if (i + 1 < end) rec_next = step_at(i + 1);
     const int head = rec.x, qi = rec.y, kj = rec.z, ordf = rec.w;
     const int ord = ordf & ((1 << 28) - 1);
     const bool first = ordf & (1 << 28), last = ordf & (1 << 29);
@@ -810,11 +814,9 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
       if (sub + 1 < SUBS) {
         nrow = qi * T + (sub + 1) * M;
       } else if (i + 1 < end) {
-        const int4 nr = step_at(i + 1);
-        nhead = nr.x;
-        nrow = nr.y * T;
+        nhead = rec_next.x;
+        nrow = rec_next.y * T;
       }
-      load_block(nhead, nrow);
       const LDS float* slse = (const LDS float*)(base + OFF_STAT + buf * 2 * M * 4);
       const LDS float* sdel = slse + M;
 
@@ -841,6 +843,8 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
         };
         fetch(0, 0);
         if (DC > 1) fetch(1, 1);
+        // the next block's loads go out after the first operand reads
+        load_block(nhead, nrow);
         // Each contraction runs at raised wave priority, so that while one wave
         // of a SIMD issues matrix-core instructions the other wave's vector and
         // LDS work fills the gaps.
