@@ -151,7 +151,8 @@ int dash_attn_fwd_window(const void* q, const void* k, const void* v, void* o, f
  * Failure reporting of the backward calls.  A persistent workgroup that waits
  * longer than spin_timeout_cycles on a dQ semaphore (which only happens when
  * the grid is not co-resident, e.g. another kernel holds compute units) gives
- * up, and every workgroup of the call exits.  The call's dQ, dK and dV are
+ * up; every later wait of the call then returns at once, so the kernel ends
+ * without further waiting.  The call's dQ, dK and dV are
  * then written with NaN, and a per-device host-visible word records the
  * failure: the next dash_attn_bwd* call on the device returns
  * DASH_ERR_TIMEOUT (and launches nothing), as does dash_check_async_error.

@@ -711,12 +711,11 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
     load_block(r0.x, r0.y * T);
     store_block(0);
   }
-  bool aborted = false;
 
   // Step records are read one step ahead, so that no sub-step waits for a
   // scalar load of its own record or of the next block's.
   int4 rec_next = beg < end ? step_at(beg) : make_int4(0, 0, 0, 0);
-  for (int i = beg; i < end && !aborted; ++i) {
+  for (int i = beg; i < end; ++i) {
     const int4 rec = rec_next;
     if (i + 1 < end) rec_next = step_at(i + 1);
     const int head = rec.x, qi = rec.y, kj = rec.z, ordf = rec.w;
@@ -803,11 +802,6 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
 #pragma unroll
     for (int sub = 0; sub < SUBS; ++sub) {
       __syncthreads();  // B1: Q/dO/LSE/Delta of this block (and sK) visible; P^T and this dS^T buffer free
-      // Read once per step (an LDS round trip before the first operand reads).
-      if (sub == 0 && *s_flag) {  // a wave gave up waiting in the previous step
-        aborted = true;
-        break;
-      }
       // Prefetch the next block while this one is computed (issued before this
       // sub-step's dQ writes, so staging it never waits for them).
       int nhead = head, nrow = qi * T + sub * M;  // no next block: re-read this one
@@ -1065,21 +1059,24 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
         p_ws = real ? wsb : a.dummy;
         p_sem = real ? semp : nullptr;
         p_val = ord + 1;
-        if (give_up && lane == 0) *s_flag = 1;  // everybody leaves after the first barrier of the next step
+        // After a give-up the error word makes every later wait of the call
+        // return at once, so the workgroup runs to the end of its list without
+        // waiting (no wave leaves the loop early, so the barriers stay matched).
+        if (give_up && lane == 0) *s_flag = 1;
       }
     }
 
-    if (last && !aborted) {  // written at the next chain's start, or after the loop
+    if (last) {  // written at the next chain's start, or after the loop
       epi_pending = true;
       epi_kvh = kvh;
       epi_kj = kj;
     }
   }
-  if (epi_pending && !aborted) write_dkdv(epi_kvh, epi_kj);
-  // Drain: the last block of this wave (K and its dS^T are still in LDS).
+  if (epi_pending) write_dkdv(epi_kvh, epi_kj);
+  // Drain: the last block of this wave (K and its dS^T are still in LDS),
+  // skipped after a give-up (the call's outputs are then discarded).
   __syncthreads();
-  if (*s_flag) aborted = true;
-  if (!aborted) {
+  if (!*s_flag) {
     const bool flush = __builtin_amdgcn_readfirstlane((int)(ATOMIC ? p_real : p_sem != nullptr));
     if (flush) {
       dq_finish();

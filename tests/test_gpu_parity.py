@@ -138,7 +138,8 @@ def test_unsupported_shapes_are_rejected_before_launch():
 
 def test_wait_budget_exhaustion_is_loud_and_recovers():
     # A one-cycle wait budget makes the first waiting workgroup give up (forced
-    # from the host; every workgroup still exits).  The failure must show:
+    # from the host; every later wait then returns at once, and every
+    # workgroup runs to the end of its list).  The failure must show:
     # with sync_check the call returns the timeout; without it the outputs are
     # NaN and the next call (or dash_check_async_error) reports it.  A normal
     # call afterwards is correct again.
