@@ -726,17 +726,17 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
     const __bf16* vh = a.v + ((size_t)kvh * Sk + (size_t)kj * T) * D;
     const int kv_valid = Sk - kj * T;  // key/value rows of this tile inside the sequence (>= T but on the last)
     if (first) {
-      // New chain.  The previous chain's last block is contracted (its dS^T
-      // and K are still in LDS) and written first, and released as soon as
-      // the new chain's loads have arrived, rather than a sub-step into the
-      // new chain: where members change chains at different rounds (the
-      // causal symmetric shift), the block's successor is mid-chain and would
-      // otherwise wait for this chain start.  Then the new chain's V rows go
-      // to registers and its K tile to LDS; the previous chain's dK/dV are
-      // written only after that, so that waiting for these loads never waits
-      // for those writes to drain.
+      // New chain.  The new chain's V and K rows are requested first; while
+      // they arrive, the previous chain's last block is contracted (its dS^T
+      // and K are still in LDS) and written, and it is released as soon as
+      // both have completed, rather than a sub-step into the new chain: where
+      // members change chains at different rounds (the causal symmetric
+      // shift), the block's successor is mid-chain and would otherwise wait
+      // for this chain start.  Then the new V rows stay in registers and the
+      // K tile goes to LDS; the previous chain's dK/dV are written only after
+      // that, so that waiting for these loads never waits for those writes to
+      // drain.
       const bool flush = __builtin_amdgcn_readfirstlane((int)(ATOMIC ? p_real : p_sem != nullptr));
-      if (flush) dq_finish();
       // Buffer descriptors over the tile's rows inside the sequence: rows past
       // Sk read as zeros (they are masked out of P).  Per-lane offsets are
       // recomputed from the lane's index here rather than kept live.
@@ -762,6 +762,8 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
         for (int u = 0; u < KCH; ++u)
           kt[u] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, ko + u * NT * 16, 0, 0));
       }
+      // the pending block is contracted and written while the new rows arrive
+      if (flush) dq_finish();
       if constexpr (!ATOMIC) {
         if (flush) {
           wait_vmem_all();
