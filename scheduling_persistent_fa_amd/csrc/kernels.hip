@@ -575,6 +575,13 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
   bf16x8 vb[DC];  // V rows of this pair as MFMA operands (K is read from LDS)
   f32x16 dk_acc[DH], dv_acc[DH];
   // Chain epilogue: single writer of dK (scaled) and dV for this wave's rows and d half.
+  // Each tensor's 32 x DH*32 block of this wave goes through LDS -- the P^T / dS^T
+  // buffers, which nothing else touches between a barrier that follows their last
+  // reads and the next sub-step's first barrier -- so that it leaves as 16-byte row
+  // chunks instead of one 2-byte store per accumulator element.
+  constexpr int EP = DH * 64 + 16;  // staging row pitch (bytes): the rows 4 apart of one write fall in other banks
+  constexpr int CPR = DH * 4;       // 16-byte chunks per staged row
+  static_assert(NW * 32 * EP <= 3 * T * PS, "epilogue staging fits the P^T / dS^T buffers");
   bool epi_pending = false;
   int epi_kvh = 0, epi_kj = 0;
   auto write_dkdv = [&](int kvh_, int kj_) {
@@ -587,17 +594,28 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(a.dv + tile0), (short)0, nbytes, 0x00020000);
     const int tid_e = opaque((int)threadIdx.x);  // recomputed here, not kept live
     const int l_e = tid_e & 63, w_e = tid_e >> 6;
-    const int o_lane = 2 * ((32 * (w_e >> 1) + 4 * (l_e >> 5)) * D + (w_e & 1) * DH * 32 + (l_e & 31));
+    LDS char* ep = base + OFF_PT + w_e * 32 * EP;
+    // element (row 8(r/4) + 4h + r%4, column 32j + l%32) of the C tiles
+    const int o_put = 4 * (l_e >> 5) * EP + 2 * (l_e & 31);
+    // first element of the block in the tensor: row 32 * pair, column block DH * half
+    const int o_blk = 2 * (32 * (w_e >> 1) * D + (w_e & 1) * DH * 32);
+    auto put = [&](const f32x16 (&acc)[DH], float mul, __amdgpu_buffer_rsrc_t rs) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+      for (int r = 0; r < 16; ++r) {
 #pragma unroll
-      for (int j = 0; j < DH; ++j) {
-        const int off = o_lane + 2 * ((8 * (r >> 2) + (r & 3)) * D + j * 32);
-        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)(dk_acc[j][r] * a.scale)), rk,
-                                              off, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)dv_acc[j][r]), rv, off, 0, 0);
+        for (int j = 0; j < DH; ++j)
+          *(LDS __bf16*)(ep + o_put + (8 * (r >> 2) + (r & 3)) * EP + 64 * j) = (__bf16)(acc[j][r] * mul);
       }
-    }
+      // chunk c = l + 64u of the block: row c / CPR, 16 bytes at (c % CPR) * 16
+#pragma unroll
+      for (int u = 0; u < 32 * CPR / 64; ++u) {
+        const int c = l_e + 64 * u, row = c / CPR, col = c % CPR;
+        const f32x4 v = *(const LDS f32x4*)(ep + row * EP + 16 * col);
+        __builtin_amdgcn_raw_buffer_store_b128(v, rs, o_blk + 2 * row * D + 16 * col, 0, 0);
+      }
+    };
+    put(dk_acc, a.scale, rk);
+    put(dv_acc, 1.f, rv);  // the same staging rows: this wave's reads above precede these writes
   };
   int buf = 0;
   // dQ of each 64-row block is contracted one sub-step late: the block of
@@ -1074,7 +1092,6 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
       epi_kj = kj;
     }
   }
-  if (epi_pending) write_dkdv(epi_kvh, epi_kj);
   // Drain: the last block of this wave (K and its dS^T are still in LDS),
   // skipped after a give-up (the call's outputs are then discarded).
   __syncthreads();
@@ -1089,6 +1106,10 @@ __global__ __launch_bounds__(bwd_threads<T>(), 1) void bwd_kernel(BwdArgs a) {
       }
     }
   }
+  // The last chain's dK/dV, staged in the P^T / dS^T buffers once every wave is
+  // done with the drain's dS^T reads.
+  __syncthreads();
+  if (epi_pending) write_dkdv(epi_kvh, epi_kj);
   if (a.stall && threadIdx.x == 0) {
     a.stall[2 * wg] = stall;
     a.stall[2 * wg + 1] = __builtin_amdgcn_s_memtime() - t_start;
