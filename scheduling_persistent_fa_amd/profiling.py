@@ -10,6 +10,10 @@
 ``python -m scheduling_persistent_fa_amd.profiling counters OUT.md "COMMANDS" DIR [DIR ...]``
     writes the per-dispatch median of every counter of the backward kernel
     found in the DIRs (one rocprofv3 --pmc pass each), with a few ratios.
+``python -m scheduling_persistent_fa_amd.profiling power OUT.md INTERVAL_S -- COMMAND ...``
+    runs COMMAND as a child process and samples the socket power and the
+    graphics clock of every chiplet with ``amd-smi metric -p -c`` every
+    INTERVAL_S seconds while it runs.
 """
 from __future__ import annotations
 
@@ -140,6 +144,41 @@ def counters_table(out_md: str, commands: str, dirs) -> None:
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
+def power_samples(out_md: str, interval: float, cmd: list) -> int:
+    """Socket power and per-chiplet graphics clocks while ``cmd`` runs (amd-smi text output)."""
+    import re
+    import subprocess
+    import time
+    child = subprocess.Popen(cmd)
+    rows = []
+    t0 = time.time()
+    while child.poll() is None:
+        time.sleep(interval)
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c"], capture_output=True, text=True, timeout=60)
+        pw = re.search(r"SOCKET_POWER: (\d+(?:\.\d+)?) W", r.stdout)
+        clks = [int(x) for x in re.findall(r"GFX_\d+:\s*\n\s*CLK: (\d+) MHz", r.stdout)]
+        if pw and clks:
+            rows.append((time.time() - t0, float(pw.group(1)), clks))
+    rc = child.wait()
+    peak = max((w for _, w, _ in rows), default=0.0)
+    loaded = [(w, c) for _, w, c in rows if w >= 0.5 * peak]
+    lines = [f"# Socket power and graphics clocks — `{os.path.basename(out_md)}`", "",
+             "Command (the sampler runs the benchmark as a child process):", "", "```",
+             f"python -m scheduling_persistent_fa_amd.profiling power {out_md} {interval:g} -- " + " ".join(cmd), "```", "",
+             "| t (s) | socket power (W) | graphics clock per chiplet, min / mean / max (MHz) |", "|---|---|---|"]
+    for t, w, c in rows:
+        lines.append(f"| {t:.1f} | {w:.0f} | {min(c)} / {sum(c) / len(c):.0f} / {max(c)} |")
+    if loaded:
+        mw = sum(w for w, _ in loaded) / len(loaded)
+        allc = [x for _, c in loaded for x in c]
+        lines += ["", f"Under load ({len(loaded)} samples at 50 % or more of the highest power): "
+                      f"mean socket power {mw:.0f} W, graphics clock {min(allc)}–{max(allc)} MHz "
+                      f"(mean {sum(allc) / len(allc):.0f} MHz) over {len(loaded[0][1])} chiplets."]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return rc
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "counters":
         counters_table(sys.argv[2], sys.argv[3], sys.argv[4:])
@@ -147,5 +186,8 @@ if __name__ == "__main__":
         stats_table(sys.argv[2], sys.argv[3], sys.argv[4])
     elif sys.argv[1] == "traffic":
         traffic(*sys.argv[2:10])
+    elif sys.argv[1] == "power":
+        sep = sys.argv.index("--")
+        sys.exit(power_samples(sys.argv[2], float(sys.argv[3]), sys.argv[sep + 1:]))
     else:
         raise SystemExit(__doc__)
